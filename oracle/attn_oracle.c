@@ -1,0 +1,265 @@
+/*
+ * attn_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously correct CPU implementation of the exact attention
+ * forward, in float64.  Only tests/, the smoke check and the bench's CPU
+ * baseline may load it; the product path never does.  It shares no code,
+ * header, table or constant with the GPU library.
+ *
+ * What it computes (source: the docs.rs page "oxicuda-dnn 0.1.8,
+ * src/attn/flash_attn/hopper.rs", doc comment of
+ * FlashAttention3Plan::generate_forward, and the `causal` field of
+ * FlashAttention3Config): for every batch b, head h and query row i,
+ *
+ *   A_i  = { j : 0 <= j < S, and j <= i when causal }
+ *   s_ij = scale * sum_d q[b,h,i,d] * k[b,h,j,d]
+ *   m_i  = max_{j in A_i} s_ij
+ *   l_i  = sum_{j in A_i} exp(s_ij - m_i)
+ *   O_i  = sum_{j in A_i} exp(s_ij - m_i) * v[b,h,j,:] / l_i
+ *   LSE_i = m_i + ln(l_i)
+ *
+ * Readings where the page is silent: the log-sum-exp is the natural logarithm
+ * of the scaled, masked scores; causal keeps key j for query i iff j <= i;
+ * tensors are contiguous [B,H,S,D] (LSE [B,H,S]); inputs are the 16-bit
+ * words the GPU receives (fp16 or bf16), widened exactly to float64.
+ *
+ * Three routines:
+ *   oracle_attn_fwd        two passes per row (max, then sums), the definition
+ *   oracle_attn_fwd_online keys in blocks with a running max m and running
+ *                          sum l, rescaling the partial output when m grows
+ *                          (the page's "online softmax with running max (m)
+ *                          and sum (l)"); used to show tiling is exact
+ *   oracle_attn_probs      the softmax matrix P itself, for small S
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static double g_f16[65536];
+static double g_bf16[65536];
+static int g_tables_ready = 0;
+
+/* IEEE binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. */
+static double decode_f16(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int e = (h >> 10) & 0x1f;
+  int f = h & 0x3ff;
+  double mag;
+  if (e == 0) {
+    mag = ldexp((double)f, -24);
+  } else if (e == 31) {
+    mag = f ? NAN : INFINITY;
+  } else {
+    mag = ldexp((double)(1024 + f), e - 25);
+  }
+  return sign ? -mag : mag;
+}
+
+/* bfloat16: the upper half of an IEEE binary32. */
+static double decode_bf16(uint16_t h) {
+  uint32_t w = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &w, sizeof f);
+  return (double)f;
+}
+
+static void init_tables(void) {
+  if (g_tables_ready) return;
+  for (int i = 0; i < 65536; ++i) {
+    g_f16[i] = decode_f16((uint16_t)i);
+    g_bf16[i] = decode_bf16((uint16_t)i);
+  }
+  g_tables_ready = 1;
+}
+
+static const double* table_for(int dtype) {
+  return dtype == 0 ? g_f16 : g_bf16;
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+void oracle_decode(const uint16_t* bits, int dtype, int64_t n, double* out) {
+  init_tables();
+  const double* t = table_for(dtype);
+  for (int64_t i = 0; i < n; ++i) out[i] = t[bits[i]];
+}
+
+/* Number of keys query i may attend to. */
+static int64_t allowed_keys(int64_t i, int64_t S, int causal) {
+  return causal ? (i + 1 < S ? i + 1 : S) : S;
+}
+
+static void scores_row(const double* tab, const uint16_t* q, const uint16_t* k,
+                       int64_t bh, int64_t i, int64_t S, int64_t D,
+                       double scale, int64_t n, double* qd, double* s) {
+  const uint16_t* qrow = q + (bh * S + i) * D;
+  for (int64_t d = 0; d < D; ++d) qd[d] = tab[qrow[d]];
+  for (int64_t j = 0; j < n; ++j) {
+    const uint16_t* krow = k + (bh * S + j) * D;
+    double acc = 0.0;
+    for (int64_t d = 0; d < D; ++d) acc += qd[d] * tab[krow[d]];
+    s[j] = scale * acc;
+  }
+}
+
+/*
+ * rows: flat row indices r = (b*H + h)*S + i, or NULL for all B*H*S rows in
+ * order.  o receives nrows*D values, lse nrows values.  Returns 0, or -1 when
+ * scratch memory cannot be had.
+ */
+int oracle_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                    int dtype, int64_t B, int64_t H, int64_t S, int64_t D,
+                    double scale, int causal, const int64_t* rows,
+                    int64_t nrows, double* o, double* lse) {
+  init_tables();
+  const double* tab = table_for(dtype);
+  if (rows == NULL) nrows = B * H * S;
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* qd = (double*)malloc(sizeof(double) * (size_t)(D > 0 ? D : 1));
+    double* s = (double*)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+    double* acc = (double*)malloc(sizeof(double) * (size_t)(D > 0 ? D : 1));
+    if (!qd || !s || !acc) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 8)
+      for (int64_t t = 0; t < nrows; ++t) {
+        int64_t r = rows ? rows[t] : t;
+        int64_t bh = r / S, i = r % S;
+        int64_t n = allowed_keys(i, S, causal);
+        double* orow = o + t * D;
+        if (n <= 0) {
+          for (int64_t d = 0; d < D; ++d) orow[d] = 0.0;
+          lse[t] = -INFINITY;
+          continue;
+        }
+        scores_row(tab, q, k, bh, i, S, D, scale, n, qd, s);
+        /* pass 1: the row maximum */
+        double m = s[0];
+        for (int64_t j = 1; j < n; ++j) m = s[j] > m ? s[j] : m;
+        /* pass 2: normaliser and weighted sum of values */
+        double l = 0.0;
+        for (int64_t d = 0; d < D; ++d) acc[d] = 0.0;
+        for (int64_t j = 0; j < n; ++j) {
+          double p = exp(s[j] - m);
+          l += p;
+          const uint16_t* vrow = v + (bh * S + j) * D;
+          for (int64_t d = 0; d < D; ++d) acc[d] += p * tab[vrow[d]];
+        }
+        for (int64_t d = 0; d < D; ++d) orow[d] = acc[d] / l;
+        lse[t] = m + log(l);
+      }
+    }
+    free(qd);
+    free(s);
+    free(acc);
+  }
+  return failed ? -1 : 0;
+}
+
+/*
+ * The same result reached blockwise: keys are visited in blocks of `block`,
+ * keeping a running max m, a running sum l and an unnormalised output that is
+ * rescaled by exp(m_old - m_new) whenever the max grows.  All rows.
+ */
+int oracle_attn_fwd_online(const uint16_t* q, const uint16_t* k,
+                           const uint16_t* v, int dtype, int64_t B, int64_t H,
+                           int64_t S, int64_t D, double scale, int causal,
+                           int64_t block, double* o, double* lse) {
+  init_tables();
+  if (block <= 0) return -1;
+  const double* tab = table_for(dtype);
+  int64_t nrows = B * H * S;
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* qd = (double*)malloc(sizeof(double) * (size_t)(D > 0 ? D : 1));
+    double* s = (double*)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+    double* acc = (double*)malloc(sizeof(double) * (size_t)(D > 0 ? D : 1));
+    if (!qd || !s || !acc) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 8)
+      for (int64_t r = 0; r < nrows; ++r) {
+        int64_t bh = r / S, i = r % S;
+        int64_t n = allowed_keys(i, S, causal);
+        double* orow = o + r * D;
+        scores_row(tab, q, k, bh, i, S, D, scale, n, qd, s);
+        double m = -INFINITY, l = 0.0;
+        for (int64_t d = 0; d < D; ++d) acc[d] = 0.0;
+        for (int64_t j0 = 0; j0 < n; j0 += block) {
+          int64_t j1 = j0 + block < n ? j0 + block : n;
+          double mb = -INFINITY;
+          for (int64_t j = j0; j < j1; ++j) mb = s[j] > mb ? s[j] : mb;
+          double m_new = mb > m ? mb : m;
+          double alpha = (m == -INFINITY) ? 0.0 : exp(m - m_new);
+          l *= alpha;
+          for (int64_t d = 0; d < D; ++d) acc[d] *= alpha;
+          for (int64_t j = j0; j < j1; ++j) {
+            double p = exp(s[j] - m_new);
+            l += p;
+            const uint16_t* vrow = v + (bh * S + j) * D;
+            for (int64_t d = 0; d < D; ++d) acc[d] += p * tab[vrow[d]];
+          }
+          m = m_new;
+        }
+        if (n <= 0) {
+          for (int64_t d = 0; d < D; ++d) orow[d] = 0.0;
+          lse[r] = -INFINITY;
+        } else {
+          for (int64_t d = 0; d < D; ++d) orow[d] = acc[d] / l;
+          lse[r] = m + log(l);
+        }
+      }
+    }
+    free(qd);
+    free(s);
+    free(acc);
+  }
+  return failed ? -1 : 0;
+}
+
+/* The softmax matrix P [B,H,S,S] (zero where masked), for small S. */
+int oracle_attn_probs(const uint16_t* q, const uint16_t* k, int dtype,
+                      int64_t B, int64_t H, int64_t S, int64_t D, double scale,
+                      int causal, double* p) {
+  init_tables();
+  const double* tab = table_for(dtype);
+  double* qd = (double*)malloc(sizeof(double) * (size_t)(D > 0 ? D : 1));
+  double* s = (double*)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+  if (!qd || !s) {
+    free(qd);
+    free(s);
+    return -1;
+  }
+  for (int64_t bh = 0; bh < B * H; ++bh) {
+    for (int64_t i = 0; i < S; ++i) {
+      double* prow = p + (bh * S + i) * S;
+      int64_t n = allowed_keys(i, S, causal);
+      for (int64_t j = 0; j < S; ++j) prow[j] = 0.0;
+      if (n <= 0) continue;
+      scores_row(tab, q, k, bh, i, S, D, scale, n, qd, s);
+      double m = s[0];
+      for (int64_t j = 1; j < n; ++j) m = s[j] > m ? s[j] : m;
+      double l = 0.0;
+      for (int64_t j = 0; j < n; ++j) l += exp(s[j] - m);
+      for (int64_t j = 0; j < n; ++j) prow[j] = exp(s[j] - m) / l;
+    }
+  }
+  free(qd);
+  free(s);
+  return 0;
+}

@@ -1,0 +1,244 @@
+"""Pins of the fp64 oracle against facts the definition fixes (CPU only).
+
+Each test would fail on a plausible slip in the oracle: a dropped scale, a
+wrong mask direction, a log in the wrong base, a max that is not subtracted
+consistently, a transposed operand, a normaliser off by a term.
+"""
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from exact_attention_52_amd import inputs
+from oracle import brute
+
+
+def words(x, dtype):
+    return inputs.round_to_bits(np.asarray(x, dtype=np.float64), dtype)
+
+
+def exact(bits, dtype):
+    return inputs.bits_to_float(bits, dtype).astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# P1: brute force on tiny shapes (independent pure-Python implementation)
+# --------------------------------------------------------------------------
+TINY = [(1, 1, 1, 1), (1, 1, 2, 3), (1, 2, 3, 2), (2, 1, 5, 4), (2, 2, 8, 8),
+        (1, 1, 7, 5), (2, 2, 4, 1), (1, 2, 6, 7)]
+
+
+@pytest.mark.parametrize("shape", TINY)
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_p1_brute_force(oracle_mod, shape, causal, dtype):
+    B, H, S, D = shape
+    seed = zlib.crc32(repr((shape, causal, dtype)).encode()) & 0xFFFF
+    for mult, scale in ((1.0, 1 / math.sqrt(D)), (4.0, 1.7), (1.0, 0.0)):
+        q, k, v = inputs.gen_qkv(B, H, S, D, dtype, seed=seed, qk_mult=mult)
+        o, lse = oracle_mod.attn_fwd(q, k, v, dtype, scale, causal)
+        ob, lb = brute.attention(q.tolist(), k.tolist(), v.tolist(), dtype, scale, causal)
+        ob, lb = np.array(ob), np.array(lb)
+        assert np.allclose(o, ob, rtol=1e-13, atol=1e-13)
+        assert np.allclose(lse, lb, rtol=1e-13, atol=1e-13)
+
+
+def test_p1_equal_scores_tie(oracle_mod):
+    # all keys identical: every allowed key gets the same weight
+    B, H, S, D = 1, 1, 6, 4
+    q = words(np.ones((B, H, S, D)), "fp16")
+    k = words(np.full((B, H, S, D), 0.5), "fp16")
+    _, _, v = inputs.gen_qkv(B, H, S, D, "fp16", seed=3)
+    o, lse = oracle_mod.attn_fwd(q, k, v, "fp16", 0.25, True)
+    ob, lb = brute.attention(q.tolist(), k.tolist(), v.tolist(), "fp16", 0.25, True)
+    assert np.allclose(o, np.array(ob), rtol=1e-13, atol=1e-13)
+    vv = exact(v, "fp16")
+    for i in range(S):
+        assert np.allclose(o[0, 0, i], vv[0, 0, :i + 1].mean(axis=0), atol=1e-14)
+        assert abs(lse[0, 0, i] - (0.25 * 0.5 * D + math.log(i + 1))) < 1e-13
+
+
+# --------------------------------------------------------------------------
+# Library cross-check: torch's float64 CPU attention and logsumexp
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype,D", [("fp16", 64), ("bf16", 128), ("bf16", 256)])
+def test_matches_torch_float64_sdpa(oracle_mod, causal, dtype, D):
+    B, H, S = 2, 2, 97
+    scale = float(np.float32(1 / math.sqrt(D)))
+    q, k, v = inputs.gen_qkv(B, H, S, D, dtype, seed=11, qk_mult=2.0)
+    o, lse = oracle_mod.attn_fwd(q, k, v, dtype, scale, causal)
+    tq, tk, tv = (torch.from_numpy(exact(x, dtype)) for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, is_causal=causal, scale=scale)
+    s = scale * (tq @ tk.transpose(-1, -2))
+    if causal:
+        s = s.masked_fill(torch.ones(S, S, dtype=torch.bool).triu(1), float("-inf"))
+    ref_lse = torch.logsumexp(s, dim=-1)
+    assert np.allclose(o, ref.numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(lse, ref_lse.numpy(), rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# P2: normalisation
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("causal", [False, True])
+def test_p2a_rows_sum_to_one_and_mask_shape(oracle_mod, causal):
+    B, H, S, D = 2, 3, 64, 32
+    q, k, v = inputs.gen_qkv(B, H, S, D, "bf16", seed=5, qk_mult=2.0)
+    p = oracle_mod.attn_probs(q, k, "bf16", 0.3, causal)
+    assert np.allclose(p.sum(axis=-1), 1.0, atol=1e-14)
+    assert np.all(p >= 0)
+    if causal:
+        assert np.all(p[..., np.triu_indices(S, 1)[0], np.triu_indices(S, 1)[1]] == 0)
+        assert np.all(np.diagonal(p, axis1=-2, axis2=-1) > 0)
+    # O is P times V (matmul as a library step)
+    o, _ = oracle_mod.attn_fwd(q, k, v, "bf16", 0.3, causal)
+    assert np.allclose(o, p @ exact(v, "bf16"), atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_p2b_constant_values(oracle_mod, causal):
+    B, H, S, D = 1, 2, 50, 16
+    q, k, _ = inputs.gen_qkv(B, H, S, D, "fp16", seed=6, qk_mult=2.0)
+    c = np.linspace(-3, 3, D)
+    v = words(np.broadcast_to(c, (B, H, S, D)), "fp16")
+    o, _ = oracle_mod.attn_fwd(q, k, v, "fp16", 0.7, causal)
+    assert np.allclose(o, exact(v, "fp16")[:, :, :1, :], atol=1e-14)
+
+
+def test_p2c_causal_row_zero(oracle_mod):
+    B, H, S, D = 2, 2, 40, 64
+    q, k, v = inputs.gen_qkv(B, H, S, D, "bf16", seed=8)
+    o, lse = oracle_mod.attn_fwd(q, k, v, "bf16", 0.125, True)
+    qq, kk, vv = exact(q, "bf16"), exact(k, "bf16"), exact(v, "bf16")
+    assert np.array_equal(o[:, :, 0], vv[:, :, 0])
+    s00 = 0.125 * np.einsum("bhd,bhd->bh", qq[:, :, 0], kk[:, :, 0])
+    assert np.allclose(lse[:, :, 0], s00, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# P3: Q = 0 closed form (uniform weights, LSE = ln |A_i|)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("causal", [False, True])
+def test_p3_zero_query_closed_form(oracle_mod, causal):
+    B, H, S, D = 1, 2, 33, 8
+    _, k, v = inputs.gen_qkv(B, H, S, D, "fp16", seed=9)
+    q = np.zeros_like(k)
+    o, lse = oracle_mod.attn_fwd(q, k, v, "fp16", 0.9, causal)
+    vv = exact(v, "fp16")
+    for i in range(S):
+        n = i + 1 if causal else S
+        assert np.allclose(o[:, :, i], vv[:, :, :n].mean(axis=2), atol=1e-14)
+        assert np.allclose(lse[:, :, i], math.log(n), atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# P4: shifting every key by one vector u leaves O alone and moves LSE by
+# scale * q_i . u
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("causal", [False, True])
+def test_p4_key_shift(oracle_mod, causal):
+    rng = np.random.default_rng(12)
+    B, H, S, D = 1, 2, 24, 8
+    # small multiples of 1/8 keep K and K + u exact in fp16
+    qf = rng.integers(-8, 9, (B, H, S, D)) / 8.0
+    kf = rng.integers(-8, 9, (B, H, S, D)) / 8.0
+    u = rng.integers(-4, 5, (D,)) / 4.0
+    _, _, v = inputs.gen_qkv(B, H, S, D, "fp16", seed=12)
+    q, k, k2 = words(qf, "fp16"), words(kf, "fp16"), words(kf + u, "fp16")
+    assert np.array_equal(exact(k2, "fp16"), kf + u)
+    scale = 0.4
+    o1, l1 = oracle_mod.attn_fwd(q, k, v, "fp16", scale, causal)
+    o2, l2 = oracle_mod.attn_fwd(q, k2, v, "fp16", scale, causal)
+    assert np.allclose(o1, o2, atol=1e-13)
+    assert np.allclose(l2, l1 + scale * (qf @ u), atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# P5: permutations (non-causal)
+# --------------------------------------------------------------------------
+def test_p5_permutations(oracle_mod):
+    B, H, S, D = 2, 1, 30, 16
+    q, k, v = inputs.gen_qkv(B, H, S, D, "bf16", seed=13, qk_mult=2.0)
+    o, lse = oracle_mod.attn_fwd(q, k, v, "bf16", 0.25, False)
+    perm = np.random.default_rng(1).permutation(S)
+    o2, l2 = oracle_mod.attn_fwd(q, k[:, :, perm], v[:, :, perm], "bf16", 0.25, False)
+    assert np.allclose(o, o2, atol=1e-13) and np.allclose(lse, l2, atol=1e-13)
+    o3, l3 = oracle_mod.attn_fwd(np.ascontiguousarray(q[:, :, perm]), k, v, "bf16", 0.25, False)
+    assert np.allclose(o[:, :, perm], o3, atol=1e-14)
+    assert np.allclose(lse[:, :, perm], l3, atol=1e-14)
+    # a causal mask breaks key-permutation invariance: the oracle must notice
+    oc, _ = oracle_mod.attn_fwd(q, k, v, "bf16", 0.25, True)
+    oc2, _ = oracle_mod.attn_fwd(q, k[:, :, perm], v[:, :, perm], "bf16", 0.25, True)
+    assert not np.allclose(oc, oc2, atol=1e-3)
+
+
+# --------------------------------------------------------------------------
+# P6: the blockwise running-max form equals the two-pass definition
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("block", [1, 7, 64, 100])
+@pytest.mark.parametrize("causal", [False, True])
+def test_p6_online_equals_two_pass(oracle_mod, block, causal):
+    B, H, S, D = 1, 3, 100, 32
+    q, k, v = inputs.gen_qkv(B, H, S, D, "fp16", seed=14, qk_mult=2.0)
+    o, lse = oracle_mod.attn_fwd(q, k, v, "fp16", 0.3, causal)
+    o2, l2 = oracle_mod.attn_fwd_online(q, k, v, "fp16", 0.3, causal, block)
+    assert np.allclose(o, o2, atol=1e-12) and np.allclose(lse, l2, atol=1e-12)
+
+
+def test_p6_rising_max_forces_rescale(oracle_mod):
+    # each later key scores higher than all before it, so a blockwise pass
+    # must rescale at every block
+    B, H, S, D = 1, 1, 64, 4
+    q = words(np.ones((B, H, S, D)), "fp16")
+    kf = np.repeat((np.arange(S) / 8.0)[None, None, :, None], D, axis=3)
+    k = words(kf, "fp16")
+    _, _, v = inputs.gen_qkv(B, H, S, D, "fp16", seed=15)
+    o, lse = oracle_mod.attn_fwd(q, k, v, "fp16", 0.5, False)
+    o2, l2 = oracle_mod.attn_fwd_online(q, k, v, "fp16", 0.5, False, 8)
+    assert np.allclose(o, o2, atol=1e-12) and np.allclose(lse, l2, atol=1e-12)
+    # closed form: scores are 0.5 * D * j/8 = j/4; LSE = ln sum_j e^{j/4}
+    ref = math.log(sum(math.exp(j / 4) for j in range(S)))
+    assert abs(lse[0, 0, 0] - ref) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# P7: one dominant key -> O is (numerically) that key's value
+# --------------------------------------------------------------------------
+def test_p7_one_hot_limit(oracle_mod):
+    B, H, S, D = 1, 1, 16, 8
+    qf = np.zeros((B, H, S, D))
+    kf = np.zeros((B, H, S, D))
+    qf[..., 0] = 1.0
+    kf[0, 0, 11, 0] = 64.0  # score 64 * scale vs 0 elsewhere
+    _, _, v = inputs.gen_qkv(B, H, S, D, "fp16", seed=16)
+    o, lse = oracle_mod.attn_fwd(words(qf, "fp16"), words(kf, "fp16"), v, "fp16", 1.0, False)
+    vv = exact(v, "fp16")
+    assert np.allclose(o[0, 0], vv[0, 0, 11], atol=1e-20 + 16 * math.exp(-64) * 10)
+    assert abs(lse[0, 0, 3] - (64 + math.log1p(15 * math.exp(-64)))) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# Sampled rows equal the full computation
+# --------------------------------------------------------------------------
+def test_row_sampling_matches_full(oracle_mod):
+    B, H, S, D = 2, 2, 37, 16
+    q, k, v = inputs.gen_qkv(B, H, S, D, "bf16", seed=17)
+    o, lse = oracle_mod.attn_fwd(q, k, v, "bf16", 0.25, True)
+    rows = np.array([0, 5, 36, 37, 100, 147])
+    o2, l2 = oracle_mod.attn_fwd(q, k, v, "bf16", 0.25, True, rows=rows)
+    assert np.array_equal(o.reshape(-1, D)[rows], o2)
+    assert np.array_equal(lse.reshape(-1)[rows], l2)
+
+
+def test_decoder_matches_torch(oracle_mod):
+    allw = np.arange(65536, dtype=np.uint16)
+    for dtype, tdt in (("fp16", torch.float16), ("bf16", torch.bfloat16)):
+        ref = torch.from_numpy(allw.view(np.int16).copy()).view(tdt).to(torch.float64).numpy()
+        got = oracle_mod.decode(allw, dtype)
+        fin = np.isfinite(ref)
+        assert np.array_equal(got[fin], ref[fin])
+        assert np.array_equal(np.isnan(got), np.isnan(ref))
