@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact attention forward on one MI355X.
+
+A step is one attn_fwd call (the whole fused path: Q tile load, K/V tile
+stream, score MFMA, mask, online softmax, PV MFMA, epilogue) over one batch of
+seeded synthetic input of the headline workload, by default
+B=2, H=16, S=4096, D=128, fp16, non-causal, Q,K ~ 2 N(0,1), V ~ N(0,1).
+
+Prints ONE JSON line.  `value` is TFLOP/s with FLOPs = 4*B*H*S^2*D (halved when
+causal) and the inputs already resident in HBM.  The roofline object uses the
+average kernel duration from HIP events recorded around every launch of the
+timed region on the stream the kernel runs on.  The CPU baseline times the
+fp64 oracle on a bounded sample of rows of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOPS + % of MI355X fp16/bf16 MFMA peak, hd128 causal/non-causal"
+PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
+HEADLINE = "c4_b2h16s4096d128_fp16_peaky"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_c4_hbm_traffic.txt")
+
+
+def flops(B, H, S, D, causal):
+    f = 4.0 * B * H * S * S * D
+    return f / 2 if causal else f
+
+
+def min_bytes(B, H, S, D):
+    return 8 * B * H * S * D + 4 * B * H * S
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "exact_attention_52_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when missing or taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for ln in open(TRAFFIC_FILE):
+        if ":" in ln and not ln.startswith("#"):
+            k, v = ln.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def make_inputs(name, seed=0):
+    import torch
+    from exact_attention_52_amd import inputs
+    B, H, S, D, dtype, causal, mult = inputs.WORKLOADS[name]
+    q, k, v = inputs.gen_qkv(B, H, S, D, dtype, seed=seed, qk_mult=mult)
+    tdt = torch.float16 if dtype == "fp16" else torch.bfloat16
+    dev = [torch.from_numpy(x.view(np.int16)).view(tdt).to("cuda:0") for x in (q, k, v)]
+    return (B, H, S, D, dtype, causal), (q, k, v), dev
+
+
+def time_workload(ea, shape, dev, steps, warmup):
+    """Returns (ms_per_step over the timed region, mean per-launch ms)."""
+    import torch
+    B, H, S, D, dtype, causal = shape
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    q, k, v = dev
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        ea.fwd(q, k, v, scale=scale, causal=causal, out=o, lse=lse, stream=stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        ev[i][0].record(stream)
+        ea.fwd(q, k, v, scale=scale, causal=causal, out=o, lse=lse, stream=stream)
+        ev[i][1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total = t0.elapsed_time(t1)
+    per = [a.elapsed_time(b) for a, b in ev]
+    return total / steps, float(np.mean(per)), o, lse
+
+
+def parity_spot_check(shape, words, o, lse, n_rows=128):
+    import oracle
+    from exact_attention_52_amd import inputs
+    B, H, S, D, dtype, causal = shape
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    rng = np.random.default_rng(123)
+    rows = np.unique(np.concatenate([[0, B * H * S - 1], rng.integers(0, B * H * S, n_rows)]))
+    o_ref, l_ref = oracle.attn_fwd(*words, dtype, scale, causal, rows=rows)
+    og = o.float().cpu().numpy().reshape(-1, D)[rows].astype(np.float64)
+    lg = lse.cpu().numpy().reshape(-1)[rows].astype(np.float64)
+    eo = float(np.abs(og - o_ref).max())
+    el = float((np.abs(lg - l_ref) / np.maximum(1.0, np.abs(l_ref))).max())
+    tol = 2e-3 if dtype == "fp16" else 1.6e-2
+    return {"rows": int(rows.size), "max_abs_err_o": eo, "max_err_lse": el,
+            "tol_o": tol, "tol_lse": 1e-4, "ok": bool(eo <= tol and el <= 1e-4)}
+
+
+def cpu_baseline(shape, words, target_s=12.0):
+    """The fp64 oracle, as it stands, on a bounded sample of rows."""
+    import oracle
+    B, H, S, D, dtype, causal = shape
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    total_rows = B * H * S
+    rng = np.random.default_rng(7)
+    probe = rng.choice(total_rows, size=min(256, total_rows), replace=False)
+    t = time.perf_counter()
+    oracle.attn_fwd(*words, dtype, scale, causal, rows=probe)
+    dt = max(time.perf_counter() - t, 1e-6)
+    n = int(min(total_rows, max(probe.size, probe.size * target_s / dt)))
+    rows = rng.choice(total_rows, size=n, replace=False)
+    t = time.perf_counter()
+    oracle.attn_fwd(*words, dtype, scale, causal, rows=rows)
+    dt = time.perf_counter() - t
+    i = rows % S
+    keys = (i + 1) if causal else np.full(rows.size, S)
+    # same FLOP convention as the GPU figure: 4*D per (query, kept key) pair,
+    # counted as the exact-half convention for causal
+    fl = float(4.0 * D * (keys.sum() if not causal else rows.size * S / 2))
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{rows.size} random query rows of {total_rows} ({rows.size / total_rows:.2%}) "
+                      f"of the same workload, fp64 two-pass oracle, {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-others", action="store_true", help="skip timing the other workloads")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the attention forward "
+              "shards by batch*head with no communication, so N GPUs run N independent copies.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_attention_52_amd as ea
+    from exact_attention_52_amd import inputs
+    ea._lib.load()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    shape, words, dev = make_inputs(args.workload)
+    B, H, S, D, dtype, causal = shape
+    ms_step, ms_kernel, o, lse = time_workload(ea, shape, dev, args.steps, args.warmup)
+    f = flops(B, H, S, D, causal)
+    value = f / (ms_step * 1e-3) / 1e12
+    achieved = f / (ms_kernel * 1e-3) / 1e12
+    print(f"# {args.workload}: {ms_step * 1e3:.1f} us/step, kernel {ms_kernel * 1e3:.1f} us, "
+          f"{achieved:.1f} TFLOP/s ({achieved / PEAK_TFLOPS:.1%} of peak)", file=sys.stderr, flush=True)
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    parity = parity_spot_check(shape, words, o, lse)
+    print(f"# parity spot check: {parity}", file=sys.stderr, flush=True)
+
+    others = {}
+    if not args.no_others:
+        for name in inputs.WORKLOADS:
+            if name == args.workload:
+                continue
+            shp, _, dv = make_inputs(name)
+            ms_s, ms_k, _, _ = time_workload(ea, shp, dv, max(5, args.steps // 2), max(2, args.warmup // 2))
+            fl = flops(shp[0], shp[1], shp[2], shp[3], shp[5])
+            others[name] = {"us_per_call": round(ms_k * 1e3, 2),
+                            "tflops": round(fl / (ms_k * 1e-3) / 1e12, 1),
+                            "frac_of_peak": round(fl / (ms_k * 1e-3) / 1e12 / PEAK_TFLOPS, 4)}
+            print(f"# {name}: {others[name]}", file=sys.stderr, flush=True)
+            del dv
+            torch.cuda.empty_cache()
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(shape, words)
+    if cpu:
+        print(f"# cpu baseline: {cpu}", file=sys.stderr, flush=True)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded Philox4x32-10 + Box-Muller)",
+        "config": {"workload": args.workload, "B": B, "H": H, "S": S, "D": D, "dtype": dtype,
+                   "causal": causal, "scale": "1/sqrt(D)", "global_batch": B, "seq_len": S,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
+                     "traffic": read_traffic(),
+                     "algorithmic_min_hbm_bytes": min_bytes(B, H, S, D)},
+        "cpu_baseline": cpu,
+        "parity_spot_check": parity,
+        "other_workloads": others,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,102 @@
+"""ctypes binding of libattn.so: the C ABI of include/attn.h, one Python name
+per exported symbol.  Argument marshalling only; every step of the attention
+runs in the library's gfx950 kernels."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+ABI_VERSION = 1
+
+ATTN_F16, ATTN_BF16 = 0, 1
+STATUS = {
+    0: "ATTN_OK", 1: "ATTN_ERR_NULL_PTR", 2: "ATTN_ERR_BAD_SHAPE",
+    3: "ATTN_ERR_UNSUPPORTED_HEAD_DIM", 4: "ATTN_ERR_UNSUPPORTED_DTYPE",
+    5: "ATTN_ERR_MISALIGNED", 6: "ATTN_ERR_BAD_SCALE", 7: "ATTN_ERR_ALIASING",
+    8: "ATTN_ERR_UNSUPPORTED_DEVICE", 9: "ATTN_ERR_LAUNCH", 10: "ATTN_ERR_BAD_ARGUMENT",
+}
+EXPORTS = ("attn_fwd", "attn_fwd_plan", "attn_fwd_workgroup_tile", "attn_status_string",
+           "attn_last_error", "attn_abi_version")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "block_m", "block_n", "kv_stages", "waves_q", "waves_k",
+        "threads_per_workgroup", "lds_bytes", "num_q_tiles", "num_workgroups")]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+_lib = None
+
+
+def load():
+    """Load libattn.so; raise loudly if it is missing (no fallback exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m exact_attention_52_amd.build` "
+            "(or __graft_entry__.build()); there is no CPU or fallback path")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, vp, ci, cf = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, cf, ci, ci, vp]
+    lib.attn_fwd.restype = ci
+    lib.attn_fwd_plan.argtypes = [i64, i64, i64, i64, ci, ci, ctypes.POINTER(Plan)]
+    lib.attn_fwd_plan.restype = ci
+    lib.attn_fwd_workgroup_tile.argtypes = [i64, i64, i64, i64, ci, ci, i64,
+                                            ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.attn_fwd_workgroup_tile.restype = ci
+    lib.attn_status_string.argtypes = [ci]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_last_error.argtypes = []
+    lib.attn_last_error.restype = ctypes.c_char_p
+    lib.attn_abi_version.argtypes = []
+    lib.attn_abi_version.restype = ci
+    if lib.attn_abi_version() != ABI_VERSION:
+        raise ImportError(f"libattn.so ABI {lib.attn_abi_version()} != expected {ABI_VERSION}")
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().attn_last_error().decode()
+
+
+def status_string(status: int) -> str:
+    return load().attn_status_string(int(status)).decode()
+
+
+def check(status: int) -> None:
+    if status != 0:
+        raise AttnError(status, last_error())
+
+
+def attn_fwd(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, S: int, D: int,
+             scale: float, causal: bool, dtype: int, stream: int) -> int:
+    """Raw call: device pointers as ints; returns the status code."""
+    return load().attn_fwd(q, k, v, o, lse, B, H, S, D, float(scale), int(bool(causal)),
+                           int(dtype), stream)
+
+
+def attn_fwd_plan(B: int, H: int, S: int, D: int, causal: bool, dtype: int) -> dict:
+    p = Plan()
+    check(load().attn_fwd_plan(B, H, S, D, int(bool(causal)), dtype, ctypes.byref(p)))
+    return p.as_dict()
+
+
+def attn_fwd_workgroup_tile(B: int, H: int, S: int, D: int, causal: bool, dtype: int, wg: int):
+    t, bh = ctypes.c_int64(), ctypes.c_int64()
+    check(load().attn_fwd_workgroup_tile(B, H, S, D, int(bool(causal)), dtype, wg,
+                                         ctypes.byref(t), ctypes.byref(bh)))
+    return t.value, bh.value

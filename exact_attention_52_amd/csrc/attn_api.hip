@@ -1,0 +1,236 @@
+// attn_api.hip -- the C ABI declared in include/attn.h: argument checks,
+// launch planning, device check and kernel dispatch for gfx950.
+//
+// The checks mirror the page's validate_config (docs.rs "oxicuda-dnn 0.1.8,
+// src/attn/flash_attn/hopper.rs"): head_dim must be one of 64/128/256, the
+// float type F16 or BF16; the launch follows its launch_params: one workgroup
+// per (query tile, batch*head), ceil(S / block_m) query tiles.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cfloat>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "attn.h"
+#include "attn_fwd_kernel.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return ATTN_OK;
+}
+
+// Per-head-dim tile shapes.  All use two K/V LDS stages.
+//   D=64 : 4 query waves x 32 rows = 128 rows, 128-key tiles, 70 KiB LDS
+//   D=128: 8 query waves = 256 rows, 128-key tiles, 136 KiB LDS
+//   D=256: 2 query waves = 64 rows (the page's 64-row Q tile for D=256), each
+//          64-key tile split over 2 key waves, 138 KiB LDS
+using Cfg64 = attn::TileCfg<64, 4, 1, 128>;
+using Cfg128 = attn::TileCfg<128, 8, 1, 128>;
+using Cfg256 = attn::TileCfg<256, 2, 2, 64>;
+
+template <class C>
+void fill_plan(int64_t B, int64_t H, int64_t S, attn_fwd_plan_t* p) {
+  p->block_m = C::BM;
+  p->block_n = C::BN;
+  p->kv_stages = C::STAGES;
+  p->waves_q = C::QW;
+  p->waves_k = C::KW;
+  p->threads_per_workgroup = C::NT;
+  p->lds_bytes = C::LDS_BYTES;
+  p->num_q_tiles = (S + C::BM - 1) / C::BM;
+  p->num_workgroups = p->num_q_tiles * B * H;
+}
+
+int check_sizes(int64_t B, int64_t H, int64_t S, int64_t D, int dtype) {
+  if (B < 0 || H < 0 || S < 0)
+    return fail(ATTN_ERR_BAD_SHAPE, "B, H and S must be >= 0 (got B=%lld H=%lld S=%lld)",
+                (long long)B, (long long)H, (long long)S);
+  if (D != 64 && D != 128 && D != 256)
+    return fail(ATTN_ERR_UNSUPPORTED_HEAD_DIM, "head_dim %lld not supported; must be one of 64, 128, 256",
+                (long long)D);
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16)
+    return fail(ATTN_ERR_UNSUPPORTED_DTYPE, "dtype %d not supported; must be ATTN_F16 (0) or ATTN_BF16 (1)",
+                dtype);
+  // The kernel indexes rows with 32-bit ints and elements with 64-bit ints;
+  // keep S*D and the element count well inside both.
+  const int64_t lim = (int64_t)1 << 31;
+  if (S >= lim / D)
+    return fail(ATTN_ERR_BAD_SHAPE, "S=%lld too large for head_dim %lld", (long long)S, (long long)D);
+  if (B > 0 && H > 0 && S > 0) {
+    const int64_t bh_lim = ((int64_t)1 << 62) / (S * D);
+    if (H > bh_lim / (B > 0 ? B : 1) || B * H > bh_lim)
+      return fail(ATTN_ERR_BAD_SHAPE, "B*H*S*D overflows");
+  }
+  return ATTN_OK;
+}
+
+int plan_for(int64_t B, int64_t H, int64_t S, int64_t D, attn_fwd_plan_t* p) {
+  switch (D) {
+    case 64: fill_plan<Cfg64>(B, H, S, p); break;
+    case 128: fill_plan<Cfg128>(B, H, S, p); break;
+    default: fill_plan<Cfg256>(B, H, S, p); break;
+  }
+  if (p->num_workgroups > (int64_t)0x7FFFFFFF)
+    return fail(ATTN_ERR_BAD_SHAPE, "grid of %lld workgroups exceeds the launch limit",
+                (long long)p->num_workgroups);
+  return ATTN_OK;
+}
+
+bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
+// gfx950 check, cached per device.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 yes, 2 no
+
+int check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0)
+    return fail(ATTN_ERR_UNSUPPORTED_DEVICE, "no current HIP device (%s)", hipGetErrorString(e));
+  int state = dev < kMaxDevices ? g_arch_ok[dev].load(std::memory_order_relaxed) : 0;
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+      return fail(ATTN_ERR_UNSUPPORTED_DEVICE, "hipGetDeviceProperties failed (%s)", hipGetErrorString(e));
+    state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    if (dev < kMaxDevices) g_arch_ok[dev].store(state, std::memory_order_relaxed);
+    if (state == 2)
+      return fail(ATTN_ERR_UNSUPPORTED_DEVICE, "device %d is %s; this library is built for gfx950 only", dev,
+                  prop.gcnArchName);
+  }
+  if (state == 2) return fail(ATTN_ERR_UNSUPPORTED_DEVICE, "device %d is not gfx950", dev);
+  return ATTN_OK;
+}
+
+template <class C, bool CAUSAL, int DT>
+int launch(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+           int64_t S, float c, hipStream_t stream) {
+  const int64_t nq = (S + C::BM - 1) / C::BM;
+  const int64_t G = nq * B * H;
+  hipLaunchKernelGGL((attn::attn_fwd_kernel<C, CAUSAL, DT>), dim3((unsigned)G), dim3(C::NT), 0, stream,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, (int)S,
+                     (int)nq, G, c);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(ATTN_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+template <class C>
+int dispatch(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+             int64_t S, float c, bool causal, int dtype, hipStream_t st) {
+  if (dtype == ATTN_F16)
+    return causal ? launch<C, true, attn::DT_F16>(q, k, v, o, lse, B, H, S, c, st)
+                  : launch<C, false, attn::DT_F16>(q, k, v, o, lse, B, H, S, c, st);
+  return causal ? launch<C, true, attn::DT_BF16>(q, k, v, o, lse, B, H, S, c, st)
+                : launch<C, false, attn::DT_BF16>(q, k, v, o, lse, B, H, S, c, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+             int64_t S, int64_t D, float scale, int causal, int dtype, void* stream) {
+  int st = check_sizes(B, H, S, D, dtype);
+  if (st != ATTN_OK) return st;
+  if (!(std::isfinite(scale) && scale >= 0.f))
+    return fail(ATTN_ERR_BAD_SCALE, "scale must be finite and >= 0 (got %g)", (double)scale);
+  if (B == 0 || H == 0 || S == 0) return ok();  // empty: nothing to compute
+  if (!q || !k || !v || !o || !lse) return fail(ATTN_ERR_NULL_PTR, "q, k, v, o and lse must be non-NULL");
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15)
+    return fail(ATTN_ERR_MISALIGNED, "q, k, v and o must be 16-byte aligned");
+  if ((uintptr_t)lse & 3) return fail(ATTN_ERR_MISALIGNED, "lse must be 4-byte aligned");
+  const int64_t nbytes = B * H * S * D * 2, lbytes = B * H * S * 4;
+  if (overlaps(o, nbytes, q, nbytes) || overlaps(o, nbytes, k, nbytes) || overlaps(o, nbytes, v, nbytes) ||
+      overlaps(o, nbytes, lse, lbytes))
+    return fail(ATTN_ERR_ALIASING, "o overlaps q, k, v or lse");
+  if (overlaps(lse, lbytes, q, nbytes) || overlaps(lse, lbytes, k, nbytes) || overlaps(lse, lbytes, v, nbytes))
+    return fail(ATTN_ERR_ALIASING, "lse overlaps q, k or v");
+  attn_fwd_plan_t plan;
+  st = plan_for(B, H, S, D, &plan);
+  if (st != ATTN_OK) return st;
+  st = check_device();
+  if (st != ATTN_OK) return st;
+
+  // scale * log2(e), kept >= FLT_MIN: a masked score (-inf) times c must stay
+  // -inf, never NaN, and for scale == 0 every kept score times FLT_MIN is far
+  // below one ulp of the row max, so the softmax is exactly uniform.
+  float c = (float)((double)scale * 1.4426950408889634074);
+  if (c < FLT_MIN) c = FLT_MIN;
+  hipStream_t hs = (hipStream_t)stream;
+  const bool cz = causal != 0;
+  switch (D) {
+    case 64: return dispatch<Cfg64>(q, k, v, o, lse, B, H, S, c, cz, dtype, hs);
+    case 128: return dispatch<Cfg128>(q, k, v, o, lse, B, H, S, c, cz, dtype, hs);
+    default: return dispatch<Cfg256>(q, k, v, o, lse, B, H, S, c, cz, dtype, hs);
+  }
+}
+
+int attn_fwd_plan(int64_t B, int64_t H, int64_t S, int64_t D, int causal, int dtype, attn_fwd_plan_t* out) {
+  (void)causal;
+  if (!out) return fail(ATTN_ERR_NULL_PTR, "out must be non-NULL");
+  int st = check_sizes(B, H, S, D, dtype);
+  if (st != ATTN_OK) return st;
+  st = plan_for(B, H, S, D, out);
+  if (st != ATTN_OK) return st;
+  return ok();
+}
+
+int attn_fwd_workgroup_tile(int64_t B, int64_t H, int64_t S, int64_t D, int causal, int dtype, int64_t wg,
+                            int64_t* q_tile, int64_t* bh) {
+  if (!q_tile || !bh) return fail(ATTN_ERR_NULL_PTR, "q_tile and bh must be non-NULL");
+  attn_fwd_plan_t p;
+  int st = attn_fwd_plan(B, H, S, D, causal, dtype, &p);
+  if (st != ATTN_OK) return st;
+  if (wg < 0 || wg >= p.num_workgroups)
+    return fail(ATTN_ERR_BAD_ARGUMENT, "workgroup %lld outside [0, %lld)", (long long)wg,
+                (long long)p.num_workgroups);
+  attn::workgroup_tile(wg, p.num_workgroups, p.num_q_tiles, causal != 0, q_tile, bh);
+  return ok();
+}
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL_PTR: return "null pointer";
+    case ATTN_ERR_BAD_SHAPE: return "bad shape";
+    case ATTN_ERR_UNSUPPORTED_HEAD_DIM: return "unsupported head dim";
+    case ATTN_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype";
+    case ATTN_ERR_MISALIGNED: return "misaligned pointer";
+    case ATTN_ERR_BAD_SCALE: return "bad scale";
+    case ATTN_ERR_ALIASING: return "aliasing buffers";
+    case ATTN_ERR_UNSUPPORTED_DEVICE: return "unsupported device";
+    case ATTN_ERR_LAUNCH: return "launch failed";
+    case ATTN_ERR_BAD_ARGUMENT: return "bad argument";
+    default: return "unknown status";
+  }
+}
+
+const char* attn_last_error(void) { return g_last_error.c_str(); }
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,414 @@
+// attn_fwd_kernel.hpp -- gfx950 (CDNA4) kernel of the exact attention forward.
+//
+// Computes, per (batch*head, query tile), O = softmax(scale * Q K^T, causal
+// mask) V and LSE with an online softmax: a running max m and running sum l
+// per query row, the partial output rescaled when m grows, and the final
+// O = O_acc / l, LSE = m + log l (docs.rs page "oxicuda-dnn 0.1.8,
+// src/attn/flash_attn/hopper.rs", doc comment of
+// FlashAttention3Plan::generate_forward).
+//
+// MI355X mapping (differs from the page's Hopper design on purpose):
+//   * One workgroup per (query tile of BM = 32*QW rows, b*H + h).  QW*KW waves
+//     of 64 lanes: wave (qw, kw) owns 32 query rows and the kw-th 1/KW slice
+//     of every key tile.  The Q fragment of a wave lives in VGPRs for the
+//     whole kernel; O and (m, l) live in VGPRs (the page keeps them in shared
+//     memory).
+//   * The score block is computed transposed, S^T = K Q^T, with
+//     v_mfma_f32_32x32x16_{f16,bf16}: lane l then holds 16 scores of the
+//     single query column l%32 per 32-key block, so the row max/sum is an
+//     in-register reduction plus one exchange between lane l and l^32, and
+//     the rescale of O^T by exp2(m_old - m_new) is one scalar per lane.
+//   * The probabilities, packed to 16 bits, are already the B operand of the
+//     second contraction O^T += V^T P^T: no LDS round trip for P.  For that,
+//     V is stored transposed in LDS (d-major) with bits 2 and 3 of each key
+//     index swapped, which lines up the key order of the packed P registers
+//     with the 8 contiguous keys each lane reads for the A operand.
+//   * K and V^T tiles stream through two LDS stages: tile j+1 is fetched
+//     from HBM into VGPRs with 16-byte coalesced loads while tile j is
+//     computed, then stored into the other stage; one workgroup barrier per
+//     tile.
+//   * exp2/log2 are the hardware v_exp_f32/v_log_f32 with the scale folded
+//     as c = scale*log2(e); P and O are rounded to nearest-even.
+//   * Causal: key tiles wholly after a wave's last query are skipped, and
+//     only tiles crossing the diagonal (or the ragged end) are masked.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+enum { DT_F16 = 0, DT_BF16 = 1 };
+
+// ---------------------------------------------------------------------------
+// Element-type helpers
+// ---------------------------------------------------------------------------
+template <int DT>
+struct Elem;
+
+template <>
+struct Elem<DT_F16> {
+  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  // Two fp32 values -> packed 16-bit pair, round to nearest even.
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    f16x2 v;
+    v[0] = (_Float16)lo;
+    v[1] = (_Float16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+  }
+};
+
+template <>
+struct Elem<DT_BF16> {
+  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    bf16x2 v;
+    v[0] = (__bf16)lo;
+    v[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Tile configuration
+// ---------------------------------------------------------------------------
+template <int D_, int QW_, int KW_, int BN_>
+struct TileCfg {
+  static constexpr int D = D_;
+  static constexpr int QW = QW_;             // waves along query rows
+  static constexpr int KW = KW_;             // waves along each key tile
+  static constexpr int BN = BN_;             // keys per tile
+  static constexpr int BM = 32 * QW;         // query rows per workgroup
+  static constexpr int NW = QW * KW;         // waves per workgroup
+  static constexpr int NT = 64 * NW;         // threads per workgroup
+  static constexpr int KSUB = BN / KW;       // keys per wave per tile
+  static constexpr int NB = KSUB / 32;       // 32-key blocks per wave per tile
+  static constexpr int DK = D / 16;          // k-steps of the score MFMA
+  static constexpr int DB = D / 32;          // 32-row blocks of O^T
+  static constexpr int KSTR = D + 8;         // K tile row stride (halves)
+  static constexpr int VSTR = BN + 8;        // V^T tile row stride (halves)
+  static constexpr int K_HALVES = BN * KSTR;
+  static constexpr int V_HALVES = D * VSTR;
+  static constexpr int STAGE_HALVES = K_HALVES + V_HALVES;
+  static constexpr int STAGES = 2;
+  static constexpr int KV_LDS_BYTES = STAGES * STAGE_HALVES * 2;
+  // partial (O^T, l, m) of the waves with kw > 0, for the final merge
+  static constexpr int MERGE_FLOATS = (KW - 1) * QW * (D / 2 + 2) * 64;
+  static constexpr int LDS_BYTES =
+      KV_LDS_BYTES > MERGE_FLOATS * 4 ? KV_LDS_BYTES : MERGE_FLOATS * 4;
+  static constexpr int K_CHUNKS = BN * D / 8;         // 16-byte chunks of K
+  static constexpr int K_PER_THREAD = K_CHUNKS / NT;
+  static constexpr int V_UNITS = (BN / 4) * (D / 8);  // 4 keys x 8 d blocks
+  static constexpr int V_PER_THREAD = V_UNITS / NT;
+
+  static_assert(D % 32 == 0, "head dim must be a multiple of 32");
+  static_assert(KSUB % 32 == 0 && NB >= 1, "each wave needs whole 32-key blocks");
+  static_assert(K_CHUNKS % NT == 0, "K tile must split evenly over threads");
+  static_assert(V_UNITS % NT == 0, "V tile must split evenly over threads");
+  static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per CU");
+};
+
+// Swap bits 2 and 3 of a key index: the position of key k inside a V^T row.
+__device__ __forceinline__ int vt_pos(int k) {
+  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
+
+// Workgroup id -> (query tile, b*H + h).  Workgroups are handed to the 8 XCDs
+// round-robin, so id g runs on XCD g % 8 as that XCD's (g / 8)-th workgroup.
+// Give each XCD a contiguous run of logical work (whole heads where the counts
+// allow), in head order, and start every head with its heaviest causal tile.
+__host__ __device__ inline void workgroup_tile(int64_t g, int64_t G, int64_t nq, int causal,
+                                               int64_t* tile, int64_t* bh) {
+  const int64_t X = 8;
+  const int64_t xcd = g % X, slot = g / X;
+  const int64_t base = G / X, rem = G % X;
+  const int64_t logical = xcd * base + (xcd < rem ? xcd : rem) + slot;
+  *bh = logical / nq;
+  const int64_t t = logical % nq;
+  *tile = causal ? nq - 1 - t : t;
+}
+
+// ---------------------------------------------------------------------------
+// The kernel
+// ---------------------------------------------------------------------------
+template <class C, bool CAUSAL, int DT>
+__global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
+    int S, int nq, int64_t G, float c /* scale * log2(e) */) {
+  using E = Elem<DT>;
+  constexpr int D = C::D, BN = C::BN, BM = C::BM, NB = C::NB, DK = C::DK, DB = C::DB;
+  constexpr int KSTR = C::KSTR, VSTR = C::VSTR;
+
+  __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_BYTES / 2];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qw = wave % C::QW;
+  const int kw = wave / C::QW;
+  const int col = lane & 31;   // query column of this lane in S^T / O^T
+  const int half = lane >> 5;  // which 8-element k-slice this lane supplies
+
+  int64_t tile64, bh64;
+  workgroup_tile(blockIdx.x, G, nq, CAUSAL, &tile64, &bh64);
+  const int q0 = (int)tile64 * BM;
+  const int64_t head = bh64 * (int64_t)S * D;
+  const uint16_t* qh = q + head;
+  const uint16_t* kh = k + head;
+  const uint16_t* vh = v + head;
+
+  const int wq_first = q0 + qw * 32;  // first query row of this wave
+  const int wq_last = wq_first + 31;
+  const int my_q = wq_first + col;
+  const int kbase = kw * C::KSUB;     // this wave's key offset inside a tile
+
+  // ---- Q fragment, resident for the whole kernel (B operand of S^T) ----
+  u32x4 qf[DK];
+  {
+    const bool ok = my_q < S;
+    const uint16_t* qr = qh + (int64_t)(ok ? my_q : 0) * D + half * 8;
+#pragma unroll
+    for (int kc = 0; kc < DK; ++kc) {
+      u32x4 t = *reinterpret_cast<const u32x4*>(qr + kc * 16);
+      qf[kc] = ok ? t : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  // ---- number of key tiles this workgroup visits ----
+  const int q_end = (q0 + BM < S) ? q0 + BM : S;
+  const int n_tiles = CAUSAL ? (q_end + BN - 1) / BN : (S + BN - 1) / BN;
+
+  // ---- staging registers for the next K/V tile ----
+  u32x4 kst[C::K_PER_THREAD];
+  u32x4 vst[C::V_PER_THREAD][4];
+
+  auto fetch = [&](int kv0) {
+#pragma unroll
+    for (int r = 0; r < C::K_PER_THREAD; ++r) {
+      const int ch = tid + r * C::NT;
+      const int row = ch / (D / 8), c8 = ch % (D / 8);
+      const int key = kv0 + row;
+      const bool ok = key < S;
+      u32x4 t = *reinterpret_cast<const u32x4*>(kh + (int64_t)(ok ? key : 0) * D + c8 * 8);
+      kst[r] = ok ? t : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int r = 0; r < C::V_PER_THREAD; ++r) {
+      const int u = tid + r * C::NT;
+      const int kg = u / (D / 8), dc = u % (D / 8);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = kv0 + kg * 4 + e;
+        const bool ok = key < S;
+        u32x4 t = *reinterpret_cast<const u32x4*>(vh + (int64_t)(ok ? key : 0) * D + dc * 8);
+        vst[r][e] = ok ? t : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+
+  auto store = [&](int stage) {
+    uint16_t* ks = lds + stage * C::STAGE_HALVES;
+    uint16_t* vs = ks + C::K_HALVES;
+#pragma unroll
+    for (int r = 0; r < C::K_PER_THREAD; ++r) {
+      const int ch = tid + r * C::NT;
+      const int row = ch / (D / 8), c8 = ch % (D / 8);
+      *reinterpret_cast<u32x4*>(ks + row * KSTR + c8 * 8) = kst[r];
+    }
+#pragma unroll
+    for (int r = 0; r < C::V_PER_THREAD; ++r) {
+      const int u = tid + r * C::NT;
+      const int kg = u / (D / 8), dc = u % (D / 8);
+      const int pos = vt_pos(kg * 4);
+      // transpose the 4 keys x 8 d block: row d gets the 4 keys' values
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t a0 = vst[r][0][w], a1 = vst[r][1][w];
+        const uint32_t a2 = vst[r][2][w], a3 = vst[r][3][w];
+        u32x2 lo, hi;
+        lo[0] = (a0 & 0xFFFFu) | (a1 << 16);
+        lo[1] = (a2 & 0xFFFFu) | (a3 << 16);
+        hi[0] = (a0 >> 16) | (a1 & 0xFFFF0000u);
+        hi[1] = (a2 >> 16) | (a3 & 0xFFFF0000u);
+        const int d = dc * 8 + 2 * w;
+        *reinterpret_cast<u32x2*>(vs + d * VSTR + pos) = lo;
+        *reinterpret_cast<u32x2*>(vs + (d + 1) * VSTR + pos) = hi;
+      }
+    }
+  };
+
+  // ---- running state (per lane: one query column) ----
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
+  float m_run = -__builtin_inff();  // running max of scale*log2(e)*s
+  float l_run = 0.f;                // partial running sum (this lane's keys)
+
+  if (n_tiles > 0) {
+    fetch(0);
+    store(0);
+  }
+  __syncthreads();
+
+  for (int j = 0; j < n_tiles; ++j) {
+    const int stage = j & 1;
+    const bool has_next = j + 1 < n_tiles;
+    if (has_next) fetch((j + 1) * BN);
+
+    const int kv0 = j * BN + kbase;  // first key of this wave's slice
+    const bool active = kv0 < S && (!CAUSAL || kv0 <= wq_last) && wq_first < S;
+    if (active) {
+      const uint16_t* ks = lds + stage * C::STAGE_HALVES;
+      const uint16_t* vs = ks + C::K_HALVES;
+
+      // S^T = K Q^T for this wave's NB key blocks
+      f32x16 sacc[NB];
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb) {
+        sacc[kb] = f32x16{};
+        const uint16_t* kr = ks + (kbase + kb * 32 + col) * KSTR + half * 8;
+#pragma unroll
+        for (int kc = 0; kc < DK; ++kc) {
+          u32x4 a = *reinterpret_cast<const u32x4*>(kr + kc * 16);
+          sacc[kb] = E::mfma(a, qf[kc], sacc[kb]);
+        }
+      }
+
+      // mask keys past the end or after the query (diagonal / ragged tiles)
+      const bool need_mask = (kv0 + C::KSUB > S) || (CAUSAL && kv0 + C::KSUB - 1 > wq_first);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kv0 + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+            const bool dead = key >= S || (CAUSAL && key > my_q);
+            sacc[kb][i] = dead ? -__builtin_inff() : sacc[kb][i];
+          }
+        }
+      }
+
+      // row max over this tile (in registers, then across the lane pair)
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+
+      const float mt = (mx == -__builtin_inff()) ? mx : mx * c;
+      const float m_new = fmaxf(m_run, mt);
+      const float m_ref = (m_new == -__builtin_inff()) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
+      m_run = m_new;
+
+      // P = exp2(c*s - m), partial row sums, pack to 16 bits
+      u32x4 pf[2 * NB];
+      float ls = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          float p[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * s2 + t], c, -m_ref));
+            ls += p[t];
+          }
+          pf[2 * kb + s2] = u32x4{E::pack2(p[0], p[1]), E::pack2(p[2], p[3]),
+                                  E::pack2(p[4], p[5]), E::pack2(p[6], p[7])};
+        }
+      }
+      l_run = l_run * alpha + ls;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+
+      // O^T += V^T P^T
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const uint16_t* vr = vs + (db * 32 + col) * VSTR + kbase + half * 8;
+#pragma unroll
+        for (int ks = 0; ks < 2 * NB; ++ks) {
+          u32x4 a = *reinterpret_cast<const u32x4*>(vr + ks * 16);
+          oacc[db] = E::mfma(a, pf[ks], oacc[db]);
+        }
+      }
+    }
+
+    if (has_next) store(stage ^ 1);
+    __syncthreads();
+  }
+
+  // ---- merge the key-split waves (KW > 1) ----
+  if constexpr (C::KW > 1) {
+    float* mg = reinterpret_cast<float*>(lds);
+    constexpr int FIELDS = D / 2 + 2;
+    if (kw > 0) {
+      float* dst = mg + ((kw - 1) * C::QW + qw) * FIELDS * 64;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dst[(db * 16 + i) * 64 + lane] = oacc[db][i];
+      dst[(D / 2) * 64 + lane] = l_run;
+      dst[(D / 2 + 1) * 64 + lane] = m_run;
+    }
+    __syncthreads();
+    if (kw > 0) return;
+#pragma unroll
+    for (int w = 1; w < C::KW; ++w) {
+      const float* src = mg + ((w - 1) * C::QW + qw) * FIELDS * 64;
+      const float lb = src[(D / 2) * 64 + lane];
+      const float mb = src[(D / 2 + 1) * 64 + lane];
+      const float mm = fmaxf(m_run, mb);
+      const float mref = (mm == -__builtin_inff()) ? 0.f : mm;
+      const float fa = __builtin_amdgcn_exp2f(m_run - mref);
+      const float fb = __builtin_amdgcn_exp2f(mb - mref);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          oacc[db][i] = oacc[db][i] * fa + src[(db * 16 + i) * 64 + lane] * fb;
+      l_run = l_run * fa + lb * fb;
+      m_run = mm;
+    }
+  }
+
+  // ---- epilogue: O = O_acc / l (RNE to 16 bits), LSE = (m + log2 l) ln 2 ----
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (my_q < S) {
+    const float inv = 1.0f / l_tot;
+    uint16_t* orow = o + head + (int64_t)my_q * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = db * 32 + 8 * g + 4 * half;
+        u32x2 w;
+        w[0] = E::pack2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv);
+        w[1] = E::pack2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+        *reinterpret_cast<u32x2*>(orow + d) = w;
+      }
+    }
+    if (half == 0) {
+      lse[bh64 * (int64_t)S + my_q] =
+          (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f;
+    }
+  }
+}
+
+}  // namespace attn

@@ -1,0 +1,135 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) exact attention forward library.
+ *
+ * The operation is the fused, tiled, exact scaled-dot-product attention
+ * forward described on the docs.rs page "oxicuda-dnn 0.1.8,
+ * src/attn/flash_attn/hopper.rs" (doc comment of
+ * FlashAttention3Plan::generate_forward): scores S = Q K^T scaled by the
+ * softmax scale, future positions removed when causal, an online softmax with
+ * a running max m and running sum l, O = (P V) / l, and the per-row
+ * log-sum-exp m + log(l).  The S x S score matrix never reaches memory.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are dense and contiguous, C order: Q, K, V, O are [B, H, S, D]
+ *     of 16-bit elements (fp16 or bf16, chosen by `dtype`); LSE is [B, H, S]
+ *     of fp32.  The caller owns every buffer; the library allocates no device
+ *     memory and keeps no pointer after a call returns.
+ *   - Causal keeps key j for query i iff j <= i (Sq == Skv == S).
+ *   - LSE is the natural logarithm of sum_j exp(scale * q_i . k_j) over the
+ *     kept keys.
+ *   - Status codes are returned, never thrown; attn_last_error() gives a
+ *     thread-local text for the most recent failure on the calling thread.
+ *   - All argument checks happen before any HIP call.  A failed check
+ *     launches nothing and leaves o and lse untouched.
+ */
+#ifndef EXACT_ATTENTION_52_AMD_ATTN_H
+#define EXACT_ATTENTION_52_AMD_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+
+/* Element type of Q, K, V and O.  The page restricts the float type to F16 or
+ * BF16 (validate_config, "float_type must be F16 or BF16"). */
+typedef enum { ATTN_F16 = 0, ATTN_BF16 = 1 } attn_dtype_t;
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL_PTR = 1,              /* a required pointer is NULL          */
+  ATTN_ERR_BAD_SHAPE = 2,             /* B, H or S < 0, or sizes overflow    */
+  ATTN_ERR_UNSUPPORTED_HEAD_DIM = 3,  /* D not in {64, 128, 256}             */
+  ATTN_ERR_UNSUPPORTED_DTYPE = 4,     /* dtype not ATTN_F16 / ATTN_BF16      */
+  ATTN_ERR_MISALIGNED = 5,            /* q/k/v/o not 16-B, lse not 4-B       */
+  ATTN_ERR_BAD_SCALE = 6,             /* scale NaN, infinite or negative     */
+  ATTN_ERR_ALIASING = 7,              /* an output overlaps another buffer   */
+  ATTN_ERR_UNSUPPORTED_DEVICE = 8,    /* current device is not gfx950        */
+  ATTN_ERR_LAUNCH = 9,                /* the HIP runtime refused the launch  */
+  ATTN_ERR_BAD_ARGUMENT = 10          /* any other invalid argument          */
+} attn_status_t;
+
+/*
+ * attn_fwd -- O = softmax(scale * Q K^T [+ causal mask]) V and LSE.
+ *
+ * Defined by the doc comment of FlashAttention3Plan::generate_forward on the
+ * page named above (Q K^T, online softmax with running max and sum, optional
+ * causal removal of future positions, O = O_acc / l, LSE = m + log(l)); its
+ * kernel parameters (q, k, v, o, lse pointers, sequence length, head_dim,
+ * num_heads, sm_scale) are the ones taken here, with batch and heads as
+ * explicit sizes instead of strides.
+ *
+ *   q, k, v  device pointers, [B,H,S,D] `dtype` elements, read only; they may
+ *            alias one another.  16-byte aligned.
+ *   o        device pointer, [B,H,S,D] `dtype`, written in full (each element
+ *            rounded to nearest-even from the fp32 result).  16-byte aligned;
+ *            must not overlap q, k, v or lse.
+ *   lse      device pointer, [B,H,S] fp32, written in full.  4-byte aligned;
+ *            must not overlap q, k, v or o.
+ *   B, H, S  batch, heads, sequence length (>= 0; any S, no multiple needed).
+ *            B*H*S == 0 is a valid empty call: nothing is launched.
+ *   D        head dimension: 64, 128 or 256 (the page's supported set).
+ *   scale    softmax scale applied to Q K^T; finite and >= 0 (0 gives a
+ *            uniform softmax over the kept keys).
+ *   causal   0 or 1 (any non-zero value means 1).
+ *   dtype    ATTN_F16 or ATTN_BF16.
+ *   stream   hipStream_t to enqueue on; NULL means the null stream.
+ *
+ * Returns ATTN_OK once the kernel is enqueued (asynchronous: no
+ * synchronisation happens), else an attn_status_t code.  Reentrant and
+ * thread-safe.  The result is deterministic: every output element is written
+ * by exactly one workgroup with a fixed order of arithmetic.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int64_t B, int64_t H, int64_t S, int64_t D, float scale,
+             int causal, int dtype, void* stream);
+
+/*
+ * attn_fwd_plan -- the launch geometry attn_fwd would use (host only, no HIP
+ * call, no device needed).  Mirrors the page's launch_params: one workgroup
+ * per (query tile, batch*head), num_q_tiles = ceil(S / block_m); the key
+ * length changes the loop trip count, not the grid.
+ */
+typedef struct {
+  int64_t block_m;               /* query rows per workgroup               */
+  int64_t block_n;               /* keys per K/V tile                      */
+  int64_t kv_stages;             /* LDS buffers for K/V tiles              */
+  int64_t waves_q;               /* waves splitting the query rows         */
+  int64_t waves_k;               /* waves splitting each key tile          */
+  int64_t threads_per_workgroup; /* 64 * waves_q * waves_k                 */
+  int64_t lds_bytes;             /* LDS per workgroup                      */
+  int64_t num_q_tiles;           /* ceil(S / block_m)                      */
+  int64_t num_workgroups;        /* num_q_tiles * B * H                    */
+} attn_fwd_plan_t;
+
+/* Returns ATTN_OK and fills *out, or a status code for invalid sizes,
+ * head dim or dtype (same rules as attn_fwd), or ATTN_ERR_NULL_PTR. */
+int attn_fwd_plan(int64_t B, int64_t H, int64_t S, int64_t D, int causal,
+                  int dtype, attn_fwd_plan_t* out);
+
+/*
+ * attn_fwd_workgroup_tile -- which (query tile, b*H + h) the workgroup with
+ * linear id `wg` (0 <= wg < num_workgroups) computes (host only).  The map is
+ * a bijection; it keeps the tiles of one head on one XCD and, when causal,
+ * starts each head with its heaviest (last) query tile.
+ */
+int attn_fwd_workgroup_tile(int64_t B, int64_t H, int64_t S, int64_t D,
+                            int causal, int dtype, int64_t wg,
+                            int64_t* q_tile, int64_t* bh);
+
+/* Static text for a status code ("unknown status" for others). */
+const char* attn_status_string(int status);
+
+/* Detail of the last non-OK return on this thread ("" if none). */
+const char* attn_last_error(void);
+
+/* ATTN_ABI_VERSION of the loaded library. */
+int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTENTION_52_AMD_ATTN_H */

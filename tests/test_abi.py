@@ -1,0 +1,178 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, plans
+launches like the page's launch_params, maps workgroups bijectively, and
+rejects every invalid argument before any HIP call."""
+import json
+import os
+import re
+
+import pytest
+
+import exact_attention_52_amd as ea
+from exact_attention_52_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "attn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = _lib.load()
+    names = declared_functions()
+    assert names, "no declarations parsed"
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.attn_abi_version() == _lib.ABI_VERSION
+    # no torch types cross the ABI: the header holds only C types
+    hdr = open(os.path.join(ROOT, "include", "attn.h")).read()
+    assert "torch" not in hdr.lower().replace("pytorch", "")
+
+
+def test_exported_symbols_in_dynamic_table():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    syms = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    for n in declared_functions():
+        assert n in syms
+
+
+def test_status_strings():
+    for code in _lib.STATUS:
+        assert _lib.status_string(code) != "unknown status"
+    assert _lib.status_string(999) == "unknown status"
+
+
+def test_launch_geometry_matches_page():
+    g = json.load(open(os.path.join(GOLDEN, "launch_geometry.json")))
+    # the D=64 instance uses the page's 128-row query tile
+    p = ea.attn_fwd_plan(1, 1, 128, 64, False, 0)
+    assert p["block_m"] == g["block_m"]
+    for c in g["cases"]:
+        p = ea.attn_fwd_plan(c["batch"], c["heads"], c["seq_len_q"], 64, False, 0)
+        assert p["num_q_tiles"] == c["grid_x"]
+        assert p["num_workgroups"] == c["grid_x"] * c["grid_y"]
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("S", [1, 63, 64, 65, 300, 1024, 8192])
+def test_plan_rules(D, S):
+    p = ea.attn_fwd_plan(3, 5, S, D, True, 1)
+    bm = p["block_m"]
+    assert p["num_q_tiles"] == -(-S // bm)
+    assert p["num_workgroups"] == p["num_q_tiles"] * 15
+    assert p["threads_per_workgroup"] == 64 * p["waves_q"] * p["waves_k"]
+    assert bm == 32 * p["waves_q"]
+    assert p["lds_bytes"] <= 160 * 1024
+    assert p["kv_stages"] == 2
+    if D == 256:
+        assert bm == 64  # the 64-row query tile of the D=256 workload
+
+
+def test_supported_and_rejected_head_dims_and_types():
+    g = json.load(open(os.path.join(GOLDEN, "launch_geometry.json")))
+    for D in g["supported_head_dims"]:
+        ea.attn_fwd_plan(1, 1, 128, D, False, 0)
+    for D in g["rejected_head_dims"] + [0, 32, 512, -64]:
+        with pytest.raises(_lib.AttnError) as e:
+            ea.attn_fwd_plan(1, 1, 128, D, False, 0)
+        assert e.value.status == 3 and "head_dim" in e.value.detail
+    for dt in (2, -1, 7):
+        with pytest.raises(_lib.AttnError) as e:
+            ea.attn_fwd_plan(1, 1, 128, 64, False, dt)
+        assert e.value.status == 4
+
+
+@pytest.mark.parametrize("D,causal", [(64, False), (64, True), (128, True), (256, True), (128, False)])
+@pytest.mark.parametrize("B,H,S", [(1, 1, 1), (2, 3, 1000), (1, 8, 8192), (3, 1, 257)])
+def test_workgroup_map_is_bijection_and_heavy_first(B, H, S, D, causal):
+    p = ea.attn_fwd_plan(B, H, S, D, causal, 0)
+    G, nq = p["num_workgroups"], p["num_q_tiles"]
+    seen = set()
+    last = {}
+    for wg in range(G):
+        t, bh = ea.attn_fwd_workgroup_tile(B, H, S, D, causal, 0, wg)
+        assert 0 <= t < nq and 0 <= bh < B * H
+        seen.add((t, bh))
+        if causal:
+            # on each XCD (wg % 8) a head's tiles come heaviest (last) first
+            key = (wg % 8, bh)
+            assert last.get(key, nq) > t
+            last[key] = t
+    assert len(seen) == G
+    if causal:
+        t0, _ = ea.attn_fwd_workgroup_tile(B, H, S, D, causal, 0, 0)
+        assert t0 == nq - 1
+    with pytest.raises(_lib.AttnError):
+        ea.attn_fwd_workgroup_tile(B, H, S, D, causal, 0, G)
+
+
+def test_workgroup_map_keeps_heads_on_one_xcd():
+    # 512 workgroups (16 tiles x 32 heads): XCD x = wg % 8 owns heads 4x..4x+3
+    B, H, S, D = 2, 16, 4096, 128
+    for wg in range(512):
+        _, bh = ea.attn_fwd_workgroup_tile(B, H, S, D, False, 0, wg)
+        assert bh // 4 == wg % 8
+
+
+FAKE = 0x10000  # never dereferenced: every case below fails before any HIP call
+
+
+def call(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, o=FAKE + 0x300000, lse=FAKE + 0x400000,
+         B=1, H=1, S=16, D=64, scale=0.125, causal=0, dtype=0):
+    return _lib.attn_fwd(q, k, v, o, lse, B, H, S, D, scale, causal, dtype, 0)
+
+
+@pytest.mark.parametrize("kwargs,status,word", [
+    (dict(q=0), 1, "NULL"),
+    (dict(lse=0), 1, "NULL"),
+    (dict(B=-1), 2, "B, H and S"),
+    (dict(S=-5), 2, "B, H and S"),
+    (dict(S=1 << 30), 2, "too large"),
+    (dict(B=1 << 40, H=1 << 20), 2, "overflow"),
+    (dict(D=96), 3, "head_dim"),
+    (dict(dtype=2), 4, "dtype"),
+    (dict(q=FAKE + 8), 5, "16-byte"),
+    (dict(o=FAKE + 0x300002), 5, "16-byte"),
+    (dict(lse=FAKE + 0x400002), 5, "4-byte"),
+    (dict(scale=float("nan")), 6, "scale"),
+    (dict(scale=float("inf")), 6, "scale"),
+    (dict(scale=-0.5), 6, "scale"),
+    (dict(o=FAKE), 7, "overlaps"),
+    (dict(o=FAKE + 0x100000 + 16), 7, "overlaps"),
+    (dict(lse=FAKE + 0x300000 + 64), 7, "overlaps"),
+    (dict(lse=FAKE + 16), 7, "overlaps"),
+])
+def test_invalid_arguments_rejected_before_launch(kwargs, status, word):
+    st = call(**kwargs)
+    assert st == status, (st, _lib.last_error())
+    assert word.lower() in _lib.last_error().lower()
+
+
+def test_empty_inputs_are_a_noop():
+    for kw in (dict(B=0), dict(H=0), dict(S=0)):
+        assert call(q=0, k=0, v=0, o=0, lse=0, **kw) == 0
+        assert _lib.last_error() == ""
+
+
+def test_qkv_may_alias_each_other():
+    # q == k == v is legal (read-only); validation passes and only the device
+    # check (no GPU here) can fail
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("would launch on a real GPU with fake pointers")
+    st = call(q=FAKE, k=FAKE, v=FAKE)
+    assert st == 8, _lib.last_error()
+
+
+def test_no_gpu_reports_unsupported_device():
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present")
+    assert call() == 8
+    assert "device" in _lib.last_error()
