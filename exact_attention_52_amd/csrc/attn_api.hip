@@ -70,10 +70,10 @@ int check_sizes(int64_t B, int64_t H, int64_t S, int64_t D, int dtype) {
   if (dtype != ATTN_F16 && dtype != ATTN_BF16)
     return fail(ATTN_ERR_UNSUPPORTED_DTYPE, "dtype %d not supported; must be ATTN_F16 (0) or ATTN_BF16 (1)",
                 dtype);
-  // The kernel indexes rows with 32-bit ints and elements with 64-bit ints;
-  // keep S*D and the element count well inside both.
-  const int64_t lim = (int64_t)1 << 31;
-  if (S >= lim / D)
+  // Per-head offsets are 32-bit byte offsets (buffer loads); keep one head's
+  // S*D elements, plus a tile of padding, far inside that range.
+  const int64_t lim = (int64_t)1 << 30;
+  if (S > lim / D)
     return fail(ATTN_ERR_BAD_SHAPE, "S=%lld too large for head_dim %lld", (long long)S, (long long)D);
   if (B > 0 && H > 0 && S > 0) {
     const int64_t bh_lim = ((int64_t)1 << 62) / (S * D);

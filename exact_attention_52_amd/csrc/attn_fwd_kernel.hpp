@@ -67,6 +67,11 @@ struct Elem<DT_F16> {
     v[1] = (_Float16)hi;
     return __builtin_bit_cast(uint32_t, v);
   }
+  // acc + both 16-bit halves of a packed pair (v_dot2 with (1, 1))
+  static __device__ __forceinline__ float sum2(uint32_t pair, float acc) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), one, acc, false);
+  }
 };
 
 template <>
@@ -80,6 +85,10 @@ struct Elem<DT_BF16> {
     v[0] = (__bf16)lo;
     v[1] = (__bf16)hi;
     return __builtin_bit_cast(uint32_t, v);
+  }
+  static __device__ __forceinline__ float sum2(uint32_t pair, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
   }
 };
 
@@ -107,7 +116,7 @@ struct TileCfg {
   static constexpr int STAGES = 2;
   static constexpr int KV_LDS_BYTES = STAGES * STAGE_HALVES * 2;
   // partial (O^T, l, m) of the waves with kw > 0, for the final merge
-  static constexpr int MERGE_FLOATS = (KW - 1) * QW * (D / 2 + 2) * 64;
+  static constexpr int MERGE_FLOATS = (KW - 1) * QW * (D / 2 + 3) * 64;
   static constexpr int LDS_BYTES =
       KV_LDS_BYTES > MERGE_FLOATS * 4 ? KV_LDS_BYTES : MERGE_FLOATS * 4;
   static constexpr int K_CHUNKS = BN * D / 8;         // 16-byte chunks of K
@@ -126,6 +135,21 @@ struct TileCfg {
 __device__ __forceinline__ int vt_pos(int k) {
   return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
+
+// Buffer descriptor over one head's [S, D] slab: loads past `bytes` return
+// zero, which pads the ragged last tile without any select after the load.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0);
+}
+
+// Running-max hysteresis (log2 units): O, l are only rescaled when some row's
+// max grows by more than this; otherwise P is taken against the old max and
+// may reach 2^8, which fp16/bf16 P and fp32 sums hold exactly as well.
+constexpr float kRescaleSlack = 8.0f;
 
 // Workgroup id -> (query tile, b*H + h).  Workgroups are handed to the 8 XCDs
 // round-robin, so id g runs on XCD g % 8 as that XCD's (g / 8)-th workgroup.
@@ -168,9 +192,10 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
   workgroup_tile(blockIdx.x, G, nq, CAUSAL, &tile64, &bh64);
   const int q0 = (int)tile64 * BM;
   const int64_t head = bh64 * (int64_t)S * D;
-  const uint16_t* qh = q + head;
-  const uint16_t* kh = k + head;
-  const uint16_t* vh = v + head;
+  const uint32_t head_bytes = (uint32_t)S * D * 2;
+  const __amdgpu_buffer_rsrc_t qr = head_rsrc(q + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t kr = head_rsrc(k + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t vr = head_rsrc(v + head, head_bytes);
 
   const int wq_first = q0 + qw * 32;  // first query row of this wave
   const int wq_last = wq_first + 31;
@@ -180,13 +205,9 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
   // ---- Q fragment, resident for the whole kernel (B operand of S^T) ----
   u32x4 qf[DK];
   {
-    const bool ok = my_q < S;
-    const uint16_t* qr = qh + (int64_t)(ok ? my_q : 0) * D + half * 8;
+    const uint32_t off = (uint32_t)(my_q * D + half * 8) * 2;  // rows >= S read 0
 #pragma unroll
-    for (int kc = 0; kc < DK; ++kc) {
-      u32x4 t = *reinterpret_cast<const u32x4*>(qr + kc * 16);
-      qf[kc] = ok ? t : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int kc = 0; kc < DK; ++kc) qf[kc] = load16(qr, off + kc * 32);
   }
 
   // ---- number of key tiles this workgroup visits ----
@@ -197,27 +218,20 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
   u32x4 kst[C::K_PER_THREAD];
   u32x4 vst[C::V_PER_THREAD][4];
 
+  // keys >= S fall outside the head's buffer range and load as zeros
   auto fetch = [&](int kv0) {
+    const uint32_t tile_off = (uint32_t)kv0 * D * 2;
 #pragma unroll
     for (int r = 0; r < C::K_PER_THREAD; ++r) {
-      const int ch = tid + r * C::NT;
-      const int row = ch / (D / 8), c8 = ch % (D / 8);
-      const int key = kv0 + row;
-      const bool ok = key < S;
-      u32x4 t = *reinterpret_cast<const u32x4*>(kh + (int64_t)(ok ? key : 0) * D + c8 * 8);
-      kst[r] = ok ? t : u32x4{0u, 0u, 0u, 0u};
+      const int ch = tid + r * C::NT;  // 16-byte chunk of the row-major tile
+      kst[r] = load16(kr, tile_off + ch * 16);
     }
 #pragma unroll
     for (int r = 0; r < C::V_PER_THREAD; ++r) {
       const int u = tid + r * C::NT;
       const int kg = u / (D / 8), dc = u % (D / 8);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = kv0 + kg * 4 + e;
-        const bool ok = key < S;
-        u32x4 t = *reinterpret_cast<const u32x4*>(vh + (int64_t)(ok ? key : 0) * D + dc * 8);
-        vst[r][e] = ok ? t : u32x4{0u, 0u, 0u, 0u};
-      }
+      for (int e = 0; e < 4; ++e) vst[r][e] = load16(vr, tile_off + ((kg * 4 + e) * D + dc * 8) * 2);
     }
   };
 
@@ -240,11 +254,11 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
       for (int w = 0; w < 4; ++w) {
         const uint32_t a0 = vst[r][0][w], a1 = vst[r][1][w];
         const uint32_t a2 = vst[r][2][w], a3 = vst[r][3][w];
-        u32x2 lo, hi;
-        lo[0] = (a0 & 0xFFFFu) | (a1 << 16);
-        lo[1] = (a2 & 0xFFFFu) | (a3 << 16);
-        hi[0] = (a0 >> 16) | (a1 & 0xFFFF0000u);
-        hi[1] = (a2 >> 16) | (a3 & 0xFFFF0000u);
+        u32x2 lo, hi;  // v_perm_b32: pick the low / high halves of two words
+        lo[0] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+        lo[1] = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
+        hi[0] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
+        hi[1] = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
         const int d = dc * 8 + 2 * w;
         *reinterpret_cast<u32x2*>(vs + d * VSTR + pos) = lo;
         *reinterpret_cast<u32x2*>(vs + (d + 1) * VSTR + pos) = hi;
@@ -257,7 +271,8 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
 #pragma unroll
   for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
   float m_run = -__builtin_inff();  // running max of scale*log2(e)*s
-  float l_run = 0.f;                // partial running sum (this lane's keys)
+  float l_run = 0.f;                // partial running sum of P (this lane's keys)
+  float lr_run = 0.f;               // the same over P rounded to 16 bits
 
   if (n_tiles > 0) {
     fetch(0);
@@ -279,12 +294,13 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
       // S^T = K Q^T for this wave's NB key blocks
       f32x16 sacc[NB];
 #pragma unroll
-      for (int kb = 0; kb < NB; ++kb) {
-        sacc[kb] = f32x16{};
-        const uint16_t* kr = ks + (kbase + kb * 32 + col) * KSTR + half * 8;
+      for (int kb = 0; kb < NB; ++kb) sacc[kb] = f32x16{};
+      const uint16_t* krow = ks + (kbase + col) * KSTR + half * 8;
 #pragma unroll
-        for (int kc = 0; kc < DK; ++kc) {
-          u32x4 a = *reinterpret_cast<const u32x4*>(kr + kc * 16);
+      for (int kc = 0; kc < DK; ++kc) {
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb) {
+          u32x4 a = *reinterpret_cast<const u32x4*>(krow + kb * 32 * KSTR + kc * 16);
           sacc[kb] = E::mfma(a, qf[kc], sacc[kb]);
         }
       }
@@ -311,40 +327,57 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
 
+      // Rescale only when some row's max outgrew the reference by the slack
+      // (always on the first tile, where m_run is -inf); the branch is
+      // uniform across the wave.
       const float mt = (mx == -__builtin_inff()) ? mx : mx * c;
-      const float m_new = fmaxf(m_run, mt);
-      const float m_ref = (m_new == -__builtin_inff()) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
-      m_run = m_new;
+      if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack) != 0) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = (m_new == -__builtin_inff()) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+        lr_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      }
+      const float m_ref = (m_run == -__builtin_inff()) ? 0.f : m_run;
 
-      // P = exp2(c*s - m), partial row sums, pack to 16 bits
+      // P = exp2(c*s - m), rounded to nearest-even as the MFMA operand.  Two
+      // row sums: of the fp32 P, for the LSE (a sum of rounded P would move
+      // it by up to 2^-9 relative in bf16), and of the rounded P, which
+      // normalises O so that its weights are exactly the ones V was
+      // multiplied by.
       u32x4 pf[2 * NB];
-      float ls = 0.f;
+      float ls0 = 0.f, ls1 = 0.f, lr0 = 0.f, lr1 = 0.f;
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb) {
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           float p[8];
 #pragma unroll
-          for (int t = 0; t < 8; ++t) {
+          for (int t = 0; t < 8; ++t)
             p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * s2 + t], c, -m_ref));
-            ls += p[t];
-          }
-          pf[2 * kb + s2] = u32x4{E::pack2(p[0], p[1]), E::pack2(p[2], p[3]),
-                                  E::pack2(p[4], p[5]), E::pack2(p[6], p[7])};
+          ls0 += (p[0] + p[1]) + (p[2] + p[3]);
+          ls1 += (p[4] + p[5]) + (p[6] + p[7]);
+          const u32x4 w = {E::pack2(p[0], p[1]), E::pack2(p[2], p[3]), E::pack2(p[4], p[5]),
+                           E::pack2(p[6], p[7])};
+          lr0 = E::sum2(w[0], lr0);
+          lr1 = E::sum2(w[1], lr1);
+          lr0 = E::sum2(w[2], lr0);
+          lr1 = E::sum2(w[3], lr1);
+          pf[2 * kb + s2] = w;
         }
       }
-      l_run = l_run * alpha + ls;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      l_run += ls0 + ls1;
+      lr_run += lr0 + lr1;
 
       // O^T += V^T P^T
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const uint16_t* vr = vs + (db * 32 + col) * VSTR + kbase + half * 8;
+      for (int ks = 0; ks < 2 * NB; ++ks) {
 #pragma unroll
-        for (int ks = 0; ks < 2 * NB; ++ks) {
-          u32x4 a = *reinterpret_cast<const u32x4*>(vr + ks * 16);
+        for (int db = 0; db < DB; ++db) {
+          const uint16_t* vrow = vs + (db * 32 + col) * VSTR + kbase + half * 8;
+          u32x4 a = *reinterpret_cast<const u32x4*>(vrow + ks * 16);
           oacc[db] = E::mfma(a, pf[ks], oacc[db]);
         }
       }
@@ -357,7 +390,7 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
   // ---- merge the key-split waves (KW > 1) ----
   if constexpr (C::KW > 1) {
     float* mg = reinterpret_cast<float*>(lds);
-    constexpr int FIELDS = D / 2 + 2;
+    constexpr int FIELDS = D / 2 + 3;
     if (kw > 0) {
       float* dst = mg + ((kw - 1) * C::QW + qw) * FIELDS * 64;
 #pragma unroll
@@ -366,6 +399,7 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
         for (int i = 0; i < 16; ++i) dst[(db * 16 + i) * 64 + lane] = oacc[db][i];
       dst[(D / 2) * 64 + lane] = l_run;
       dst[(D / 2 + 1) * 64 + lane] = m_run;
+      dst[(D / 2 + 2) * 64 + lane] = lr_run;
     }
     __syncthreads();
     if (kw > 0) return;
@@ -374,6 +408,7 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
       const float* src = mg + ((w - 1) * C::QW + qw) * FIELDS * 64;
       const float lb = src[(D / 2) * 64 + lane];
       const float mb = src[(D / 2 + 1) * 64 + lane];
+      const float lrb = src[(D / 2 + 2) * 64 + lane];
       const float mm = fmaxf(m_run, mb);
       const float mref = (mm == -__builtin_inff()) ? 0.f : mm;
       const float fa = __builtin_amdgcn_exp2f(m_run - mref);
@@ -384,14 +419,16 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
         for (int i = 0; i < 16; ++i)
           oacc[db][i] = oacc[db][i] * fa + src[(db * 16 + i) * 64 + lane] * fb;
       l_run = l_run * fa + lb * fb;
+      lr_run = lr_run * fa + lrb * fb;
       m_run = mm;
     }
   }
 
   // ---- epilogue: O = O_acc / l (RNE to 16 bits), LSE = (m + log2 l) ln 2 ----
   const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float lr_tot = lr_run + __shfl_xor(lr_run, 32);
   if (my_q < S) {
-    const float inv = 1.0f / l_tot;
+    const float inv = 1.0f / lr_tot;
     uint16_t* orow = o + head + (int64_t)my_q * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {

@@ -134,6 +134,7 @@ def call(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, o=FAKE + 0x300000, lse=FA
     (dict(B=-1), 2, "B, H and S"),
     (dict(S=-5), 2, "B, H and S"),
     (dict(S=1 << 30), 2, "too large"),
+    (dict(S=(1 << 24) + 1, D=64), 2, "too large"),
     (dict(B=1 << 40, H=1 << 20), 2, "overflow"),
     (dict(D=96), 3, "head_dim"),
     (dict(dtype=2), 4, "dtype"),
