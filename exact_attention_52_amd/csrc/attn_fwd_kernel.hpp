@@ -19,14 +19,16 @@
 //     in-register reduction plus one exchange between lane l and l^32, and
 //     the rescale of O^T by exp2(m_old - m_new) is one scalar per lane.
 //   * The probabilities, packed to 16 bits, are already the B operand of the
-//     second contraction O^T += V^T P^T: no LDS round trip for P.  For that,
-//     V is stored transposed in LDS (d-major) with bits 2 and 3 of each key
-//     index swapped, which lines up the key order of the packed P registers
-//     with the 8 contiguous keys each lane reads for the A operand.
-//   * K and V^T tiles stream through two LDS stages: tile j+1 is fetched
-//     from HBM into VGPRs with 16-byte coalesced loads while tile j is
-//     computed, then stored into the other stage; one workgroup barrier per
-//     tile.
+//     second contraction O^T += V^T P^T: no LDS round trip for P.  V stays
+//     row-major in LDS and its transposed A operand is read with gfx950's
+//     ds_read_b64_tr_b16 (each 16-lane group reads a 4-key x 16-d block and
+//     gets it back one d column per lane); the 4-key row groups are picked to
+//     match the key order of the packed P registers.
+//   * K and V tiles stream through two LDS stages: tile j+1 is fetched from
+//     HBM into VGPRs with 16-byte buffer loads while tile j is computed, then
+//     stored into the other stage; one workgroup barrier per tile.  Row
+//     strides are padded so the 16-byte K reads (8 rows per bank sweep) and
+//     the transposing V reads (4 rows of 32 bytes) hit disjoint banks.
 //   * exp2/log2 are the hardware v_exp_f32/v_log_f32 with the scale folded
 //     as c = scale*log2(e); P and O are rounded to nearest-even.
 //   * Causal: key tiles wholly after a wave's last query are skipped, and
@@ -108,10 +110,10 @@ struct TileCfg {
   static constexpr int NB = KSUB / 32;       // 32-key blocks per wave per tile
   static constexpr int DK = D / 16;          // k-steps of the score MFMA
   static constexpr int DB = D / 32;          // 32-row blocks of O^T
-  static constexpr int KSTR = D + 8;         // K tile row stride (halves)
-  static constexpr int VSTR = BN + 8;        // V^T tile row stride (halves)
+  static constexpr int KSTR = D + 8;         // K tile row stride (halves): 4 dwords mod 32
+  static constexpr int VSTR = D + 16;        // V tile row stride (halves): 8 dwords mod 32
   static constexpr int K_HALVES = BN * KSTR;
-  static constexpr int V_HALVES = D * VSTR;
+  static constexpr int V_HALVES = BN * VSTR;
   static constexpr int STAGE_HALVES = K_HALVES + V_HALVES;
   static constexpr int STAGES = 2;
   static constexpr int KV_LDS_BYTES = STAGES * STAGE_HALVES * 2;
@@ -119,21 +121,24 @@ struct TileCfg {
   static constexpr int MERGE_FLOATS = (KW - 1) * QW * (D / 2 + 3) * 64;
   static constexpr int LDS_BYTES =
       KV_LDS_BYTES > MERGE_FLOATS * 4 ? KV_LDS_BYTES : MERGE_FLOATS * 4;
-  static constexpr int K_CHUNKS = BN * D / 8;         // 16-byte chunks of K
+  static constexpr int K_CHUNKS = BN * D / 8;         // 16-byte chunks of a K or V tile
   static constexpr int K_PER_THREAD = K_CHUNKS / NT;
-  static constexpr int V_UNITS = (BN / 4) * (D / 8);  // 4 keys x 8 d blocks
-  static constexpr int V_PER_THREAD = V_UNITS / NT;
 
   static_assert(D % 32 == 0, "head dim must be a multiple of 32");
   static_assert(KSUB % 32 == 0 && NB >= 1, "each wave needs whole 32-key blocks");
   static_assert(K_CHUNKS % NT == 0, "K tile must split evenly over threads");
-  static_assert(V_UNITS % NT == 0, "V tile must split evenly over threads");
   static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per CU");
 };
 
-// Swap bits 2 and 3 of a key index: the position of key k inside a V^T row.
-__device__ __forceinline__ int vt_pos(int k) {
-  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+typedef short s16x4 __attribute__((vector_size(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i supplies the address
+// of 4 consecutive 16-bit elements of row i/4 (columns 4*(i%4)..+3) of a
+// 4 x 16 block and receives column i of the block's 4 rows.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
 }
 
 // Buffer descriptor over one head's [S, D] slab: loads past `bytes` return
@@ -216,7 +221,7 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
 
   // ---- staging registers for the next K/V tile ----
   u32x4 kst[C::K_PER_THREAD];
-  u32x4 vst[C::V_PER_THREAD][4];
+  u32x4 vst[C::K_PER_THREAD];
 
   // keys >= S fall outside the head's buffer range and load as zeros
   auto fetch = [&](int kv0) {
@@ -227,12 +232,7 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
       kst[r] = load16(kr, tile_off + ch * 16);
     }
 #pragma unroll
-    for (int r = 0; r < C::V_PER_THREAD; ++r) {
-      const int u = tid + r * C::NT;
-      const int kg = u / (D / 8), dc = u % (D / 8);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) vst[r][e] = load16(vr, tile_off + ((kg * 4 + e) * D + dc * 8) * 2);
-    }
+    for (int r = 0; r < C::K_PER_THREAD; ++r) vst[r] = load16(vr, tile_off + (tid + r * C::NT) * 16);
   };
 
   auto store = [&](int stage) {
@@ -245,24 +245,10 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
       *reinterpret_cast<u32x4*>(ks + row * KSTR + c8 * 8) = kst[r];
     }
 #pragma unroll
-    for (int r = 0; r < C::V_PER_THREAD; ++r) {
-      const int u = tid + r * C::NT;
-      const int kg = u / (D / 8), dc = u % (D / 8);
-      const int pos = vt_pos(kg * 4);
-      // transpose the 4 keys x 8 d block: row d gets the 4 keys' values
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t a0 = vst[r][0][w], a1 = vst[r][1][w];
-        const uint32_t a2 = vst[r][2][w], a3 = vst[r][3][w];
-        u32x2 lo, hi;  // v_perm_b32: pick the low / high halves of two words
-        lo[0] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
-        lo[1] = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
-        hi[0] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
-        hi[1] = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
-        const int d = dc * 8 + 2 * w;
-        *reinterpret_cast<u32x2*>(vs + d * VSTR + pos) = lo;
-        *reinterpret_cast<u32x2*>(vs + (d + 1) * VSTR + pos) = hi;
-      }
+    for (int r = 0; r < C::K_PER_THREAD; ++r) {
+      const int ch = tid + r * C::NT;
+      const int row = ch / (D / 8), c8 = ch % (D / 8);
+      *reinterpret_cast<u32x4*>(vs + row * VSTR + c8 * 8) = vst[r];
     }
   };
 
@@ -371,13 +357,20 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
       l_run += ls0 + ls1;
       lr_run += lr0 + lr1;
 
-      // O^T += V^T P^T
+      // O^T += V^T P^T.  MFMA k-slot t of this lane holds the key
+      // 16*ks + 8*(t/4) + 4*half + t%4 (the score accumulator layout), so the
+      // transposing read r = t/4 covers the 4 consecutive keys
+      // 16*ks + 8*r + 4*half + (0..3) at d columns 32*db + (lane&31).
+      const uint16_t* vbase = vs + (kbase + 4 * half + ((lane & 15) >> 2)) * VSTR +
+                              16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
       for (int ks = 0; ks < 2 * NB; ++ks) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const uint16_t* vrow = vs + (db * 32 + col) * VSTR + kbase + half * 8;
-          u32x4 a = *reinterpret_cast<const u32x4*>(vrow + ks * 16);
+          const uint16_t* vp = vbase + ks * 16 * VSTR + db * 32;
+          const u32x2 lo = lds_read_tr16(vp);
+          const u32x2 hi = lds_read_tr16(vp + 8 * VSTR);
+          const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
           oacc[db] = E::mfma(a, pf[ks], oacc[db]);
         }
       }
