@@ -95,8 +95,19 @@ struct Elem<DT_BF16> {
 };
 
 // ---------------------------------------------------------------------------
-// Tile configuration
+// Tile configuration and LDS layout
 // ---------------------------------------------------------------------------
+// K and V tiles are copied HBM -> LDS by buffer_load_dwordx4 ... lds, where
+// one wave instruction writes 1 KiB: lane i's 16 bytes land at base + 16*i.
+// Each such 1 KiB "line" holds RPL = 512/D whole rows of the tile, and lines
+// are padded so that the operand reads hit distinct banks of the 64 x 4-byte
+// LDS (256 bytes per bank sweep):
+//   K: line L of a 16-line block holds rows L, L+16, L+32, ... (pad 16 B), so
+//      the 16 consecutive rows read by one 16-lane quarter of a 16-byte
+//      operand read sit 16 bytes apart modulo 256;
+//   V: line L of a 4-line block holds rows L, L+4, ... (pad 64 B), so the 4
+//      consecutive rows of a transposing read, 64 bytes wide across two
+//      16-lane groups, sit 64 bytes apart modulo 256.
 template <int D_, int QW_, int KW_, int BN_>
 struct TileCfg {
   static constexpr int D = D_;
@@ -110,45 +121,61 @@ struct TileCfg {
   static constexpr int NB = KSUB / 32;       // 32-key blocks per wave per tile
   static constexpr int DK = D / 16;          // k-steps of the score MFMA
   static constexpr int DB = D / 32;          // 32-row blocks of O^T
-  static constexpr int KSTR = D + 8;         // K tile row stride (halves): 4 dwords mod 32
-  static constexpr int VSTR = D + 16;        // V tile row stride (halves): 8 dwords mod 32
-  static constexpr int K_HALVES = BN * KSTR;
-  static constexpr int V_HALVES = BN * VSTR;
-  static constexpr int STAGE_HALVES = K_HALVES + V_HALVES;
+  static constexpr int ROW_BYTES = 2 * D;
+  static constexpr int RPL = 1024 / ROW_BYTES;           // rows per 1 KiB line
+  static constexpr int LINES = BN * ROW_BYTES / 1024;    // lines per tile
+  static constexpr int K_LINE = 1024 + 16;
+  static constexpr int V_LINE = 1024 + 64;
+  static constexpr int K_TILE = LINES * K_LINE;
+  static constexpr int V_TILE = LINES * V_LINE;
   static constexpr int STAGES = 2;
-  static constexpr int KV_LDS_BYTES = STAGES * STAGE_HALVES * 2;
-  // partial (O^T, l, m) of the waves with kw > 0, for the final merge
-  static constexpr int MERGE_FLOATS = (KW - 1) * QW * (D / 2 + 3) * 64;
-  static constexpr int LDS_BYTES =
-      KV_LDS_BYTES > MERGE_FLOATS * 4 ? KV_LDS_BYTES : MERGE_FLOATS * 4;
-  static constexpr int K_CHUNKS = BN * D / 8;         // 16-byte chunks of a K or V tile
-  static constexpr int K_PER_THREAD = K_CHUNKS / NT;
+  static constexpr int KV_LDS_BYTES = STAGES * (K_TILE + V_TILE);
+  static constexpr int LOADS_PER_WAVE = LINES / NW;      // K lines (and V lines) per wave
+  static constexpr int LDS_BYTES = KV_LDS_BYTES;
 
-  static_assert(D % 32 == 0, "head dim must be a multiple of 32");
+  // byte offset of tile row `row` inside a K / V tile
+  static constexpr __host__ __device__ int k_off(int row) {
+    return (row / (16 * RPL)) * 16 * K_LINE + (row % 16) * K_LINE + ((row % (16 * RPL)) / 16) * ROW_BYTES;
+  }
+  static constexpr __host__ __device__ int v_off(int row) {
+    return (row / (4 * RPL)) * 4 * V_LINE + (row % 4) * V_LINE + ((row % (4 * RPL)) / 4) * ROW_BYTES;
+  }
+  // first tile row of load line n (the line's rows step by 16 for K, 4 for V)
+  static constexpr __host__ __device__ int k_line_row(int n) { return (n / 16) * 16 * RPL + n % 16; }
+  static constexpr __host__ __device__ int v_line_row(int n) { return (n / 4) * 4 * RPL + n % 4; }
+
+  static_assert(D % 32 == 0 && RPL >= 1, "head dim must be a multiple of 32, at most 512");
   static_assert(KSUB % 32 == 0 && NB >= 1, "each wave needs whole 32-key blocks");
-  static_assert(K_CHUNKS % NT == 0, "K tile must split evenly over threads");
+  static_assert(BN % (16 * RPL) == 0, "tile must hold whole K line blocks");
+  static_assert(LINES % NW == 0, "load lines must split evenly over the waves");
   static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per CU");
 };
 
 typedef short s16x4 __attribute__((vector_size(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 // ds_read_b64_tr_b16: within each 16-lane group, lane i supplies the address
 // of 4 consecutive 16-bit elements of row i/4 (columns 4*(i%4)..+3) of a
 // 4 x 16 block and receives column i of the block's 4 rows.
-__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
   s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
   return __builtin_bit_cast(u32x2, v);
 }
 
-// Buffer descriptor over one head's [S, D] slab: loads past `bytes` return
+// Buffer descriptor over `bytes` bytes at `base`: loads past the end return
 // zero, which pads the ragged last tile without any select after the load.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base, uint32_t bytes) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
 }
 
 __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0);
+}
+
+// 16 bytes per lane from global memory straight into LDS at lds + 16*lane.
+__device__ __forceinline__ void load16_lds(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t byte_off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, (int)byte_off, 0, 0, 0);
 }
 
 // Running-max hysteresis (log2 units): O, l are only rescaled when some row's
@@ -178,12 +205,16 @@ template <class C, bool CAUSAL, int DT>
 __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
-    int S, int nq, int64_t G, float c /* scale * log2(e) */) {
+    int S, int nq, int64_t G, float c /* scale * log2(e), > 0 */) {
   using E = Elem<DT>;
   constexpr int D = C::D, BN = C::BN, BM = C::BM, NB = C::NB, DK = C::DK, DB = C::DB;
-  constexpr int KSTR = C::KSTR, VSTR = C::VSTR;
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_BYTES / 2];
+  // one array per stage and operand, so that the compiler can tell reads of
+  // one stage from the asynchronous HBM->LDS copies into the other
+  __shared__ __attribute__((aligned(1024))) uint8_t kt0[C::K_TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t kt1[C::K_TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vt0[C::V_TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vt1[C::V_TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -197,10 +228,8 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
   workgroup_tile(blockIdx.x, G, nq, CAUSAL, &tile64, &bh64);
   const int q0 = (int)tile64 * BM;
   const int64_t head = bh64 * (int64_t)S * D;
-  const uint32_t head_bytes = (uint32_t)S * D * 2;
-  const __amdgpu_buffer_rsrc_t qr = head_rsrc(q + head, head_bytes);
-  const __amdgpu_buffer_rsrc_t kr = head_rsrc(k + head, head_bytes);
-  const __amdgpu_buffer_rsrc_t vr = head_rsrc(v + head, head_bytes);
+  const uint16_t* kh = k + head;
+  const uint16_t* vh = v + head;
 
   const int wq_first = q0 + qw * 32;  // first query row of this wave
   const int wq_last = wq_first + 31;
@@ -210,6 +239,7 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
   // ---- Q fragment, resident for the whole kernel (B operand of S^T) ----
   u32x4 qf[DK];
   {
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(q + head, (uint32_t)S * D * 2);
     const uint32_t off = (uint32_t)(my_q * D + half * 8) * 2;  // rows >= S read 0
 #pragma unroll
     for (int kc = 0; kc < DK; ++kc) qf[kc] = load16(qr, off + kc * 32);
@@ -219,38 +249,24 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
   const int q_end = (q0 + BM < S) ? q0 + BM : S;
   const int n_tiles = CAUSAL ? (q_end + BN - 1) / BN : (S + BN - 1) / BN;
 
-  // ---- staging registers for the next K/V tile ----
-  u32x4 kst[C::K_PER_THREAD];
-  u32x4 vst[C::K_PER_THREAD];
-
-  // keys >= S fall outside the head's buffer range and load as zeros
-  auto fetch = [&](int kv0) {
-    const uint32_t tile_off = (uint32_t)kv0 * D * 2;
+  // ---- HBM -> LDS copy of one K/V tile: this wave's share of the lines ----
+  // lane i of line n carries row (line row + step*(i / (D/8))), chunk i % (D/8)
+  const int lrow = lane / (D / 8), lchunk = lane % (D / 8);
+  auto fetch = [&](int kv0, uint8_t* kt, uint8_t* vt) {
+    const uint32_t rem = (uint32_t)(S - kv0) * D * 2;  // keys >= S read as zeros
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kh + (int64_t)kv0 * D, rem);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vh + (int64_t)kv0 * D, rem);
 #pragma unroll
-    for (int r = 0; r < C::K_PER_THREAD; ++r) {
-      const int ch = tid + r * C::NT;  // 16-byte chunk of the row-major tile
-      kst[r] = load16(kr, tile_off + ch * 16);
-    }
-#pragma unroll
-    for (int r = 0; r < C::K_PER_THREAD; ++r) vst[r] = load16(vr, tile_off + (tid + r * C::NT) * 16);
-  };
-
-  auto store = [&](int stage) {
-    uint16_t* ks = lds + stage * C::STAGE_HALVES;
-    uint16_t* vs = ks + C::K_HALVES;
-#pragma unroll
-    for (int r = 0; r < C::K_PER_THREAD; ++r) {
-      const int ch = tid + r * C::NT;
-      const int row = ch / (D / 8), c8 = ch % (D / 8);
-      *reinterpret_cast<u32x4*>(ks + row * KSTR + c8 * 8) = kst[r];
-    }
-#pragma unroll
-    for (int r = 0; r < C::K_PER_THREAD; ++r) {
-      const int ch = tid + r * C::NT;
-      const int row = ch / (D / 8), c8 = ch % (D / 8);
-      *reinterpret_cast<u32x4*>(vs + row * VSTR + c8 * 8) = vst[r];
+    for (int i = 0; i < C::LOADS_PER_WAVE; ++i) {
+      const int n = wave * C::LOADS_PER_WAVE + i;
+      load16_lds(kr, kt + n * C::K_LINE, (C::k_line_row(n) + 16 * lrow) * C::ROW_BYTES + lchunk * 16);
+      load16_lds(vr, vt + n * C::V_LINE, (C::v_line_row(n) + 4 * lrow) * C::ROW_BYTES + lchunk * 16);
     }
   };
+
+  // lane parts of the operand read addresses (the rest are immediates)
+  const int k_lane = C::k_off(kbase + col) + half * 16;
+  const int v_lane = C::v_off(kbase + 4 * half + ((lane & 15) >> 2)) + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
 
   // ---- running state (per lane: one query column) ----
   f32x16 oacc[DB];
@@ -260,132 +276,127 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
   float l_run = 0.f;                // partial running sum of P (this lane's keys)
   float lr_run = 0.f;               // the same over P rounded to 16 bits
 
-  if (n_tiles > 0) {
-    fetch(0);
-    store(0);
-  }
-  __syncthreads();
-
-  for (int j = 0; j < n_tiles; ++j) {
-    const int stage = j & 1;
-    const bool has_next = j + 1 < n_tiles;
-    if (has_next) fetch((j + 1) * BN);
-
+  auto compute = [&](int j, const uint8_t* kt, const uint8_t* vt) {
     const int kv0 = j * BN + kbase;  // first key of this wave's slice
-    const bool active = kv0 < S && (!CAUSAL || kv0 <= wq_last) && wq_first < S;
-    if (active) {
-      const uint16_t* ks = lds + stage * C::STAGE_HALVES;
-      const uint16_t* vs = ks + C::K_HALVES;
+    if (!(kv0 < S && (!CAUSAL || kv0 <= wq_last) && wq_first < S)) return;
 
-      // S^T = K Q^T for this wave's NB key blocks
-      f32x16 sacc[NB];
+    // S^T = K Q^T for this wave's NB key blocks
+    f32x16 sacc[NB];
 #pragma unroll
-      for (int kb = 0; kb < NB; ++kb) sacc[kb] = f32x16{};
-      const uint16_t* krow = ks + (kbase + col) * KSTR + half * 8;
+    for (int kb = 0; kb < NB; ++kb) sacc[kb] = f32x16{};
 #pragma unroll
-      for (int kc = 0; kc < DK; ++kc) {
+    for (int kc = 0; kc < DK; ++kc) {
 #pragma unroll
-        for (int kb = 0; kb < NB; ++kb) {
-          u32x4 a = *reinterpret_cast<const u32x4*>(krow + kb * 32 * KSTR + kc * 16);
-          sacc[kb] = E::mfma(a, qf[kc], sacc[kb]);
-        }
+      for (int kb = 0; kb < NB; ++kb) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(kt + k_lane + C::k_off(32 * kb) + 32 * kc);
+        sacc[kb] = E::mfma(a, qf[kc], sacc[kb]);
       }
+    }
 
-      // mask keys past the end or after the query (diagonal / ragged tiles)
-      const bool need_mask = (kv0 + C::KSUB > S) || (CAUSAL && kv0 + C::KSUB - 1 > wq_first);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < NB; ++kb) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kv0 + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-            const bool dead = key >= S || (CAUSAL && key > my_q);
-            sacc[kb][i] = dead ? -__builtin_inff() : sacc[kb][i];
-          }
-        }
-      }
-
-      // row max over this tile (in registers, then across the lane pair)
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-
-      // Rescale only when some row's max outgrew the reference by the slack
-      // (always on the first tile, where m_run is -inf); the branch is
-      // uniform across the wave.
-      const float mt = (mx == -__builtin_inff()) ? mx : mx * c;
-      if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack) != 0) {
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = (m_new == -__builtin_inff()) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-        lr_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-      }
-      const float m_ref = (m_run == -__builtin_inff()) ? 0.f : m_run;
-
-      // P = exp2(c*s - m), rounded to nearest-even as the MFMA operand.  Two
-      // row sums: of the fp32 P, for the LSE (a sum of rounded P would move
-      // it by up to 2^-9 relative in bf16), and of the rounded P, which
-      // normalises O so that its weights are exactly the ones V was
-      // multiplied by.
-      u32x4 pf[2 * NB];
-      float ls0 = 0.f, ls1 = 0.f, lr0 = 0.f, lr1 = 0.f;
+    // mask keys past the end or after the query (diagonal / ragged tiles)
+    const bool need_mask = (kv0 + C::KSUB > S) || (CAUSAL && kv0 + C::KSUB - 1 > wq_first);
+    if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb) {
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          float p[8];
-#pragma unroll
-          for (int t = 0; t < 8; ++t)
-            p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * s2 + t], c, -m_ref));
-          ls0 += (p[0] + p[1]) + (p[2] + p[3]);
-          ls1 += (p[4] + p[5]) + (p[6] + p[7]);
-          const u32x4 w = {E::pack2(p[0], p[1]), E::pack2(p[2], p[3]), E::pack2(p[4], p[5]),
-                           E::pack2(p[6], p[7])};
-          lr0 = E::sum2(w[0], lr0);
-          lr1 = E::sum2(w[1], lr1);
-          lr0 = E::sum2(w[2], lr0);
-          lr1 = E::sum2(w[3], lr1);
-          pf[2 * kb + s2] = w;
-        }
-      }
-      l_run += ls0 + ls1;
-      lr_run += lr0 + lr1;
-
-      // O^T += V^T P^T.  MFMA k-slot t of this lane holds the key
-      // 16*ks + 8*(t/4) + 4*half + t%4 (the score accumulator layout), so the
-      // transposing read r = t/4 covers the 4 consecutive keys
-      // 16*ks + 8*r + 4*half + (0..3) at d columns 32*db + (lane&31).
-      const uint16_t* vbase = vs + (kbase + 4 * half + ((lane & 15) >> 2)) * VSTR +
-                              16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll
-      for (int ks = 0; ks < 2 * NB; ++ks) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const uint16_t* vp = vbase + ks * 16 * VSTR + db * 32;
-          const u32x2 lo = lds_read_tr16(vp);
-          const u32x2 hi = lds_read_tr16(vp + 8 * VSTR);
-          const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-          oacc[db] = E::mfma(a, pf[ks], oacc[db]);
+        for (int i = 0; i < 16; ++i) {
+          const int key = kv0 + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+          const bool dead = key >= S || (CAUSAL && key > my_q);
+          sacc[kb][i] = dead ? -__builtin_inff() : sacc[kb][i];
         }
       }
     }
 
-    if (has_next) store(stage ^ 1);
+    // row max over this tile (in registers, then across the lane pair)
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+
+    // Rescale only when some row's max outgrew the reference by the slack
+    // (always on the first tile, where m_run is -inf); the branch is
+    // uniform across the wave.
+    const float mt = (mx == -__builtin_inff()) ? mx : mx * c;
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = (m_new == -__builtin_inff()) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+      lr_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+    }
+    const float m_ref = (m_run == -__builtin_inff()) ? 0.f : m_run;
+
+    // P = exp2(c*s - m), rounded to nearest-even as the MFMA operand.  Two
+    // row sums: of the fp32 P, for the LSE (a sum of rounded P would move
+    // it by up to 2^-9 relative in bf16), and of the rounded P, which
+    // normalises O so that its weights are exactly the ones V was
+    // multiplied by.
+    u32x4 pf[2 * NB];
+    float ls0 = 0.f, ls1 = 0.f, lr0 = 0.f, lr1 = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) {
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        float p[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * s2 + t], c, -m_ref));
+        ls0 += (p[0] + p[1]) + (p[2] + p[3]);
+        ls1 += (p[4] + p[5]) + (p[6] + p[7]);
+        const u32x4 w = {E::pack2(p[0], p[1]), E::pack2(p[2], p[3]), E::pack2(p[4], p[5]),
+                         E::pack2(p[6], p[7])};
+        lr0 = E::sum2(w[0], lr0);
+        lr1 = E::sum2(w[1], lr1);
+        lr0 = E::sum2(w[2], lr0);
+        lr1 = E::sum2(w[3], lr1);
+        pf[2 * kb + s2] = w;
+      }
+    }
+    l_run += ls0 + ls1;
+    lr_run += lr0 + lr1;
+
+    // O^T += V^T P^T.  MFMA k-slot t of this lane holds the key
+    // 16*ks + 8*(t/4) + 4*half + t%4 (the score accumulator layout), so the
+    // transposing read r = t/4 covers the 4 consecutive keys
+    // 16*ks + 8*r + 4*half + (0..3) at d columns 32*db + (lane&31).
+#pragma unroll
+    for (int ks = 0; ks < 2 * NB; ++ks) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const uint8_t* vp = vt + v_lane + 64 * db;
+        const u32x2 lo = lds_read_tr16(vp + C::v_off(16 * ks));
+        const u32x2 hi = lds_read_tr16(vp + C::v_off(16 * ks + 8));
+        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+        oacc[db] = E::mfma(a, pf[ks], oacc[db]);
+      }
+    }
+  };
+
+  // ---- main loop: two LDS stages, one barrier per tile ----
+  if (n_tiles > 0) fetch(0, kt0, vt0);
+  __syncthreads();
+  for (int j = 0; j < n_tiles; j += 2) {
+    if (j + 1 < n_tiles) fetch((j + 1) * BN, kt1, vt1);
+    compute(j, kt0, vt0);
     __syncthreads();
+    if (j + 1 < n_tiles) {
+      if (j + 2 < n_tiles) fetch((j + 2) * BN, kt0, vt0);
+      compute(j + 1, kt1, vt1);
+      __syncthreads();
+    }
   }
 
   // ---- merge the key-split waves (KW > 1) ----
   if constexpr (C::KW > 1) {
-    float* mg = reinterpret_cast<float*>(lds);
+    // partials of wave (kw, qw), kw > 0, go to V stage (kw - 1) * QW + qw
     constexpr int FIELDS = D / 2 + 3;
+    static_assert((C::KW - 1) * C::QW <= 2 && FIELDS * 64 * 4 <= C::V_TILE, "merge area too small");
     if (kw > 0) {
-      float* dst = mg + ((kw - 1) * C::QW + qw) * FIELDS * 64;
+      float* dst = reinterpret_cast<float*>(((kw - 1) * C::QW + qw) == 0 ? vt0 : vt1);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -398,7 +409,7 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
     if (kw > 0) return;
 #pragma unroll
     for (int w = 1; w < C::KW; ++w) {
-      const float* src = mg + ((w - 1) * C::QW + qw) * FIELDS * 64;
+      const float* src = reinterpret_cast<const float*>(((w - 1) * C::QW + qw) == 0 ? vt0 : vt1);
       const float lb = src[(D / 2) * 64 + lane];
       const float mb = src[(D / 2 + 1) * 64 + lane];
       const float lrb = src[(D / 2 + 2) * 64 + lane];
