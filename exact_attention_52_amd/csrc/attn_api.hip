@@ -43,9 +43,18 @@ int ok() {
 //   D=128: 8 query waves = 256 rows, 128-key tiles, 136 KiB LDS
 //   D=256: 2 query waves = 64 rows (the page's 64-row Q tile for D=256), each
 //          64-key tile split over 2 key waves, 138 KiB LDS
-using Cfg64 = attn::TileCfg<64, 4, 1, 128>;
-using Cfg128 = attn::TileCfg<128, 8, 1, 128>;
-using Cfg256 = attn::TileCfg<256, 2, 2, 64>;
+#ifndef ATTN_CFG64
+#define ATTN_CFG64 64, 8, 1, 128, true
+#endif
+#ifndef ATTN_CFG128
+#define ATTN_CFG128 128, 8, 1, 64, true
+#endif
+#ifndef ATTN_CFG256
+#define ATTN_CFG256 256, 2, 2, 64
+#endif
+using Cfg64 = attn::TileCfg<ATTN_CFG64>;
+using Cfg128 = attn::TileCfg<ATTN_CFG128>;
+using Cfg256 = attn::TileCfg<ATTN_CFG256>;
 
 template <class C>
 void fill_plan(int64_t B, int64_t H, int64_t S, attn_fwd_plan_t* p) {
@@ -130,9 +139,14 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
            int64_t S, float c, hipStream_t stream) {
   const int64_t nq = (S + C::BM - 1) / C::BM;
   const int64_t G = nq * B * H;
-  hipLaunchKernelGGL((attn::attn_fwd_kernel<C, CAUSAL, DT>), dim3((unsigned)G), dim3(C::NT), 0, stream,
-                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, (int)S,
-                     (int)nq, G, c);
+  if constexpr (C::PINGPONG)
+    hipLaunchKernelGGL((attn::attn_fwd_pingpong_kernel<C, CAUSAL, DT>), dim3((unsigned)G), dim3(C::NT), 0,
+                       stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
+                       (int)S, (int)nq, G, c);
+  else
+    hipLaunchKernelGGL((attn::attn_fwd_kernel<C, CAUSAL, DT>), dim3((unsigned)G), dim3(C::NT), 0, stream,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, (int)S,
+                       (int)nq, G, c);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(ATTN_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -69,11 +69,7 @@ struct Elem<DT_F16> {
     v[1] = (_Float16)hi;
     return __builtin_bit_cast(uint32_t, v);
   }
-  // acc + both 16-bit halves of a packed pair (v_dot2 with (1, 1))
-  static __device__ __forceinline__ float sum2(uint32_t pair, float acc) {
-    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), one, acc, false);
-  }
+  static constexpr uint32_t kOnePair = 0x3C003C00u;  // (1.0, 1.0)
 };
 
 template <>
@@ -88,10 +84,7 @@ struct Elem<DT_BF16> {
     v[1] = (__bf16)hi;
     return __builtin_bit_cast(uint32_t, v);
   }
-  static __device__ __forceinline__ float sum2(uint32_t pair, float acc) {
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
-  }
+  static constexpr uint32_t kOnePair = 0x3F803F80u;  // (1.0, 1.0)
 };
 
 // ---------------------------------------------------------------------------
@@ -108,8 +101,9 @@ struct Elem<DT_BF16> {
 //   V: line L of a 4-line block holds rows L, L+4, ... (pad 64 B), so the 4
 //      consecutive rows of a transposing read, 64 bytes wide across two
 //      16-lane groups, sit 64 bytes apart modulo 256.
-template <int D_, int QW_, int KW_, int BN_>
+template <int D_, int QW_, int KW_, int BN_, bool PINGPONG_ = false>
 struct TileCfg {
+  static constexpr bool PINGPONG = PINGPONG_;  // use the two-group ping-pong kernel
   static constexpr int D = D_;
   static constexpr int QW = QW_;             // waves along query rows
   static constexpr int KW = KW_;             // waves along each key tile
@@ -163,6 +157,54 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// Lane l and lane l^32 combined, in every lane (v_permlane32_swap returns
+// both halves' values without a trip through LDS).
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+__device__ __forceinline__ float fmax4(float a, float b, float c, float d) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), __builtin_elementwise_maximum(c, d));
+}
+
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
+// LDS read instructions of pipeline operand T: 2 transposing reads for a PV
+// operand (T < NPV), 1 for a score operand, none past the end.
+template <int T, int NOPS, int NPV>
+constexpr int op_reads() {
+  return T < NOPS ? (T < NPV ? 2 : 1) : 0;
+}
+
+// Scheduling groups for a PIPE-deep operand pipeline of NOPS MFMAs: the
+// reads of operands 0..PIPE-1, then for each T: MFMA T, reads of T+PIPE.
+template <int T, int NOPS, int NPV, int PIPE>
+__device__ __forceinline__ void sched_prologue() {
+  if constexpr (T < PIPE) {
+    if constexpr (op_reads<T, NOPS, NPV>() > 0)
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, op_reads<T, NOPS, NPV>(), 0);
+    sched_prologue<T + 1, NOPS, NPV, PIPE>();
+  }
+}
+template <int T, int NOPS, int NPV, int PIPE>
+__device__ __forceinline__ void sched_steady() {
+  if constexpr (T < NOPS) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    if constexpr (op_reads<T + PIPE, NOPS, NPV>() > 0)
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, op_reads<T + PIPE, NOPS, NPV>(), 0);
+    sched_steady<T + 1, NOPS, NPV, PIPE>();
+  }
+}
+
 // Buffer descriptor over `bytes` bytes at `base`: loads past the end return
 // zero, which pads the ragged last tile without any select after the load.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -199,89 +241,73 @@ __host__ __device__ inline void workgroup_tile(int64_t g, int64_t G, int64_t nq,
 }
 
 // ---------------------------------------------------------------------------
-// The kernel
+// Per-wave state and the three steps of one key tile
 // ---------------------------------------------------------------------------
+// A wave owns 32 query rows (one per lane column) and the kw-th slice of
+// every key tile.  Per tile j it runs
+//   qk(j)      S^T = K_j Q^T into sacc (MFMA),
+//   softmax(j) mask, running max, P = exp2(c*s - m) packed into pf, row sums
+//              (VALU),
+//   pv(j)      O^T += V_j^T P^T (MFMA),
+// in that order; the kernels below only decide how these steps of different
+// waves and tiles are interleaved.
 template <class C, bool CAUSAL, int DT>
-__global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
-    int S, int nq, int64_t G, float c /* scale * log2(e), > 0 */) {
+struct Wave {
   using E = Elem<DT>;
-  constexpr int D = C::D, BN = C::BN, BM = C::BM, NB = C::NB, DK = C::DK, DB = C::DB;
+  static constexpr int D = C::D, BN = C::BN, NB = C::NB, DK = C::DK, DB = C::DB;
 
-  // one array per stage and operand, so that the compiler can tell reads of
-  // one stage from the asynchronous HBM->LDS copies into the other
-  __shared__ __attribute__((aligned(1024))) uint8_t kt0[C::K_TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t kt1[C::K_TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t vt0[C::V_TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t vt1[C::V_TILE];
+  // A operand of all ones: ones^T P^T puts the sum of a column of P^T in
+  // every row of the result
+  static constexpr u32x4 kOnes = {E::kOnePair, E::kOnePair, E::kOnePair, E::kOnePair};
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int qw = wave % C::QW;
-  const int kw = wave / C::QW;
-  const int col = lane & 31;   // query column of this lane in S^T / O^T
-  const int half = lane >> 5;  // which 8-element k-slice this lane supplies
+  u32x4 qf[DK];      // Q fragment (B operand of S^T), resident
+  f32x16 oacc[DB];   // O^T accumulator
+  f32x16 sacc[NB];   // scores of the tile between qk and softmax
+  u32x4 pf[2 * NB];  // packed P of the tile between softmax and pv
+  f32x16 lacc;       // every row: running sum of the rounded P of this column
+  float m_run;       // running max of c*s (log2 units)
+  float l_run;       // partial running sum of the fp32 P over this lane's keys
+  int lane, half, wq_first, wq_last, my_q, kbase, S, k_lane, v_lane;
+  float c;
 
-  int64_t tile64, bh64;
-  workgroup_tile(blockIdx.x, G, nq, CAUSAL, &tile64, &bh64);
-  const int q0 = (int)tile64 * BM;
-  const int64_t head = bh64 * (int64_t)S * D;
-  const uint16_t* kh = k + head;
-  const uint16_t* vh = v + head;
-
-  const int wq_first = q0 + qw * 32;  // first query row of this wave
-  const int wq_last = wq_first + 31;
-  const int my_q = wq_first + col;
-  const int kbase = kw * C::KSUB;     // this wave's key offset inside a tile
-
-  // ---- Q fragment, resident for the whole kernel (B operand of S^T) ----
-  u32x4 qf[DK];
-  {
+  __device__ __forceinline__ void init(const uint16_t* q, int64_t head, int q_first, int kbase_, int S_,
+                                       float c_) {
+    lane = threadIdx.x & 63;
+    const int col = lane & 31;
+    half = lane >> 5;
+    wq_first = q_first;
+    wq_last = q_first + 31;
+    my_q = q_first + col;
+    kbase = kbase_;
+    S = S_;
+    c = c_;
+    // lane parts of the operand read addresses (the rest are immediates)
+    k_lane = C::k_off(kbase + col) + half * 16;
+    v_lane = C::v_off(kbase + 4 * half + ((lane & 15) >> 2)) + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(q + head, (uint32_t)S * D * 2);
     const uint32_t off = (uint32_t)(my_q * D + half * 8) * 2;  // rows >= S read 0
 #pragma unroll
     for (int kc = 0; kc < DK; ++kc) qf[kc] = load16(qr, off + kc * 32);
+#pragma unroll
+    for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
+    lacc = f32x16{};
+    m_run = -__builtin_inff();
+    l_run = 0.f;
   }
 
-  // ---- number of key tiles this workgroup visits ----
-  const int q_end = (q0 + BM < S) ? q0 + BM : S;
-  const int n_tiles = CAUSAL ? (q_end + BN - 1) / BN : (S + BN - 1) / BN;
-
-  // ---- HBM -> LDS copy of one K/V tile: this wave's share of the lines ----
-  // lane i of line n carries row (line row + step*(i / (D/8))), chunk i % (D/8)
-  const int lrow = lane / (D / 8), lchunk = lane % (D / 8);
-  auto fetch = [&](int kv0, uint8_t* kt, uint8_t* vt) {
-    const uint32_t rem = (uint32_t)(S - kv0) * D * 2;  // keys >= S read as zeros
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kh + (int64_t)kv0 * D, rem);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vh + (int64_t)kv0 * D, rem);
+  // P of a tile this wave skips: the next pv then adds exact zeros
+  __device__ __forceinline__ void zero_pf() {
 #pragma unroll
-    for (int i = 0; i < C::LOADS_PER_WAVE; ++i) {
-      const int n = wave * C::LOADS_PER_WAVE + i;
-      load16_lds(kr, kt + n * C::K_LINE, (C::k_line_row(n) + 16 * lrow) * C::ROW_BYTES + lchunk * 16);
-      load16_lds(vr, vt + n * C::V_LINE, (C::v_line_row(n) + 4 * lrow) * C::ROW_BYTES + lchunk * 16);
-    }
-  };
+    for (int i = 0; i < 2 * NB; ++i) pf[i] = u32x4{0u, 0u, 0u, 0u};
+  }
 
-  // lane parts of the operand read addresses (the rest are immediates)
-  const int k_lane = C::k_off(kbase + col) + half * 16;
-  const int v_lane = C::v_off(kbase + 4 * half + ((lane & 15) >> 2)) + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+  // does this wave have any unmasked key in tile j?
+  __device__ __forceinline__ bool active(int j) const {
+    const int kv0 = j * BN + kbase;
+    return kv0 < S && (!CAUSAL || kv0 <= wq_last) && wq_first < S;
+  }
 
-  // ---- running state (per lane: one query column) ----
-  f32x16 oacc[DB];
-#pragma unroll
-  for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
-  float m_run = -__builtin_inff();  // running max of scale*log2(e)*s
-  float l_run = 0.f;                // partial running sum of P (this lane's keys)
-  float lr_run = 0.f;               // the same over P rounded to 16 bits
-
-  auto compute = [&](int j, const uint8_t* kt, const uint8_t* vt) {
-    const int kv0 = j * BN + kbase;  // first key of this wave's slice
-    if (!(kv0 < S && (!CAUSAL || kv0 <= wq_last) && wq_first < S)) return;
-
-    // S^T = K Q^T for this wave's NB key blocks
-    f32x16 sacc[NB];
+  __device__ __forceinline__ void qk(const uint8_t* kt) {
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb) sacc[kb] = f32x16{};
 #pragma unroll
@@ -292,7 +318,10 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
         sacc[kb] = E::mfma(a, qf[kc], sacc[kb]);
       }
     }
+  }
 
+  __device__ __forceinline__ void softmax(int j) {
+    const int kv0 = j * BN + kbase;
     // mask keys past the end or after the query (diagonal / ragged tiles)
     const bool need_mask = (kv0 + C::KSUB > S) || (CAUSAL && kv0 + C::KSUB - 1 > wq_first);
     if (need_mask) {
@@ -307,36 +336,43 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
       }
     }
 
-    // row max over this tile (in registers, then across the lane pair)
-    float mx = -__builtin_inff();
+    // row max over this tile: a tree over the lane's 16*NB scores (short
+    // dependency chains), then across the lane pair
+    // (IEEE maximum: gfx950's v_maximum3_f32, no canonicalising moves; the
+    // scores are never NaN)
+    float part[4 * NB];
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+      for (int g = 0; g < 4; ++g)
+        part[4 * kb + g] = fmax4(sacc[kb][4 * g], sacc[kb][4 * g + 1], sacc[kb][4 * g + 2], sacc[kb][4 * g + 3]);
+#pragma unroll
+    for (int w = 4 * NB; w > 1; w /= 2)
+#pragma unroll
+      for (int i = 0; i < w / 2; ++i) part[i] = __builtin_elementwise_maximum(part[i], part[i + w / 2]);
+    const float mx = max_halves(part[0]);
 
     // Rescale only when some row's max outgrew the reference by the slack
-    // (always on the first tile, where m_run is -inf); the branch is
-    // uniform across the wave.
+    // (always on the first tile, where m_run is -inf); the branch is uniform
+    // across the wave.
     const float mt = (mx == -__builtin_inff()) ? mx : mx * c;
     if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack) != 0) {
       const float m_new = fmaxf(m_run, mt);
       const float alpha = (m_new == -__builtin_inff()) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
-      lr_run *= alpha;
+      lacc *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
     }
     const float m_ref = (m_run == -__builtin_inff()) ? 0.f : m_run;
 
-    // P = exp2(c*s - m), rounded to nearest-even as the MFMA operand.  Two
-    // row sums: of the fp32 P, for the LSE (a sum of rounded P would move
-    // it by up to 2^-9 relative in bf16), and of the rounded P, which
-    // normalises O so that its weights are exactly the ones V was
-    // multiplied by.
-    u32x4 pf[2 * NB];
-    float ls0 = 0.f, ls1 = 0.f, lr0 = 0.f, lr1 = 0.f;
+    // P = exp2(c*s - m), rounded to nearest-even as the MFMA operand.  The
+    // fp32 row sum feeds the LSE (a sum of rounded P would move it by up to
+    // 2^-9 relative in bf16); the sum of the rounded P, which normalises O
+    // so that its weights are exactly the ones V was multiplied by, is
+    // accumulated by the matrix core in pv.
+    float ls[2 * NB];
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb) {
 #pragma unroll
@@ -345,24 +381,23 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
 #pragma unroll
         for (int t = 0; t < 8; ++t)
           p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * s2 + t], c, -m_ref));
-        ls0 += (p[0] + p[1]) + (p[2] + p[3]);
-        ls1 += (p[4] + p[5]) + (p[6] + p[7]);
-        const u32x4 w = {E::pack2(p[0], p[1]), E::pack2(p[2], p[3]), E::pack2(p[4], p[5]),
-                         E::pack2(p[6], p[7])};
-        lr0 = E::sum2(w[0], lr0);
-        lr1 = E::sum2(w[1], lr1);
-        lr0 = E::sum2(w[2], lr0);
-        lr1 = E::sum2(w[3], lr1);
-        pf[2 * kb + s2] = w;
+        ls[2 * kb + s2] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+        pf[2 * kb + s2] = u32x4{E::pack2(p[0], p[1]), E::pack2(p[2], p[3]), E::pack2(p[4], p[5]),
+                                E::pack2(p[6], p[7])};
       }
     }
-    l_run += ls0 + ls1;
-    lr_run += lr0 + lr1;
+#pragma unroll
+    for (int w = 2 * NB; w > 1; w /= 2)
+#pragma unroll
+      for (int i = 0; i < w / 2; ++i) ls[i] += ls[i + w / 2];
+    l_run += ls[0];
+  }
 
-    // O^T += V^T P^T.  MFMA k-slot t of this lane holds the key
-    // 16*ks + 8*(t/4) + 4*half + t%4 (the score accumulator layout), so the
-    // transposing read r = t/4 covers the 4 consecutive keys
-    // 16*ks + 8*r + 4*half + (0..3) at d columns 32*db + (lane&31).
+  // O^T += V^T P^T.  MFMA k-slot t of this lane holds the key
+  // 16*ks + 8*(t/4) + 4*half + t%4 (the score accumulator layout), so the
+  // transposing read r = t/4 covers the 4 consecutive keys
+  // 16*ks + 8*r + 4*half + (0..3) at d columns 32*db + (lane&31).
+  __device__ __forceinline__ void pv(const uint8_t* vt) {
 #pragma unroll
     for (int ks = 0; ks < 2 * NB; ++ks) {
 #pragma unroll
@@ -373,26 +408,180 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
         const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
         oacc[db] = E::mfma(a, pf[ks], oacc[db]);
       }
+      lacc = E::mfma(kOnes, pf[ks], lacc);
     }
+  }
+
+  // The MFMA work of one phase as one software pipeline: pv (O^T += V^T P^T
+  // over the tile in vt) when PV, then qk (S^T = K Q^T over the tile in kt)
+  // when QK.  Operand t+PIPE is read from LDS while MFMA t runs, and the
+  // scheduling groups pin that interleave.
+#ifndef ATTN_PIPE
+#define ATTN_PIPE 4
+#endif
+  template <bool PV, bool QK, int PIPE = ATTN_PIPE>
+  __device__ __forceinline__ void mfma_ops(const uint8_t* vt, const uint8_t* kt) {
+    constexpr int NPV = PV ? 2 * NB * DB : 0;
+    constexpr int NQK = QK ? DK * NB : 0;
+    constexpr int NOPS = NPV + NQK;
+    auto load = [&](int t) __attribute__((always_inline)) -> u32x4 {
+      if (t < NPV) {
+        const int ks = t / DB, db = t % DB;
+        const uint8_t* vp = vt + v_lane + 64 * db;
+        const u32x2 lo = lds_read_tr16(vp + C::v_off(16 * ks));
+        const u32x2 hi = lds_read_tr16(vp + C::v_off(16 * ks + 8));
+        return u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+      const int t2 = t - NPV, kc = t2 / NB, kb = t2 % NB;
+      return *reinterpret_cast<const u32x4*>(kt + k_lane + C::k_off(32 * kb) + 32 * kc);
+    };
+    u32x4 buf[PIPE];
+#pragma unroll
+    for (int t = 0; t < PIPE && t < NOPS; ++t) buf[t] = load(t);
+#pragma unroll
+    for (int t = 0; t < NOPS; ++t) {
+      const u32x4 a = buf[t % PIPE];
+      if (t + PIPE < NOPS) buf[t % PIPE] = load(t + PIPE);
+      if (t < NPV) {
+        const int ks = t / DB, db = t % DB;
+        oacc[db] = E::mfma(a, pf[ks], oacc[db]);
+        if (db == DB - 1) lacc = E::mfma(kOnes, pf[ks], lacc);
+      } else {
+        const int t2 = t - NPV, kc = t2 / NB, kb = t2 % NB;
+        sacc[kb] = E::mfma(a, qf[kc], kc == 0 ? f32x16{} : sacc[kb]);
+      }
+    }
+    // desired order: the first PIPE operand reads, then MFMA t followed by
+    // the reads of operand t+PIPE
+    sched_prologue<0, NOPS, NPV, PIPE>();
+    sched_steady<0, NOPS, NPV, PIPE>();
+  }
+
+  // O = O_acc / l (RNE to 16 bits), LSE = (m + log2 l) ln 2.
+  __device__ __forceinline__ void epilogue(uint16_t* o, float* lse, int64_t head, int64_t bh) {
+    const float l_tot = sum_halves(l_run);
+    const float lr_tot = lacc[0];
+    if (my_q < S) {
+      const float inv = 1.0f / lr_tot;
+      uint16_t* orow = o + head + (int64_t)my_q * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = db * 32 + 8 * g + 4 * half;
+          u32x2 w;
+          w[0] = E::pack2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv);
+          w[1] = E::pack2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+          *reinterpret_cast<u32x2*>(orow + d) = w;
+        }
+      }
+      if (half == 0)
+        lse[bh * (int64_t)S + my_q] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f;
+    }
+  }
+};
+
+// HBM -> LDS copy of this wave's share of the lines of one K or V tile.
+// Lane i of line n carries row (first row of line n) + step*(i / (D/8)) and
+// 16-byte chunk i % (D/8); keys >= S fall outside the buffer and read as 0.
+template <class C, bool IS_K, int LOADERS = C::NW>
+__device__ __forceinline__ void fetch_tile(const uint16_t* src_head, int S, int kv0, uint8_t* tile, int wave,
+                                           int lane) {
+  constexpr int D = C::D;
+  constexpr int PER_WAVE = C::LINES / LOADERS;
+  static_assert(C::LINES % LOADERS == 0, "load lines must split evenly over the loading waves");
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(src_head + (int64_t)kv0 * D, (uint32_t)(S - kv0) * D * 2);
+  const int lrow = lane / (D / 8), lchunk = lane % (D / 8);
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int n = wave * PER_WAVE + i;
+    if constexpr (IS_K)
+      load16_lds(r, tile + n * C::K_LINE, (C::k_line_row(n) + 16 * lrow) * C::ROW_BYTES + lchunk * 16);
+    else
+      load16_lds(r, tile + n * C::V_LINE, (C::v_line_row(n) + 4 * lrow) * C::ROW_BYTES + lchunk * 16);
+  }
+}
+
+// Workgroup barrier that does not drain outstanding memory operations (the
+// HBM -> LDS prefetch stays in flight); the memory clobber keeps the compiler
+// from moving LDS accesses across it.
+__device__ __forceinline__ void barrier_keep_loads() { asm volatile("s_barrier" ::: "memory"); }
+
+// Wait for this wave's HBM -> LDS copies (vmcnt = 0).
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Wait until at most N of this wave's vector-memory operations are in flight
+// (they complete in issue order): the older copies are then in LDS.
+template <int N>
+__device__ __forceinline__ void wait_loads_but() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 0xF) | ((N & 0x30) << 10));
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 1: every wave runs qk, softmax, pv per tile; one barrier per tile.
+// Supports key-split waves (KW > 1), merged at the end through LDS.
+// ---------------------------------------------------------------------------
+template <class C, bool CAUSAL, int DT>
+__global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
+    int S, int nq, int64_t G, float c /* scale * log2(e), > 0 */) {
+  constexpr int D = C::D, BN = C::BN, BM = C::BM, DB = C::DB;
+
+  // one array per stage and operand, so that the compiler can tell reads of
+  // one stage from the asynchronous HBM->LDS copies into the other
+  __shared__ __attribute__((aligned(1024))) uint8_t kt0[C::K_TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t kt1[C::K_TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vt0[C::V_TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vt1[C::V_TILE];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int qw = wave % C::QW;
+  const int kw = wave / C::QW;
+
+  int64_t tile64, bh64;
+  workgroup_tile(blockIdx.x, G, nq, CAUSAL, &tile64, &bh64);
+  const int q0 = (int)tile64 * BM;
+  const int64_t head = bh64 * (int64_t)S * D;
+  const uint16_t* kh = k + head;
+  const uint16_t* vh = v + head;
+
+  Wave<C, CAUSAL, DT> w;
+  w.init(q, head, q0 + qw * 32, kw * C::KSUB, S, c);
+
+  const int q_end = (q0 + BM < S) ? q0 + BM : S;
+  const int n_tiles = CAUSAL ? (q_end + BN - 1) / BN : (S + BN - 1) / BN;
+
+  auto fetch = [&](int j, uint8_t* kt, uint8_t* vt) __attribute__((always_inline)) {
+    fetch_tile<C, true>(kh, S, j * BN, kt, wave, lane);
+    fetch_tile<C, false>(vh, S, j * BN, vt, wave, lane);
+  };
+  auto compute = [&](int j, const uint8_t* kt, const uint8_t* vt) __attribute__((always_inline)) {
+    if (!w.active(j)) return;
+    w.qk(kt);
+    w.softmax(j);
+    w.pv(vt);
   };
 
-  // ---- main loop: two LDS stages, one barrier per tile ----
+  // two LDS stages, one barrier per tile
   if (n_tiles > 0) fetch(0, kt0, vt0);
   __syncthreads();
   for (int j = 0; j < n_tiles; j += 2) {
-    if (j + 1 < n_tiles) fetch((j + 1) * BN, kt1, vt1);
+    if (j + 1 < n_tiles) fetch(j + 1, kt1, vt1);
     compute(j, kt0, vt0);
     __syncthreads();
     if (j + 1 < n_tiles) {
-      if (j + 2 < n_tiles) fetch((j + 2) * BN, kt0, vt0);
+      if (j + 2 < n_tiles) fetch(j + 2, kt0, vt0);
       compute(j + 1, kt1, vt1);
       __syncthreads();
     }
   }
 
-  // ---- merge the key-split waves (KW > 1) ----
+  // merge the key-split waves (KW > 1): partials of wave (kw, qw), kw > 0,
+  // go to V stage (kw - 1) * QW + qw
   if constexpr (C::KW > 1) {
-    // partials of wave (kw, qw), kw > 0, go to V stage (kw - 1) * QW + qw
     constexpr int FIELDS = D / 2 + 3;
     static_assert((C::KW - 1) * C::QW <= 2 && FIELDS * 64 * 4 <= C::V_TILE, "merge area too small");
     if (kw > 0) {
@@ -400,56 +589,126 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) dst[(db * 16 + i) * 64 + lane] = oacc[db][i];
-      dst[(D / 2) * 64 + lane] = l_run;
-      dst[(D / 2 + 1) * 64 + lane] = m_run;
-      dst[(D / 2 + 2) * 64 + lane] = lr_run;
+        for (int i = 0; i < 16; ++i) dst[(db * 16 + i) * 64 + lane] = w.oacc[db][i];
+      dst[(D / 2) * 64 + lane] = w.l_run;
+      dst[(D / 2 + 1) * 64 + lane] = w.m_run;
+      dst[(D / 2 + 2) * 64 + lane] = w.lacc[0];
     }
     __syncthreads();
     if (kw > 0) return;
 #pragma unroll
-    for (int w = 1; w < C::KW; ++w) {
-      const float* src = reinterpret_cast<const float*>(((w - 1) * C::QW + qw) == 0 ? vt0 : vt1);
+    for (int ww = 1; ww < C::KW; ++ww) {
+      const float* src = reinterpret_cast<const float*>(((ww - 1) * C::QW + qw) == 0 ? vt0 : vt1);
       const float lb = src[(D / 2) * 64 + lane];
       const float mb = src[(D / 2 + 1) * 64 + lane];
       const float lrb = src[(D / 2 + 2) * 64 + lane];
-      const float mm = fmaxf(m_run, mb);
+      const float mm = fmaxf(w.m_run, mb);
       const float mref = (mm == -__builtin_inff()) ? 0.f : mm;
-      const float fa = __builtin_amdgcn_exp2f(m_run - mref);
+      const float fa = __builtin_amdgcn_exp2f(w.m_run - mref);
       const float fb = __builtin_amdgcn_exp2f(mb - mref);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          oacc[db][i] = oacc[db][i] * fa + src[(db * 16 + i) * 64 + lane] * fb;
-      l_run = l_run * fa + lb * fb;
-      lr_run = lr_run * fa + lrb * fb;
-      m_run = mm;
+          w.oacc[db][i] = w.oacc[db][i] * fa + src[(db * 16 + i) * 64 + lane] * fb;
+      w.l_run = w.l_run * fa + lb * fb;
+      w.lacc[0] = w.lacc[0] * fa + lrb * fb;
+      w.m_run = mm;
     }
   }
 
-  // ---- epilogue: O = O_acc / l (RNE to 16 bits), LSE = (m + log2 l) ln 2 ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float lr_tot = lr_run + __shfl_xor(lr_run, 32);
-  if (my_q < S) {
-    const float inv = 1.0f / lr_tot;
-    uint16_t* orow = o + head + (int64_t)my_q * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = db * 32 + 8 * g + 4 * half;
-        u32x2 w;
-        w[0] = E::pack2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv);
-        w[1] = E::pack2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + d) = w;
-      }
-    }
-    if (half == 0) {
-      lse[bh64 * (int64_t)S + my_q] =
-          (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f;
-    }
+  w.epilogue(o, lse, head, bh64);
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 2 (ping-pong): 8 waves in two groups of 4, one wave of each group
+// per SIMD.  A wave never overlaps its own MFMA and VALU work, but the SIMD
+// does overlap one wave's MFMAs with another wave's VALU instructions.  So
+// time is cut into phases X_j, Y_j separated by workgroup barriers, and in
+// each phase one group issues MFMA work while the other issues VALU work:
+//   X_j: group 0 pv(j-1), qk(j)      group 1 softmax(j-1)
+//   Y_j: group 0 softmax(j)          group 1 pv(j-1), qk(j)
+// Both groups run the same loop body [pv(j-1), qk(j)] barrier [softmax(j)]
+// barrier, j = 0..n; group 1 starts one phase later.  The MFMA half is the
+// same straight-line block in every phase: a tile a wave does not need (and
+// j = 0, j = n) gets P = 0, so its pv adds exact zeros, and its scores are
+// never used.  K and V tiles rotate through three LDS stages: group 0
+// issues the copies of K_{j+2} and V_{j+1} at the start of X_j and, before
+// the barrier that ends Y_j, waits for the copies issued one iteration
+// earlier (K_{j+1}, V_j), which X_{j+1} and Y_{j+1} read.
+// ---------------------------------------------------------------------------
+template <class C, bool CAUSAL, int DT>
+__global__ __launch_bounds__(C::NT) void attn_fwd_pingpong_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
+    int S, int nq, int64_t G, float c /* scale * log2(e), > 0 */) {
+  static_assert(C::NW == 8 && C::KW == 1, "ping-pong needs 8 query waves");
+  constexpr int D = C::D, BN = C::BN, BM = C::BM;
+  constexpr int LPW = C::LINES / 4;  // copy instructions per loading wave and operand
+  static_assert(3 * (C::K_TILE + C::V_TILE) <= 160 * 1024, "three stages must fit in LDS");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t kt0[C::K_TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t kt1[C::K_TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t kt2[C::K_TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vt0[C::V_TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vt1[C::V_TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vt2[C::V_TILE];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int group = wave >> 2;
+
+  int64_t tile64, bh64;
+  workgroup_tile(blockIdx.x, G, nq, CAUSAL, &tile64, &bh64);
+  const int q0 = (int)tile64 * BM;
+  const int64_t head = bh64 * (int64_t)S * D;
+  const uint16_t* kh = k + head;
+  const uint16_t* vh = v + head;
+
+  Wave<C, CAUSAL, DT> w;
+  w.init(q, head, q0 + wave * 32, 0, S, c);
+  w.zero_pf();
+
+  const int q_end = (q0 + BM < S) ? q0 + BM : S;
+  const int n = CAUSAL ? (q_end + BN - 1) / BN : (S + BN - 1) / BN;
+
+  // one loop iteration of this wave: kt_j holds K_j, vt_prev holds V_{j-1};
+  // K_{j+2} goes to kt_j2 and V_{j+1} to vt_j1
+  auto iter = [&](int j, const uint8_t* kt_j, uint8_t* kt_j2, uint8_t* vt_j1,
+                  const uint8_t* vt_prev) __attribute__((always_inline)) {
+    const bool load_k = group == 0 && j + 2 < n;
+    const bool load_v = group == 0 && j + 1 < n;
+    if (load_k) fetch_tile<C, true, 4>(kh, S, (j + 2) * BN, kt_j2, wave, lane);
+    if (load_v) fetch_tile<C, false, 4>(vh, S, (j + 1) * BN, vt_j1, wave, lane);
+    w.template mfma_ops<true, true>(vt_prev, kt_j);
+    barrier_keep_loads();
+    if (j < n && w.active(j)) w.softmax(j);
+    else w.zero_pf();
+    // the copies issued in the previous iteration must have landed
+    if (load_k) wait_loads_but<2 * LPW>();
+    else if (load_v) wait_loads_but<LPW>();
+    else wait_loads();
+    if (group == 0 || j < n) barrier_keep_loads();
+  };
+
+  // V stage 2 is read by pv(-1) before any copy fills it: make it zeros
+  for (int i = threadIdx.x * 16; i < C::V_TILE; i += C::NT * 16)
+    *reinterpret_cast<u32x4*>(vt2 + i) = u32x4{0u, 0u, 0u, 0u};
+  if (group == 0) {
+    fetch_tile<C, true, 4>(kh, S, 0, kt0, wave, lane);
+    if (n > 1) fetch_tile<C, true, 4>(kh, S, BN, kt1, wave, lane);
+    fetch_tile<C, false, 4>(vh, S, 0, vt0, wave, lane);
   }
+  wait_loads();
+  __syncthreads();
+  if (group == 1) barrier_keep_loads();  // group 1 idles through X_0
+  for (int j = 0; j <= n; j += 3) {
+    iter(j, kt0, kt2, vt1, vt2);
+    if (j + 1 <= n) iter(j + 1, kt1, kt0, vt2, vt0);
+    if (j + 2 <= n) iter(j + 2, kt2, kt1, vt0, vt1);
+  }
+
+  w.epilogue(o, lse, head, bh64);
 }
 
 }  // namespace attn
