@@ -50,13 +50,19 @@ def test_status_strings():
 
 def test_launch_geometry_matches_page():
     g = json.load(open(os.path.join(GOLDEN, "launch_geometry.json")))
-    # the D=64 instance uses the page's 128-row query tile
-    p = ea.attn_fwd_plan(1, 1, 128, 64, False, 0)
-    assert p["block_m"] == g["block_m"]
+    bm = g["block_m"]
     for c in g["cases"]:
-        p = ea.attn_fwd_plan(c["batch"], c["heads"], c["seq_len_q"], 64, False, 0)
-        assert p["num_q_tiles"] == c["grid_x"]
-        assert p["num_workgroups"] == c["grid_x"] * c["grid_y"]
+        # the page's rule with its 128-row tile gives its printed grid
+        assert -(-c["seq_len_q"] // bm) == c["grid_x"]
+        assert c["batch"] * c["heads"] == c["grid_y"]
+        # our plan applies the same rule with its own tile height, and the key
+        # length never enters the grid
+        for D in (64, 128, 256):
+            p = ea.attn_fwd_plan(c["batch"], c["heads"], c["seq_len_q"], D, False, 0)
+            assert p["num_q_tiles"] == -(-c["seq_len_q"] // p["block_m"])
+            assert p["num_workgroups"] == p["num_q_tiles"] * c["grid_y"]
+            if p["block_m"] == bm:
+                assert p["num_q_tiles"] == c["grid_x"]
 
 
 @pytest.mark.parametrize("D", [64, 128, 256])
