@@ -159,7 +159,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true", help="skip timing the other workloads")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
-                    help="also run one plain device copy of this many MiB (counter calibration)")
+                    help="also run one element-wise add reading and writing this many MiB "
+                         "(calibrates the HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -186,11 +187,15 @@ def main():
           f"{achieved:.1f} TFLOP/s ({achieved / PEAK_TFLOPS:.1%} of peak)", file=sys.stderr, flush=True)
 
     if args.calib_copy_mib:
+        # a plain streaming kernel of known traffic for HBM-counter calibration:
+        # reads and writes exactly calib_copy_mib MiB
         n = args.calib_copy_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)
-        dst.copy_(src)
         torch.cuda.synchronize()
+        torch.add(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     parity = parity_spot_check(shape, words, o, lse)
     print(f"# parity spot check: {parity}", file=sys.stderr, flush=True)
