@@ -44,10 +44,10 @@ int ok() {
 //   D=256: 2 query waves = 64 rows (the page's 64-row Q tile for D=256), each
 //          64-key tile split over 2 key waves, 138 KiB LDS
 #ifndef ATTN_CFG64
-#define ATTN_CFG64 64, 8, 1, 128, true
+#define ATTN_CFG64 64, 8, 1, 128, false
 #endif
 #ifndef ATTN_CFG128
-#define ATTN_CFG128 128, 8, 1, 64, true
+#define ATTN_CFG128 128, 8, 1, 128, true
 #endif
 #ifndef ATTN_CFG256
 #define ATTN_CFG256 256, 2, 2, 64

@@ -632,10 +632,12 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
 // barrier, j = 0..n; group 1 starts one phase later.  The MFMA half is the
 // same straight-line block in every phase: a tile a wave does not need (and
 // j = 0, j = n) gets P = 0, so its pv adds exact zeros, and its scores are
-// never used.  K and V tiles rotate through three LDS stages: group 0
-// issues the copies of K_{j+2} and V_{j+1} at the start of X_j and, before
-// the barrier that ends Y_j, waits for the copies issued one iteration
-// earlier (K_{j+1}, V_j), which X_{j+1} and Y_{j+1} read.
+// never used.  K and V tiles rotate through three LDS stages when they fit
+// (group 0 issues the copies of K_{j+2} and V_{j+1} at the start of X_j and,
+// before the barrier that ends Y_j, waits for the copies issued one
+// iteration earlier, K_{j+1} and V_j, which X_{j+1} and Y_{j+1} read), else
+// through two (K_{j+1} and V_j issued at the start of X_j, waited for at the
+// end of Y_j).
 // ---------------------------------------------------------------------------
 template <class C, bool CAUSAL, int DT>
 __global__ __launch_bounds__(C::NT) void attn_fwd_pingpong_kernel(
@@ -645,14 +647,16 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_pingpong_kernel(
   static_assert(C::NW == 8 && C::KW == 1, "ping-pong needs 8 query waves");
   constexpr int D = C::D, BN = C::BN, BM = C::BM;
   constexpr int LPW = C::LINES / 4;  // copy instructions per loading wave and operand
-  static_assert(3 * (C::K_TILE + C::V_TILE) <= 160 * 1024, "three stages must fit in LDS");
+  constexpr int ST = 3 * (C::K_TILE + C::V_TILE) <= 160 * 1024 ? 3 : 2;  // LDS stages
+  static_assert(2 * (C::K_TILE + C::V_TILE) <= 160 * 1024, "two stages must fit in LDS");
+  constexpr int T3 = ST == 3 ? 1 : 0;
 
   __shared__ __attribute__((aligned(1024))) uint8_t kt0[C::K_TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t kt1[C::K_TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t kt2[C::K_TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t kt2[T3 ? C::K_TILE : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t vt0[C::V_TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t vt1[C::V_TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t vt2[C::V_TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vt2[T3 ? C::V_TILE : 16];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -673,39 +677,53 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_pingpong_kernel(
   const int n = CAUSAL ? (q_end + BN - 1) / BN : (S + BN - 1) / BN;
 
   // one loop iteration of this wave: kt_j holds K_j, vt_prev holds V_{j-1};
-  // K_{j+2} goes to kt_j2 and V_{j+1} to vt_j1
-  auto iter = [&](int j, const uint8_t* kt_j, uint8_t* kt_j2, uint8_t* vt_j1,
+  // the copies of K_{j+ST-1} and V_{j+ST-2} go to kt_ld and vt_ld
+  auto iter = [&](int j, const uint8_t* kt_j, uint8_t* kt_ld, uint8_t* vt_ld,
                   const uint8_t* vt_prev) __attribute__((always_inline)) {
-    const bool load_k = group == 0 && j + 2 < n;
-    const bool load_v = group == 0 && j + 1 < n;
-    if (load_k) fetch_tile<C, true, 4>(kh, S, (j + 2) * BN, kt_j2, wave, lane);
-    if (load_v) fetch_tile<C, false, 4>(vh, S, (j + 1) * BN, vt_j1, wave, lane);
+    const bool load_k = group == 0 && j + ST - 1 < n;
+    const bool load_v = group == 0 && j + ST - 2 < n;
+    if (load_k) fetch_tile<C, true, 4>(kh, S, (j + ST - 1) * BN, kt_ld, wave, lane);
+    if (load_v) fetch_tile<C, false, 4>(vh, S, (j + ST - 2) * BN, vt_ld, wave, lane);
     w.template mfma_ops<true, true>(vt_prev, kt_j);
     barrier_keep_loads();
     if (j < n && w.active(j)) w.softmax(j);
     else w.zero_pf();
-    // the copies issued in the previous iteration must have landed
-    if (load_k) wait_loads_but<2 * LPW>();
-    else if (load_v) wait_loads_but<LPW>();
-    else wait_loads();
+    if constexpr (ST == 3) {
+      // the copies issued in the previous iteration must have landed
+      if (load_k) wait_loads_but<2 * LPW>();
+      else if (load_v) wait_loads_but<LPW>();
+      else wait_loads();
+    } else {
+      wait_loads();
+    }
     if (group == 0 || j < n) barrier_keep_loads();
   };
 
-  // V stage 2 is read by pv(-1) before any copy fills it: make it zeros
+  // the V stage read by pv(-1) before any copy fills it must hold zeros
+  uint8_t* const v_first_prev = T3 ? vt2 : vt1;
   for (int i = threadIdx.x * 16; i < C::V_TILE; i += C::NT * 16)
-    *reinterpret_cast<u32x4*>(vt2 + i) = u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(v_first_prev + i) = u32x4{0u, 0u, 0u, 0u};
   if (group == 0) {
     fetch_tile<C, true, 4>(kh, S, 0, kt0, wave, lane);
-    if (n > 1) fetch_tile<C, true, 4>(kh, S, BN, kt1, wave, lane);
-    fetch_tile<C, false, 4>(vh, S, 0, vt0, wave, lane);
+    if constexpr (ST == 3) {
+      if (n > 1) fetch_tile<C, true, 4>(kh, S, BN, kt1, wave, lane);
+      fetch_tile<C, false, 4>(vh, S, 0, vt0, wave, lane);
+    }
   }
   wait_loads();
   __syncthreads();
   if (group == 1) barrier_keep_loads();  // group 1 idles through X_0
-  for (int j = 0; j <= n; j += 3) {
-    iter(j, kt0, kt2, vt1, vt2);
-    if (j + 1 <= n) iter(j + 1, kt1, kt0, vt2, vt0);
-    if (j + 2 <= n) iter(j + 2, kt2, kt1, vt0, vt1);
+  if constexpr (ST == 3) {
+    for (int j = 0; j <= n; j += 3) {
+      iter(j, kt0, kt2, vt1, vt2);
+      if (j + 1 <= n) iter(j + 1, kt1, kt0, vt2, vt0);
+      if (j + 2 <= n) iter(j + 2, kt2, kt1, vt0, vt1);
+    }
+  } else {
+    for (int j = 0; j <= n; j += 2) {
+      iter(j, kt0, kt1, vt0, vt1);
+      if (j + 1 <= n) iter(j + 1, kt1, kt0, vt1, vt0);
+    }
   }
 
   w.epilogue(o, lse, head, bh64);
