@@ -24,11 +24,11 @@
 //     ds_read_b64_tr_b16 (each 16-lane group reads a 4-key x 16-d block and
 //     gets it back one d column per lane); the 4-key row groups are picked to
 //     match the key order of the packed P registers.
-//   * K and V tiles stream through two LDS stages: tile j+1 is fetched from
-//     HBM into VGPRs with 16-byte buffer loads while tile j is computed, then
-//     stored into the other stage; one workgroup barrier per tile.  Row
-//     strides are padded so the 16-byte K reads (8 rows per bank sweep) and
-//     the transposing V reads (4 rows of 32 bytes) hit disjoint banks.
+//   * K and V tiles stream through two or three LDS stages, copied straight
+//     from HBM into LDS by 16-byte buffer loads while earlier tiles are
+//     computed.  Row strides are padded so the 16-byte K reads (8 rows per
+//     bank sweep) and the transposing V reads (4 rows of 32 bytes) hit
+//     disjoint banks.
 //   * exp2/log2 are the hardware v_exp_f32/v_log_f32 with the scale folded
 //     as c = scale*log2(e); P and O are rounded to nearest-even.
 //   * Causal: key tiles wholly after a wave's last query are skipped, and
@@ -37,6 +37,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 namespace attn {
 
@@ -69,7 +71,10 @@ struct Elem<DT_F16> {
     v[1] = (_Float16)hi;
     return __builtin_bit_cast(uint32_t, v);
   }
-  static constexpr uint32_t kOnePair = 0x3C003C00u;  // (1.0, 1.0)
+  // acc + lo + hi of a packed pair, in fp32 (v_dot2c_f32_f16 against (1, 1))
+  static __device__ __forceinline__ float add_pair(uint32_t pair, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), __builtin_bit_cast(f16x2, 0x3C003C00u), acc, false);
+  }
 };
 
 template <>
@@ -84,7 +89,10 @@ struct Elem<DT_BF16> {
     v[1] = (__bf16)hi;
     return __builtin_bit_cast(uint32_t, v);
   }
-  static constexpr uint32_t kOnePair = 0x3F803F80u;  // (1.0, 1.0)
+  static __device__ __forceinline__ float add_pair(uint32_t pair, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), __builtin_bit_cast(bf16x2, 0x3F803F80u),
+                                           acc, false);
+  }
 };
 
 // ---------------------------------------------------------------------------
@@ -170,12 +178,29 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
-__device__ __forceinline__ float fmax4(float a, float b, float c, float d) {
-  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), __builtin_elementwise_maximum(c, d));
+// Maximum of x[0..N-1] as a tree of 3-input maxima (v_maximum3_f32: IEEE
+// maximum, no canonicalising moves; the inputs are never NaN): N/2 steps.
+template <int N>
+__device__ __forceinline__ float max_tree(const float* x) {
+  if constexpr (N == 1) {
+    return x[0];
+  } else if constexpr (N == 2) {
+    return __builtin_elementwise_maximum(x[0], x[1]);
+  } else {
+    constexpr int M = N / 3 + (N % 3 != 0);
+    float y[M];
+#pragma unroll
+    for (int i = 0; i < N / 3; ++i)
+      y[i] = __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[3 * i], x[3 * i + 1]), x[3 * i + 2]);
+    if constexpr (N % 3 == 1) y[N / 3] = x[N - 1];
+    if constexpr (N % 3 == 2) y[N / 3] = __builtin_elementwise_maximum(x[N - 2], x[N - 1]);
+    return max_tree<M>(y);
+  }
 }
 
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedMfma = 0x008;
+constexpr int kSchedVmem = 0x010;
 constexpr int kSchedDsRead = 0x100;
 
 // LDS read instructions of pipeline operand T: 2 transposing reads for a PV
@@ -185,8 +210,16 @@ constexpr int op_reads() {
   return T < NOPS ? (T < NPV ? 2 : 1) : 0;
 }
 
+// Does MFMA T of a block carry one of NL copy instructions (one after every
+// LSTRIDE-th MFMA, from the first)?
+template <int T, int NL, int LSTRIDE>
+constexpr bool copy_after() {
+  return NL > 0 && T % LSTRIDE == 0 && T / LSTRIDE < NL;
+}
+
 // Scheduling groups for a PIPE-deep operand pipeline of NOPS MFMAs: the
-// reads of operands 0..PIPE-1, then for each T: MFMA T, reads of T+PIPE.
+// reads of operands 0..PIPE-1, then for each T: MFMA T, reads of T+PIPE, and
+// the copy instruction that goes with MFMA T, if any.
 template <int T, int NOPS, int NPV, int PIPE>
 __device__ __forceinline__ void sched_prologue() {
   if constexpr (T < PIPE) {
@@ -195,15 +228,21 @@ __device__ __forceinline__ void sched_prologue() {
     sched_prologue<T + 1, NOPS, NPV, PIPE>();
   }
 }
-template <int T, int NOPS, int NPV, int PIPE>
+template <int T, int NOPS, int NPV, int PIPE, int NL, int LSTRIDE>
 __device__ __forceinline__ void sched_steady() {
   if constexpr (T < NOPS) {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
     if constexpr (op_reads<T + PIPE, NOPS, NPV>() > 0)
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, op_reads<T + PIPE, NOPS, NPV>(), 0);
-    sched_steady<T + 1, NOPS, NPV, PIPE>();
+    if constexpr (copy_after<T, NL, LSTRIDE>()) __builtin_amdgcn_sched_group_barrier(kSchedVmem, 1, 0);
+    sched_steady<T + 1, NOPS, NPV, PIPE, NL, LSTRIDE>();
   }
 }
+
+// Copy hook of an MFMA block that issues no copies.
+struct NoCopy {
+  __device__ __forceinline__ void operator()(int) const {}
+};
 
 // Buffer descriptor over `bytes` bytes at `base`: loads past the end return
 // zero, which pads the ragged last tile without any select after the load.
@@ -215,9 +254,11 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0);
 }
 
-// 16 bytes per lane from global memory straight into LDS at lds + 16*lane.
-__device__ __forceinline__ void load16_lds(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t byte_off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, (int)byte_off, 0, 0, 0);
+// 16 bytes per lane from global memory straight into LDS at lds + 16*lane;
+// the source is byte_off (per lane) + wave_off (wave-uniform, an SGPR).
+__device__ __forceinline__ void load16_lds(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t byte_off,
+                                           uint32_t wave_off = 0) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, (int)byte_off, (int)wave_off, 0, 0);
 }
 
 // Running-max hysteresis (log2 units): O, l are only rescaled when some row's
@@ -256,17 +297,13 @@ struct Wave {
   using E = Elem<DT>;
   static constexpr int D = C::D, BN = C::BN, NB = C::NB, DK = C::DK, DB = C::DB;
 
-  // A operand of all ones: ones^T P^T puts the sum of a column of P^T in
-  // every row of the result
-  static constexpr u32x4 kOnes = {E::kOnePair, E::kOnePair, E::kOnePair, E::kOnePair};
-
   u32x4 qf[DK];      // Q fragment (B operand of S^T), resident
   f32x16 oacc[DB];   // O^T accumulator
   f32x16 sacc[NB];   // scores of the tile between qk and softmax
   u32x4 pf[2 * NB];  // packed P of the tile between softmax and pv
-  f32x16 lacc;       // every row: running sum of the rounded P of this column
   float m_run;       // running max of c*s (log2 units)
   float l_run;       // partial running sum of the fp32 P over this lane's keys
+  float lr_run;      // the same sum over the P as rounded to 16 bits
   int lane, half, wq_first, wq_last, my_q, kbase, S, k_lane, v_lane;
   float c;
 
@@ -290,9 +327,9 @@ struct Wave {
     for (int kc = 0; kc < DK; ++kc) qf[kc] = load16(qr, off + kc * 32);
 #pragma unroll
     for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
-    lacc = f32x16{};
     m_run = -__builtin_inff();
     l_run = 0.f;
+    lr_run = 0.f;
   }
 
   // P of a tile this wave skips: the next pv then adds exact zeros
@@ -336,21 +373,14 @@ struct Wave {
       }
     }
 
-    // row max over this tile: a tree over the lane's 16*NB scores (short
-    // dependency chains), then across the lane pair
-    // (IEEE maximum: gfx950's v_maximum3_f32, no canonicalising moves; the
-    // scores are never NaN)
-    float part[4 * NB];
+    // row max over this tile: a tree over the lane's 16*NB scores, then
+    // across the lane pair
+    float sc[16 * NB];
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        part[4 * kb + g] = fmax4(sacc[kb][4 * g], sacc[kb][4 * g + 1], sacc[kb][4 * g + 2], sacc[kb][4 * g + 3]);
-#pragma unroll
-    for (int w = 4 * NB; w > 1; w /= 2)
-#pragma unroll
-      for (int i = 0; i < w / 2; ++i) part[i] = __builtin_elementwise_maximum(part[i], part[i + w / 2]);
-    const float mx = max_halves(part[0]);
+      for (int i = 0; i < 16; ++i) sc[16 * kb + i] = sacc[kb][i];
+    const float mx = max_halves(max_tree<16 * NB>(sc));
 
     // Rescale only when some row's max outgrew the reference by the slack
     // (always on the first tile, where m_run is -inf); the branch is uniform
@@ -361,7 +391,7 @@ struct Wave {
       const float alpha = (m_new == -__builtin_inff()) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
-      lacc *= alpha;
+      lr_run *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
     }
@@ -369,9 +399,8 @@ struct Wave {
 
     // P = exp2(c*s - m), rounded to nearest-even as the MFMA operand.  The
     // fp32 row sum feeds the LSE (a sum of rounded P would move it by up to
-    // 2^-9 relative in bf16); the sum of the rounded P, which normalises O
-    // so that its weights are exactly the ones V was multiplied by, is
-    // accumulated by the matrix core in pv.
+    // 2^-9 relative in bf16); the fp32 sum of the rounded P normalises O, so
+    // that its weights are exactly the ones V was multiplied by.
     float ls[2 * NB];
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb) {
@@ -391,6 +420,13 @@ struct Wave {
 #pragma unroll
       for (int i = 0; i < w / 2; ++i) ls[i] += ls[i + w / 2];
     l_run += ls[0];
+    // four independent chains of pair sums over the packed P
+    float lr[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 2 * NB; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) lr[e] = E::add_pair(pf[i][e], lr[e]);
+    lr_run += (lr[0] + lr[1]) + (lr[2] + lr[3]);
   }
 
   // O^T += V^T P^T.  MFMA k-slot t of this lane holds the key
@@ -408,19 +444,21 @@ struct Wave {
         const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
         oacc[db] = E::mfma(a, pf[ks], oacc[db]);
       }
-      lacc = E::mfma(kOnes, pf[ks], lacc);
     }
   }
 
   // The MFMA work of one phase as one software pipeline: pv (O^T += V^T P^T
   // over the tile in vt) when PV, then qk (S^T = K Q^T over the tile in kt)
   // when QK.  Operand t+PIPE is read from LDS while MFMA t runs, and the
-  // scheduling groups pin that interleave.
+  // scheduling groups pin that interleave.  copy(i), i < NL, issues the i-th
+  // HBM -> LDS copy instruction of the phase right after MFMA i*LSTRIDE, so
+  // the copies queue up one at a time behind running MFMAs instead of
+  // stalling the wave in a burst.
 #ifndef ATTN_PIPE
 #define ATTN_PIPE 4
 #endif
-  template <bool PV, bool QK, int PIPE = ATTN_PIPE>
-  __device__ __forceinline__ void mfma_ops(const uint8_t* vt, const uint8_t* kt) {
+  template <bool PV, bool QK, int NL = 0, int LSTRIDE = 1, class COPY = NoCopy, int PIPE = ATTN_PIPE>
+  __device__ __forceinline__ void mfma_ops(const uint8_t* vt, const uint8_t* kt, const COPY& copy = COPY{}) {
     constexpr int NPV = PV ? 2 * NB * DB : 0;
     constexpr int NQK = QK ? DK * NB : 0;
     constexpr int NOPS = NPV + NQK;
@@ -445,22 +483,23 @@ struct Wave {
       if (t < NPV) {
         const int ks = t / DB, db = t % DB;
         oacc[db] = E::mfma(a, pf[ks], oacc[db]);
-        if (db == DB - 1) lacc = E::mfma(kOnes, pf[ks], lacc);
       } else {
         const int t2 = t - NPV, kc = t2 / NB, kb = t2 % NB;
         sacc[kb] = E::mfma(a, qf[kc], kc == 0 ? f32x16{} : sacc[kb]);
       }
+      if (NL > 0 && t % LSTRIDE == 0 && t / LSTRIDE < NL) copy(t / LSTRIDE);
     }
+    static_assert(NL == 0 || (NL - 1) * LSTRIDE < NOPS, "copies must fit in the block");
     // desired order: the first PIPE operand reads, then MFMA t followed by
-    // the reads of operand t+PIPE
+    // the reads of operand t+PIPE (and its copy)
     sched_prologue<0, NOPS, NPV, PIPE>();
-    sched_steady<0, NOPS, NPV, PIPE>();
+    sched_steady<0, NOPS, NPV, PIPE, NL, LSTRIDE>();
   }
 
   // O = O_acc / l (RNE to 16 bits), LSE = (m + log2 l) ln 2.
   __device__ __forceinline__ void epilogue(uint16_t* o, float* lse, int64_t head, int64_t bh) {
     const float l_tot = sum_halves(l_run);
-    const float lr_tot = lacc[0];
+    const float lr_tot = sum_halves(lr_run);
     if (my_q < S) {
       const float inv = 1.0f / lr_tot;
       uint16_t* orow = o + head + (int64_t)my_q * D;
@@ -503,9 +542,15 @@ __device__ __forceinline__ void fetch_tile(const uint16_t* src_head, int S, int 
 }
 
 // Workgroup barrier that does not drain outstanding memory operations (the
-// HBM -> LDS prefetch stays in flight); the memory clobber keeps the compiler
-// from moving LDS accesses across it.
-__device__ __forceinline__ void barrier_keep_loads() { asm volatile("s_barrier" ::: "memory"); }
+// HBM -> LDS prefetch stays in flight).  The memory clobber keeps LDS accesses
+// on their side; the scheduling fences keep register-only work (MFMAs, VALU)
+// there too, which the clobber alone does not: without them the scheduler
+// sinks the last MFMAs of a phase below the barrier, into the next phase.
+__device__ __forceinline__ void barrier_keep_loads() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 // Wait for this wave's HBM -> LDS copies (vmcnt = 0).
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -592,7 +637,7 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
         for (int i = 0; i < 16; ++i) dst[(db * 16 + i) * 64 + lane] = w.oacc[db][i];
       dst[(D / 2) * 64 + lane] = w.l_run;
       dst[(D / 2 + 1) * 64 + lane] = w.m_run;
-      dst[(D / 2 + 2) * 64 + lane] = w.lacc[0];
+      dst[(D / 2 + 2) * 64 + lane] = w.lr_run;
     }
     __syncthreads();
     if (kw > 0) return;
@@ -612,7 +657,7 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
         for (int i = 0; i < 16; ++i)
           w.oacc[db][i] = w.oacc[db][i] * fa + src[(db * 16 + i) * 64 + lane] * fb;
       w.l_run = w.l_run * fa + lb * fb;
-      w.lacc[0] = w.lacc[0] * fa + lrb * fb;
+      w.lr_run = w.lr_run * fa + lrb * fb;
       w.m_run = mm;
     }
   }
@@ -622,23 +667,27 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
 
 // ---------------------------------------------------------------------------
 // Kernel 2 (ping-pong): 8 waves in two groups of 4, one wave of each group
-// per SIMD.  A wave never overlaps its own MFMA and VALU work, but the SIMD
-// does overlap one wave's MFMAs with another wave's VALU instructions.  So
-// time is cut into phases X_j, Y_j separated by workgroup barriers, and in
-// each phase one group issues MFMA work while the other issues VALU work:
+// per SIMD (waves w and w+4 share a SIMD).  The SIMD overlaps one wave's MFMAs
+// with another wave's VALU instructions, so time is cut into phases X_j, Y_j
+// separated by workgroup barriers, and in each phase one group issues MFMA
+// work while the other issues VALU work:
 //   X_j: group 0 pv(j-1), qk(j)      group 1 softmax(j-1)
 //   Y_j: group 0 softmax(j)          group 1 pv(j-1), qk(j)
-// Both groups run the same loop body [pv(j-1), qk(j)] barrier [softmax(j)]
+// Both groups run the loop body [pv(j-1), qk(j)] barrier [softmax(j)]
 // barrier, j = 0..n; group 1 starts one phase later.  The MFMA half is the
 // same straight-line block in every phase: a tile a wave does not need (and
 // j = 0, j = n) gets P = 0, so its pv adds exact zeros, and its scores are
-// never used.  K and V tiles rotate through three LDS stages when they fit
-// (group 0 issues the copies of K_{j+2} and V_{j+1} at the start of X_j and,
-// before the barrier that ends Y_j, waits for the copies issued one
-// iteration earlier, K_{j+1} and V_j, which X_{j+1} and Y_{j+1} read), else
-// through two (K_{j+1} and V_j issued at the start of X_j, waited for at the
-// end of Y_j).
+// never used.  K and V tiles rotate through three LDS stages when they fit,
+// else two.  Group 0 copies them: its MFMA block in X_j carries the copy
+// instructions of K_{j+ST-1} and V_{j+ST-2}, one after every LSTRIDE-th
+// MFMA, and before the barrier that ends Y_j it waits for the copies that
+// X_{j+1} reads (three stages: those of the previous iteration; two: those
+// of this one).  Copies past the last tile read through an empty buffer
+// descriptor: they fetch nothing and fill a stage no later phase reads.
 // ---------------------------------------------------------------------------
+#ifndef ATTN_LSTRIDE
+#define ATTN_LSTRIDE 3
+#endif
 template <class C, bool CAUSAL, int DT>
 __global__ __launch_bounds__(C::NT) void attn_fwd_pingpong_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -676,27 +725,58 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_pingpong_kernel(
   const int q_end = (q0 + BM < S) ? q0 + BM : S;
   const int n = CAUSAL ? (q_end + BN - 1) / BN : (S + BN - 1) / BN;
 
+  // lane part of a copy: row step*(lane / (D/8)) of the line, 16-byte chunk
+  // lane % (D/8)
+  const uint32_t k_lane_src = (16 * (lane / (D / 8))) * C::ROW_BYTES + (lane % (D / 8)) * 16;
+  const uint32_t v_lane_src = (4 * (lane / (D / 8))) * C::ROW_BYTES + (lane % (D / 8)) * 16;
+  // descriptor over the rows of the key tile starting at kv0 (empty past S)
+  auto tile_rsrc = [&](const uint16_t* src, int kv0) __attribute__((always_inline)) {
+    return make_rsrc(src + (int64_t)kv0 * D, kv0 < S ? (uint32_t)(S - kv0) * D * 2 : 0u);
+  };
+
   // one loop iteration of this wave: kt_j holds K_j, vt_prev holds V_{j-1};
-  // the copies of K_{j+ST-1} and V_{j+ST-2} go to kt_ld and vt_ld
-  auto iter = [&](int j, const uint8_t* kt_j, uint8_t* kt_ld, uint8_t* vt_ld,
+  // group 0 (COPIES) copies K_{j+ST-1} and V_{j+ST-2} into kt_ld and vt_ld
+  auto iter = [&](auto copies, int j, const uint8_t* kt_j, uint8_t* kt_ld, uint8_t* vt_ld,
                   const uint8_t* vt_prev) __attribute__((always_inline)) {
-    const bool load_k = group == 0 && j + ST - 1 < n;
-    const bool load_v = group == 0 && j + ST - 2 < n;
-    if (load_k) fetch_tile<C, true, 4>(kh, S, (j + ST - 1) * BN, kt_ld, wave, lane);
-    if (load_v) fetch_tile<C, false, 4>(vh, S, (j + ST - 2) * BN, vt_ld, wave, lane);
-    w.template mfma_ops<true, true>(vt_prev, kt_j);
+    constexpr bool COPIES = decltype(copies)::value;
+    if constexpr (COPIES) {
+      const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kh, (j + ST - 1) * BN);
+      const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vh, (j + ST - 2) * BN);
+      auto copy = [&](int i) __attribute__((always_inline)) {
+        if (i < LPW) {
+          const int ln = wave * LPW + i;
+          load16_lds(rk, kt_ld + ln * C::K_LINE, k_lane_src, C::k_line_row(ln) * C::ROW_BYTES);
+        } else {
+          const int ln = wave * LPW + i - LPW;
+          load16_lds(rv, vt_ld + ln * C::V_LINE, v_lane_src, C::v_line_row(ln) * C::ROW_BYTES);
+        }
+      };
+      w.template mfma_ops<true, true, 2 * LPW, ATTN_LSTRIDE>(vt_prev, kt_j, copy);
+    } else {
+      w.template mfma_ops<true, true>(vt_prev, kt_j);
+    }
     barrier_keep_loads();
     if (j < n && w.active(j)) w.softmax(j);
     else w.zero_pf();
-    if constexpr (ST == 3) {
-      // the copies issued in the previous iteration must have landed
-      if (load_k) wait_loads_but<2 * LPW>();
-      else if (load_v) wait_loads_but<LPW>();
+    if constexpr (COPIES) {
+      if constexpr (ST == 3) wait_loads_but<2 * LPW>();  // the previous iteration's copies landed
       else wait_loads();
-    } else {
-      wait_loads();
     }
-    if (group == 0 || j < n) barrier_keep_loads();
+    if (COPIES || j < n) barrier_keep_loads();
+  };
+  auto loop = [&](auto copies) __attribute__((always_inline)) {
+    if constexpr (ST == 3) {
+      for (int j = 0; j <= n; j += 3) {
+        iter(copies, j, kt0, kt2, vt1, vt2);
+        if (j + 1 <= n) iter(copies, j + 1, kt1, kt0, vt2, vt0);
+        if (j + 2 <= n) iter(copies, j + 2, kt2, kt1, vt0, vt1);
+      }
+    } else {
+      for (int j = 0; j <= n; j += 2) {
+        iter(copies, j, kt0, kt1, vt0, vt1);
+        if (j + 1 <= n) iter(copies, j + 1, kt1, kt0, vt1, vt0);
+      }
+    }
   };
 
   // the V stage read by pv(-1) before any copy fills it must hold zeros
@@ -712,18 +792,11 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_pingpong_kernel(
   }
   wait_loads();
   __syncthreads();
-  if (group == 1) barrier_keep_loads();  // group 1 idles through X_0
-  if constexpr (ST == 3) {
-    for (int j = 0; j <= n; j += 3) {
-      iter(j, kt0, kt2, vt1, vt2);
-      if (j + 1 <= n) iter(j + 1, kt1, kt0, vt2, vt0);
-      if (j + 2 <= n) iter(j + 2, kt2, kt1, vt0, vt1);
-    }
+  if (group == 0) {
+    loop(std::true_type{});
   } else {
-    for (int j = 0; j <= n; j += 2) {
-      iter(j, kt0, kt1, vt0, vt1);
-      if (j + 1 <= n) iter(j + 1, kt1, kt0, vt1, vt0);
-    }
+    barrier_keep_loads();  // group 1 idles through X_0
+    loop(std::false_type{});
   }
 
   w.epilogue(o, lse, head, bh64);
