@@ -170,7 +170,8 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
 __device__ __forceinline__ float max_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
                                                   false, false);
-  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+  return __builtin_elementwise_maximum(__builtin_bit_cast(float, (uint32_t)r[0]),
+                                      __builtin_bit_cast(float, (uint32_t)r[1]));
 }
 __device__ __forceinline__ float sum_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
@@ -302,8 +303,11 @@ struct Wave {
   f32x16 sacc[NB];   // scores of the tile between qk and softmax
   u32x4 pf[2 * NB];  // packed P of the tile between softmax and pv
   float m_run;       // running max of c*s (log2 units)
+  float nm_ref;      // -m_run, or 0 while m_run is -inf: the exp2 offset
+  float m_thr;       // m_run + kRescaleSlack: scores above it force a rescale
   float l_run;       // partial running sum of the fp32 P over this lane's keys
-  float lr_run;      // the same sum over the P as rounded to 16 bits
+  float lr4[4];      // the same sum over the P as rounded to 16 bits, in
+                     // four chains (one per word of a packed P register)
   int lane, half, wq_first, wq_last, my_q, kbase, S, k_lane, v_lane;
   float c;
 
@@ -328,8 +332,11 @@ struct Wave {
 #pragma unroll
     for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
     m_run = -__builtin_inff();
+    nm_ref = 0.f;
+    m_thr = -__builtin_inff();
     l_run = 0.f;
-    lr_run = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) lr4[e] = 0.f;
   }
 
   // P of a tile this wave skips: the next pv then adds exact zeros
@@ -383,19 +390,23 @@ struct Wave {
     const float mx = max_halves(max_tree<16 * NB>(sc));
 
     // Rescale only when some row's max outgrew the reference by the slack
-    // (always on the first tile, where m_run is -inf); the branch is uniform
-    // across the wave.
-    const float mt = (mx == -__builtin_inff()) ? mx : mx * c;
-    if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack) != 0) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = (m_new == -__builtin_inff()) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    // (always on the first tile with an unmasked key, m_run being -inf
+    // before); the branch is uniform across the wave.  c > 0, so a fully
+    // masked max stays -inf and never turns into NaN.
+    const float mt = mx * c;
+    if (__builtin_amdgcn_ballot_w64(mt > m_thr) != 0) {
+      const float m_new = __builtin_elementwise_maximum(m_run, mt);
+      const bool none = m_new == -__builtin_inff();
+      const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
+      nm_ref = none ? 0.f : -m_new;
+      m_thr = m_new + kRescaleSlack;
       l_run *= alpha;
-      lr_run *= alpha;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) lr4[e] *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
     }
-    const float m_ref = (m_run == -__builtin_inff()) ? 0.f : m_run;
 
     // P = exp2(c*s - m), rounded to nearest-even as the MFMA operand.  The
     // fp32 row sum feeds the LSE (a sum of rounded P would move it by up to
@@ -409,7 +420,7 @@ struct Wave {
         float p[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t)
-          p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * s2 + t], c, -m_ref));
+          p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * s2 + t], c, nm_ref));
         ls[2 * kb + s2] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
         pf[2 * kb + s2] = u32x4{E::pack2(p[0], p[1]), E::pack2(p[2], p[3]), E::pack2(p[4], p[5]),
                                 E::pack2(p[6], p[7])};
@@ -420,14 +431,16 @@ struct Wave {
 #pragma unroll
       for (int i = 0; i < w / 2; ++i) ls[i] += ls[i + w / 2];
     l_run += ls[0];
-    // four independent chains of pair sums over the packed P
-    float lr[4] = {0.f, 0.f, 0.f, 0.f};
+    // the sums of the rounded P (v_dot2 here: issued between the wave's
+    // own MFMAs instead, they stall the MFMA stream)
 #pragma unroll
     for (int i = 0; i < 2 * NB; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) lr[e] = E::add_pair(pf[i][e], lr[e]);
-    lr_run += (lr[0] + lr[1]) + (lr[2] + lr[3]);
+      for (int e = 0; e < 4; ++e) lr4[e] = E::add_pair(pf[i][e], lr4[e]);
   }
+
+  // all four chains of the rounded-P sum
+  __device__ __forceinline__ float lr_sum() const { return (lr4[0] + lr4[1]) + (lr4[2] + lr4[3]); }
 
   // O^T += V^T P^T.  MFMA k-slot t of this lane holds the key
   // 16*ks + 8*(t/4) + 4*half + t%4 (the score accumulator layout), so the
@@ -499,7 +512,7 @@ struct Wave {
   // O = O_acc / l (RNE to 16 bits), LSE = (m + log2 l) ln 2.
   __device__ __forceinline__ void epilogue(uint16_t* o, float* lse, int64_t head, int64_t bh) {
     const float l_tot = sum_halves(l_run);
-    const float lr_tot = sum_halves(lr_run);
+    const float lr_tot = sum_halves(lr_sum());
     if (my_q < S) {
       const float inv = 1.0f / lr_tot;
       uint16_t* orow = o + head + (int64_t)my_q * D;
@@ -637,7 +650,7 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
         for (int i = 0; i < 16; ++i) dst[(db * 16 + i) * 64 + lane] = w.oacc[db][i];
       dst[(D / 2) * 64 + lane] = w.l_run;
       dst[(D / 2 + 1) * 64 + lane] = w.m_run;
-      dst[(D / 2 + 2) * 64 + lane] = w.lr_run;
+      dst[(D / 2 + 2) * 64 + lane] = w.lr_sum();
     }
     __syncthreads();
     if (kw > 0) return;
@@ -657,7 +670,8 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
         for (int i = 0; i < 16; ++i)
           w.oacc[db][i] = w.oacc[db][i] * fa + src[(db * 16 + i) * 64 + lane] * fb;
       w.l_run = w.l_run * fa + lb * fb;
-      w.lr_run = w.lr_run * fa + lrb * fb;
+      w.lr4[0] = w.lr_sum() * fa + lrb * fb;
+      w.lr4[1] = w.lr4[2] = w.lr4[3] = 0.f;
       w.m_run = mm;
     }
   }
