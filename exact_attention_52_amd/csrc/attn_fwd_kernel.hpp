@@ -369,13 +369,17 @@ struct Wave {
     // mask keys past the end or after the query (diagonal / ragged tiles)
     const bool need_mask = (kv0 + C::KSUB > S) || (CAUSAL && kv0 + C::KSUB - 1 > wq_first);
     if (need_mask) {
+      // score i of block kb is key kv0 + 4*half + off(kb, i); it is kept iff
+      // key <= min(my_q, S-1) (causal) or key <= S-1: one compare of a
+      // constant offset against a per-lane limit
+      const int last = CAUSAL ? (my_q < S - 1 ? my_q : S - 1) : S - 1;
+      const int lim = last - kv0 - 4 * half;
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = kv0 + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-          const bool dead = key >= S || (CAUSAL && key > my_q);
-          sacc[kb][i] = dead ? -__builtin_inff() : sacc[kb][i];
+          const int off = kb * 32 + 8 * (i >> 2) + (i & 3);
+          sacc[kb][i] = off > lim ? -__builtin_inff() : sacc[kb][i];
         }
       }
     }
@@ -688,16 +692,17 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
 //   X_j: group 0 pv(j-1), qk(j)      group 1 softmax(j-1)
 //   Y_j: group 0 softmax(j)          group 1 pv(j-1), qk(j)
 // Both groups run the loop body [pv(j-1), qk(j)] barrier [softmax(j)]
-// barrier, j = 0..n; group 1 starts one phase later.  The MFMA half is the
-// same straight-line block in every phase: a tile a wave does not need (and
-// j = 0, j = n) gets P = 0, so its pv adds exact zeros, and its scores are
-// never used.  K and V tiles rotate through three LDS stages when they fit,
-// else two.  Group 0 copies them: its MFMA block in X_j carries the copy
-// instructions of K_{j+ST-1} and V_{j+ST-2}, one after every LSTRIDE-th
-// MFMA, and before the barrier that ends Y_j it waits for the copies that
-// X_{j+1} reads (three stages: those of the previous iteration; two: those
-// of this one).  Copies past the last tile read through an empty buffer
-// descriptor: they fetch nothing and fill a stage no later phase reads.
+// barrier, j = 0..n (n key tiles); group 1 starts one phase later.  The
+// first iteration has no pv and the last (j = n) no qk and no softmax; in
+// between the MFMA half is one straight-line block, and a tile a wave does
+// not need gets P = 0, so its pv adds exact zeros.  K and V tiles rotate
+// through three LDS stages when they fit, else two.  Group 0 copies them:
+// its MFMA block in X_j carries the copy instructions of K_{j+ST-1} and
+// V_{j+ST-2}, one after every few MFMAs, and before the barrier that ends
+// Y_j it waits for the copies that X_{j+1} reads (three stages: those of the
+// previous iteration; two: those of this one).  Copies past the last tile
+// read through an empty buffer descriptor: they fetch nothing and fill a
+// stage no later phase reads.
 // ---------------------------------------------------------------------------
 #ifndef ATTN_LSTRIDE
 #define ATTN_LSTRIDE 3
@@ -734,10 +739,9 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_pingpong_kernel(
 
   Wave<C, CAUSAL, DT> w;
   w.init(q, head, q0 + wave * 32, 0, S, c);
-  w.zero_pf();
 
   const int q_end = (q0 + BM < S) ? q0 + BM : S;
-  const int n = CAUSAL ? (q_end + BN - 1) / BN : (S + BN - 1) / BN;
+  const int n = CAUSAL ? (q_end + BN - 1) / BN : (S + BN - 1) / BN;  // >= 1
 
   // lane part of a copy: row step*(lane / (D/8)) of the line, 16-byte chunk
   // lane % (D/8)
@@ -748,12 +752,17 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_pingpong_kernel(
     return make_rsrc(src + (int64_t)kv0 * D, kv0 < S ? (uint32_t)(S - kv0) * D * 2 : 0u);
   };
 
-  // one loop iteration of this wave: kt_j holds K_j, vt_prev holds V_{j-1};
-  // group 0 (COPIES) copies K_{j+ST-1} and V_{j+ST-2} into kt_ld and vt_ld
-  auto iter = [&](auto copies, int j, const uint8_t* kt_j, uint8_t* kt_ld, uint8_t* vt_ld,
+  // One iteration of this wave.  PV, QK select the halves of the MFMA block;
+  // group 0 (COPIES) also copies the next tiles.  kt_j holds K_j, vt_prev
+  // holds V_{j-1}; the copies of K_{j+ST-1} and V_{j+ST-2} go to kt_ld and
+  // vt_ld.  The stages of iterations that copy are always named arrays: the
+  // compiler keeps apart LDS reads and in-flight copies only by their array.
+  auto iter = [&](auto copies, auto pv, auto qk, int j, const uint8_t* kt_j, uint8_t* kt_ld, uint8_t* vt_ld,
                   const uint8_t* vt_prev) __attribute__((always_inline)) {
     constexpr bool COPIES = decltype(copies)::value;
-    if constexpr (COPIES) {
+    constexpr bool PV = decltype(pv)::value, QK = decltype(qk)::value;
+    constexpr bool LAST = !QK;  // j = n: pv(n-1) only
+    if constexpr (COPIES && !LAST) {
       const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kh, (j + ST - 1) * BN);
       const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vh, (j + ST - 2) * BN);
       auto copy = [&](int i) __attribute__((always_inline)) {
@@ -765,38 +774,45 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_pingpong_kernel(
           load16_lds(rv, vt_ld + ln * C::V_LINE, v_lane_src, C::v_line_row(ln) * C::ROW_BYTES);
         }
       };
-      w.template mfma_ops<true, true, 2 * LPW, ATTN_LSTRIDE>(vt_prev, kt_j, copy);
+      constexpr int LS = (PV && QK) ? ATTN_LSTRIDE : 2;
+      w.template mfma_ops<PV, QK, 2 * LPW, LS>(vt_prev, kt_j, copy);
     } else {
-      w.template mfma_ops<true, true>(vt_prev, kt_j);
+      w.template mfma_ops<PV, QK>(vt_prev, kt_j);
     }
     barrier_keep_loads();
-    if (j < n && w.active(j)) w.softmax(j);
-    else w.zero_pf();
+    if constexpr (!LAST) {
+      if (w.active(j)) w.softmax(j);
+      else w.zero_pf();
+    }
     if constexpr (COPIES) {
-      if constexpr (ST == 3) wait_loads_but<2 * LPW>();  // the previous iteration's copies landed
+      if constexpr (ST == 3 && !LAST) wait_loads_but<2 * LPW>();  // the previous iteration's copies landed
       else wait_loads();
     }
-    if (COPIES || j < n) barrier_keep_loads();
+    if (COPIES || !LAST) barrier_keep_loads();
   };
   auto loop = [&](auto copies) __attribute__((always_inline)) {
+    using Y = std::true_type;
+    using N = std::false_type;
+    // stages of iteration j: kt[j % ST], kt[(j+ST-1) % ST], vt[(j+ST-2) % ST], vt[(j+ST-1) % ST]
     if constexpr (ST == 3) {
-      for (int j = 0; j <= n; j += 3) {
-        iter(copies, j, kt0, kt2, vt1, vt2);
-        if (j + 1 <= n) iter(copies, j + 1, kt1, kt0, vt2, vt0);
-        if (j + 2 <= n) iter(copies, j + 2, kt2, kt1, vt0, vt1);
+      iter(copies, N{}, Y{}, 0, kt0, kt2, vt1, vt2);
+      for (int j = 1; j < n; j += 3) {
+        iter(copies, Y{}, Y{}, j, kt1, kt0, vt2, vt0);
+        if (j + 1 < n) iter(copies, Y{}, Y{}, j + 1, kt2, kt1, vt0, vt1);
+        if (j + 2 < n) iter(copies, Y{}, Y{}, j + 2, kt0, kt2, vt1, vt2);
       }
+      const int r = (n - 1) % 3;
+      iter(copies, Y{}, N{}, n, kt0, kt0, vt0, r == 0 ? vt0 : (r == 1 ? vt1 : vt2));
     } else {
-      for (int j = 0; j <= n; j += 2) {
-        iter(copies, j, kt0, kt1, vt0, vt1);
-        if (j + 1 <= n) iter(copies, j + 1, kt1, kt0, vt1, vt0);
+      iter(copies, N{}, Y{}, 0, kt0, kt1, vt0, vt1);
+      for (int j = 1; j < n; j += 2) {
+        iter(copies, Y{}, Y{}, j, kt1, kt0, vt1, vt0);
+        if (j + 1 < n) iter(copies, Y{}, Y{}, j + 1, kt0, kt1, vt0, vt1);
       }
+      iter(copies, Y{}, N{}, n, kt0, kt0, vt0, (n & 1) ? vt0 : vt1);
     }
   };
 
-  // the V stage read by pv(-1) before any copy fills it must hold zeros
-  uint8_t* const v_first_prev = T3 ? vt2 : vt1;
-  for (int i = threadIdx.x * 16; i < C::V_TILE; i += C::NT * 16)
-    *reinterpret_cast<u32x4*>(v_first_prev + i) = u32x4{0u, 0u, 0u, 0u};
   if (group == 0) {
     fetch_tile<C, true, 4>(kh, S, 0, kt0, wave, lane);
     if constexpr (ST == 3) {
