@@ -106,6 +106,31 @@ def time_workload(ea, shape, dev, steps, warmup):
     return total / steps, float(np.mean(per)), o, lse
 
 
+def reference_gemm(n, steps=50):
+    """Context for the MFMA roofline: a plain fp16 n x n x n torch.matmul (the vendor
+    GEMM library) on random N(0,1) data, timed back to back like the attention launches.
+    Random-data MFMA work runs the card at its power limit, so this is the dense-MFMA
+    rate the box actually sustains; it is not used for any figure of merit."""
+    import torch
+    g = torch.Generator(device="cuda:0").manual_seed(0)
+    a = torch.randn(n, n, device="cuda:0", dtype=torch.float16, generator=g)
+    b = torch.randn(n, n, device="cuda:0", dtype=torch.float16, generator=g)
+    for _ in range(3):
+        c = a @ b
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        c = a @ b
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"what": f"torch.matmul fp16 {n}x{n}x{n}, random N(0,1), {steps} back to back",
+            "us_per_call": round(ms * 1e3, 1), "tflops": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)}
+
+
 def parity_spot_check(shape, words, o, lse, n_rows=128):
     import oracle
     from exact_attention_52_amd import inputs
@@ -158,6 +183,8 @@ def main():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true", help="skip timing the other workloads")
+    ap.add_argument("--ref-gemm", type=int, default=8192,
+                    help="also time an fp16 N^3 torch.matmul as context for the MFMA roofline (0: skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one element-wise add reading and writing this many MiB "
                          "(calibrates the HBM byte counters)")
@@ -215,6 +242,10 @@ def main():
             del dv
             torch.cuda.empty_cache()
 
+    gemm = reference_gemm(args.ref_gemm) if args.ref_gemm > 0 and not args.no_others else None
+    if gemm:
+        print(f"# reference gemm: {gemm}", file=sys.stderr, flush=True)
+
     cpu = None if args.no_cpu_baseline else cpu_baseline(shape, words)
     if cpu:
         print(f"# cpu baseline: {cpu}", file=sys.stderr, flush=True)
@@ -242,6 +273,7 @@ def main():
         "cpu_baseline": cpu,
         "parity_spot_check": parity,
         "other_workloads": others,
+        "reference_gemm": gemm,
     }
     print(json.dumps(line), flush=True)
 
