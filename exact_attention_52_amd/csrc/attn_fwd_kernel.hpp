@@ -268,18 +268,30 @@ __device__ __forceinline__ void load16_lds(__amdgpu_buffer_rsrc_t r, uint8_t* ld
 constexpr float kRescaleSlack = 8.0f;
 
 // Workgroup id -> (query tile, b*H + h).  Workgroups are handed to the 8 XCDs
-// round-robin, so id g runs on XCD g % 8 as that XCD's (g / 8)-th workgroup.
-// Give each XCD a contiguous run of logical work (whole heads where the counts
-// allow), in head order, and start every head with its heaviest causal tile.
+// round-robin in id order, so id g runs on XCD g % 8, and each XCD gives its
+// next workgroup to the first CU that frees up.
+//   Causal: tile costs differ (query tile t has t+1 tiles' worth of keys), so
+//   ids go in order of decreasing cost: id g takes the (g / heads)-th tile
+//   counted from the last and head g % heads.  Every XCD then runs its share
+//   longest first (list scheduling in longest-processing-time order, which
+//   pairs long and short tiles on each CU), and when heads is a multiple of 8
+//   all tiles of head h run on XCD h % 8 and share its L2.
+//   Non-causal: equal costs; each XCD gets a contiguous run of logical work
+//   (whole heads where the counts allow), in head order.
 __host__ __device__ inline void workgroup_tile(int64_t g, int64_t G, int64_t nq, int causal,
                                                int64_t* tile, int64_t* bh) {
+  if (causal) {
+    const int64_t heads = G / nq;
+    *bh = g % heads;
+    *tile = nq - 1 - g / heads;
+    return;
+  }
   const int64_t X = 8;
   const int64_t xcd = g % X, slot = g / X;
   const int64_t base = G / X, rem = G % X;
   const int64_t logical = xcd * base + (xcd < rem ? xcd : rem) + slot;
   *bh = logical / nq;
-  const int64_t t = logical % nq;
-  *tile = causal ? nq - 1 - t : t;
+  *tile = logical % nq;
 }
 
 // ---------------------------------------------------------------------------

@@ -112,8 +112,10 @@ int attn_fwd_plan(int64_t B, int64_t H, int64_t S, int64_t D, int causal,
 /*
  * attn_fwd_workgroup_tile -- which (query tile, b*H + h) the workgroup with
  * linear id `wg` (0 <= wg < num_workgroups) computes (host only).  The map is
- * a bijection; it keeps the tiles of one head on one XCD and, when causal,
- * starts each head with its heaviest (last) query tile.
+ * a bijection.  Non-causal: each XCD (workgroup id mod 8) gets a contiguous run
+ * of heads.  Causal: ids go in order of decreasing cost (last query tile of
+ * every head first), so each XCD runs its share longest first; when B*H is a
+ * multiple of 8, head h stays on XCD h mod 8.
  */
 int attn_fwd_workgroup_tile(int64_t B, int64_t H, int64_t S, int64_t D,
                             int causal, int dtype, int64_t wg,

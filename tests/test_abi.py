@@ -95,8 +95,8 @@ def test_supported_and_rejected_head_dims_and_types():
 
 
 @pytest.mark.parametrize("D,causal", [(64, False), (64, True), (128, True), (256, True), (128, False)])
-@pytest.mark.parametrize("B,H,S", [(1, 1, 1), (2, 3, 1000), (1, 8, 8192), (3, 1, 257)])
-def test_workgroup_map_is_bijection_and_heavy_first(B, H, S, D, causal):
+@pytest.mark.parametrize("B,H,S", [(1, 1, 1), (2, 3, 1000), (1, 8, 8192), (3, 1, 257), (4, 16, 2048)])
+def test_workgroup_map_is_bijection_and_longest_first(B, H, S, D, causal):
     p = ea.attn_fwd_plan(B, H, S, D, causal, 0)
     G, nq = p["num_workgroups"], p["num_q_tiles"]
     seen = set()
@@ -106,16 +106,35 @@ def test_workgroup_map_is_bijection_and_heavy_first(B, H, S, D, causal):
         assert 0 <= t < nq and 0 <= bh < B * H
         seen.add((t, bh))
         if causal:
-            # on each XCD (wg % 8) a head's tiles come heaviest (last) first
-            key = (wg % 8, bh)
-            assert last.get(key, nq) > t
+            # each XCD (wg % 8) is handed its tiles in order of non-increasing cost
+            # (tile t costs t + 1 key tiles)
+            key = wg % 8
+            assert last.get(key, nq) >= t
             last[key] = t
+            if (B * H) % 8 == 0:
+                assert bh % 8 == wg % 8  # a head's tiles share one XCD
     assert len(seen) == G
     if causal:
         t0, _ = ea.attn_fwd_workgroup_tile(B, H, S, D, causal, 0, 0)
         assert t0 == nq - 1
     with pytest.raises(_lib.AttnError):
         ea.attn_fwd_workgroup_tile(B, H, S, D, causal, 0, G)
+
+
+def test_causal_map_balances_each_xcd():
+    # c3 (B4 H16 S2048 D128 causal): 64 x 8 tiles, tile t costs t + 1. Greedy
+    # list scheduling of each XCD's workgroups, in id order, onto 32 CUs that
+    # each hold one workgroup at a time gives every CU the same total.
+    B, H, S, D = 4, 16, 2048, 128
+    p = ea.attn_fwd_plan(B, H, S, D, True, 1)
+    G = p["num_workgroups"]
+    for x in range(8):
+        cus = [0] * 32
+        for wg in range(x, G, 8):
+            t, _ = ea.attn_fwd_workgroup_tile(B, H, S, D, True, 1, wg)
+            i = min(range(32), key=lambda c: cus[c])
+            cus[i] += t + 1
+        assert max(cus) == min(cus)
 
 
 def test_workgroup_map_keeps_heads_on_one_xcd():
