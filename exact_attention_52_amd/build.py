@@ -20,6 +20,11 @@ FLAGS = [
     "-Wall", "-Wno-unused-command-line-argument",
     # keep the compiler from emitting packed-fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: left to its heuristics the compiler parks the
+    # D=256 output accumulator in AGPRs and copies all of it to VGPRs and back
+    # on every key tile (the rescale multiplies it on the VALU, which cannot
+    # address AGPRs); in VGPR form the kernel fits in 249 VGPRs with no copies
+    "-mllvm", "--amdgpu-mfma-vgpr-form=1",
 ]
 
 
