@@ -50,7 +50,7 @@ int ok() {
 #define ATTN_CFG128 128, 8, 1, 128, true
 #endif
 #ifndef ATTN_CFG256
-#define ATTN_CFG256 256, 2, 2, 64
+#define ATTN_CFG256 256, 2, 2, 64, false, true
 #endif
 using Cfg64 = attn::TileCfg<ATTN_CFG64>;
 using Cfg128 = attn::TileCfg<ATTN_CFG128>;

@@ -109,9 +109,10 @@ struct Elem<DT_BF16> {
 //   V: line L of a 4-line block holds rows L, L+4, ... (pad 64 B), so the 4
 //      consecutive rows of a transposing read, 64 bytes wide across two
 //      16-lane groups, sit 64 bytes apart modulo 256.
-template <int D_, int QW_, int KW_, int BN_, bool PINGPONG_ = false>
+template <int D_, int QW_, int KW_, int BN_, bool PINGPONG_ = false, bool STAGGER_ = false>
 struct TileCfg {
   static constexpr bool PINGPONG = PINGPONG_;  // use the two-group ping-pong kernel
+  static constexpr bool STAGGER = STAGGER_;    // kernel 1: staggered K/V copies, two barriers per tile
   static constexpr int D = D_;
   static constexpr int QW = QW_;             // waves along query rows
   static constexpr int KW = KW_;             // waves along each key tile
@@ -593,7 +594,19 @@ __device__ __forceinline__ void wait_loads_but() {
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 1: every wave runs qk, softmax, pv per tile; one barrier per tile.
+// Kernel 1: every wave runs qk, softmax, pv per tile; K and V tiles use two LDS
+// stages each.  Two copy schedules:
+//   STAGGER: every copy gets about a tile and a half to land, for workgroups
+//   that are alone on their CU (D=256):
+//     qk(j)      carries the copy of V_{j+1} (into the V stage pv(j-1) freed)
+//     softmax(j)
+//     wait V_j, barrier
+//     pv(j)      carries the copy of K_{j+2} (into the K stage qk(j) freed)
+//     wait K_{j+1}, barrier
+//   (the copy instructions ride in the MFMA blocks, one after every few MFMAs);
+//   otherwise K_{j+1} and V_{j+1} are copied while tile j is computed, with
+//   one barrier per tile, when two workgroups share a CU and cover each
+//   other's copy latency (D=64).
 // Supports key-split waves (KW > 1), merged at the end through LDS.
 // ---------------------------------------------------------------------------
 template <class C, bool CAUSAL, int DT>
@@ -602,6 +615,10 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
     int S, int nq, int64_t G, float c /* scale * log2(e), > 0 */) {
   constexpr int D = C::D, BN = C::BN, BM = C::BM, DB = C::DB;
+  constexpr int LPW = C::LINES / C::NW;              // copy lines per wave per operand
+  constexpr int NQK = C::DK * C::NB, NPV = 2 * C::NB * DB;  // MFMAs of qk, pv
+  constexpr int LSQ = NQK / LPW, LSP = NPV / LPW;      // MFMAs per copy
+  static_assert(LSQ >= 1 && LSP >= 1, "copies must fit in the MFMA blocks");
 
   // one array per stage and operand, so that the compiler can tell reads of
   // one stage from the asynchronous HBM->LDS copies into the other
@@ -626,32 +643,99 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
   w.init(q, head, q0 + qw * 32, kw * C::KSUB, S, c);
 
   const int q_end = (q0 + BM < S) ? q0 + BM : S;
-  const int n_tiles = CAUSAL ? (q_end + BN - 1) / BN : (S + BN - 1) / BN;
+  const int n = CAUSAL ? (q_end + BN - 1) / BN : (S + BN - 1) / BN;  // >= 1
 
-  auto fetch = [&](int j, uint8_t* kt, uint8_t* vt) __attribute__((always_inline)) {
-    fetch_tile<C, true>(kh, S, j * BN, kt, wave, lane);
-    fetch_tile<C, false>(vh, S, j * BN, vt, wave, lane);
+  // lane part of a copy: row step*(lane / (D/8)) of the line, 16-byte chunk
+  // lane % (D/8); a tile past the last one this workgroup needs reads through
+  // an empty descriptor (no fetch; it fills a stage no later step reads)
+  const uint32_t k_lane_src = (16 * (lane / (D / 8))) * C::ROW_BYTES + (lane % (D / 8)) * 16;
+  const uint32_t v_lane_src = (4 * (lane / (D / 8))) * C::ROW_BYTES + (lane % (D / 8)) * 16;
+  auto tile_rsrc = [&](const uint16_t* src, int t) __attribute__((always_inline)) {
+    const int kv0 = t * BN;
+    return make_rsrc(src + (int64_t)kv0 * D, (t < n && kv0 < S) ? (uint32_t)(S - kv0) * D * 2 : 0u);
   };
-  auto compute = [&](int j, const uint8_t* kt, const uint8_t* vt) __attribute__((always_inline)) {
-    if (!w.active(j)) return;
-    w.qk(kt);
-    w.softmax(j);
-    w.pv(vt);
+  auto k_copier = [&](int t, uint8_t* dst) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(kh, t);
+    return [=](int i) __attribute__((always_inline)) {
+      const int ln = wave * LPW + i;
+      load16_lds(r, dst + ln * C::K_LINE, k_lane_src, C::k_line_row(ln) * C::ROW_BYTES);
+    };
+  };
+  auto v_copier = [&](int t, uint8_t* dst) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(vh, t);
+    return [=](int i) __attribute__((always_inline)) {
+      const int ln = wave * LPW + i;
+      load16_lds(r, dst + ln * C::V_LINE, v_lane_src, C::v_line_row(ln) * C::ROW_BYTES);
+    };
   };
 
-  // two LDS stages, one barrier per tile
-  if (n_tiles > 0) fetch(0, kt0, vt0);
-  __syncthreads();
-  for (int j = 0; j < n_tiles; j += 2) {
-    if (j + 1 < n_tiles) fetch(j + 1, kt1, vt1);
-    compute(j, kt0, vt0);
+  if constexpr (C::STAGGER) {
+    // tile j: K_j in kt_j, V_j in vt_j; vt_o is the other V stage
+    auto iter = [&](int j, uint8_t* kt_j, uint8_t* vt_j, uint8_t* vt_o) __attribute__((always_inline)) {
+      const bool act = w.active(j);
+      const auto cv = v_copier(j + 1, vt_o);
+      if (act) {
+        w.template mfma_ops<false, true, LPW, LSQ>(vt_j, kt_j, cv);
+        w.softmax(j);
+      } else {
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) cv(i);
+      }
+      wait_loads_but<2 * LPW>();  // V_j landed (K_{j+1}, V_{j+1} may still be in flight)
+      barrier_keep_loads();       // V_j complete in LDS; every wave is done with kt_j
+      const auto ck = k_copier(j + 2, kt_j);
+      if (act) {
+        w.template mfma_ops<true, false, LPW, LSP>(vt_j, kt_j, ck);
+      } else {
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) ck(i);
+      }
+      wait_loads_but<2 * LPW>();  // K_{j+1} landed (V_{j+1}, K_{j+2} may still be in flight)
+      barrier_keep_loads();       // K_{j+1} complete in LDS; every wave is done with vt_j
+    };
+    {
+      const auto k0 = k_copier(0, kt0);
+      const auto v0 = v_copier(0, vt0);
+      const auto k1 = k_copier(1, kt1);
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) k0(i), v0(i), k1(i);
+    }
+    wait_loads();
     __syncthreads();
-    if (j + 1 < n_tiles) {
-      if (j + 2 < n_tiles) fetch(j + 2, kt0, vt0);
-      compute(j + 1, kt1, vt1);
+    for (int j = 0; j < n; j += 2) {
+      iter(j, kt0, vt0, vt1);
+      if (j + 1 < n) iter(j + 1, kt1, vt1, vt0);
+    }
+  } else {
+    auto fetch = [&](int j, uint8_t* kt, uint8_t* vt) __attribute__((always_inline)) {
+      const auto ck = k_copier(j, kt);
+      const auto cv = v_copier(j, vt);
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) ck(i), cv(i);
+    };
+    auto compute = [&](int j, const uint8_t* kt, const uint8_t* vt) __attribute__((always_inline)) {
+      if (!w.active(j)) return;
+      w.qk(kt);
+      w.softmax(j);
+      w.pv(vt);
+    };
+    fetch(0, kt0, vt0);
+    __syncthreads();
+    for (int j = 0; j < n; j += 2) {
+      if (j + 1 < n) fetch(j + 1, kt1, vt1);
+      compute(j, kt0, vt0);
       __syncthreads();
+      if (j + 1 < n) {
+        if (j + 2 < n) fetch(j + 2, kt0, vt0);
+        compute(j + 1, kt1, vt1);
+        __syncthreads();
+      }
     }
   }
+  wait_loads();  // the (empty) copies issued past the last tile
+  // the key-split merge below reuses the V stages: every wave's copies must
+  // have landed before any wave writes there
+  if constexpr (C::KW > 1) __syncthreads();
 
   // merge the key-split waves (KW > 1): partials of wave (kw, qw), kw > 0,
   // go to V stage (kw - 1) * QW + qw
