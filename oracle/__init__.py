@@ -44,6 +44,9 @@ def _load():
         lib.oracle_attn_fwd.argtypes = [vp, vp, vp, ci, i64, i64, i64, i64, dbl, ci,
                                         vp, i64, vp, vp]
         lib.oracle_attn_fwd.restype = ci
+        lib.oracle_attn_fwd_qk.argtypes = [vp, vp, vp, ci, i64, i64, i64, i64, i64, dbl, ci,
+                                           vp, i64, vp, vp]
+        lib.oracle_attn_fwd_qk.restype = ci
         lib.oracle_attn_fwd_online.argtypes = [vp, vp, vp, ci, i64, i64, i64, i64, dbl,
                                                ci, i64, vp, vp]
         lib.oracle_attn_fwd_online.restype = ci
@@ -79,28 +82,30 @@ def decode(bits, dtype: str) -> np.ndarray:
 def attn_fwd(q, k, v, dtype: str, scale: float, causal: bool, rows=None):
     """Two-pass fp64 attention.
 
-    q, k, v: uint16 [B,H,S,D].  rows: None (all rows; returns O [B,H,S,D],
-    LSE [B,H,S]) or flat row indices (b*H + h)*S + i (returns O [n,D],
-    LSE [n]).
+    q: uint16 [B,H,Sq,D]; k, v: uint16 [B,H,Skv,D] (Sq may differ from Skv;
+    causal then keeps key j for query i iff j <= i + Skv - Sq).  rows: None
+    (all rows; returns O [B,H,Sq,D], LSE [B,H,Sq]) or flat row indices
+    (b*H + h)*Sq + i (returns O [n,D], LSE [n]).
     """
     q, k, v = _words(q), _words(k), _words(v)
-    B, H, S, D = q.shape
-    if k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must share one shape")
+    B, H, Sq, D = q.shape
+    Skv = k.shape[2]
+    if k.shape != (B, H, Skv, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [B,H,Skv,D] with q's B, H, D")
     if rows is None:
-        o = np.empty((B, H, S, D), dtype=np.float64)
-        lse = np.empty((B, H, S), dtype=np.float64)
+        o = np.empty((B, H, Sq, D), dtype=np.float64)
+        lse = np.empty((B, H, Sq), dtype=np.float64)
         rp, n = None, 0
     else:
         rows = np.ascontiguousarray(rows, dtype=np.int64)
-        if rows.size and (rows.min() < 0 or rows.max() >= B * H * S):
+        if rows.size and (rows.min() < 0 or rows.max() >= B * H * Sq):
             raise ValueError("row index out of range")
         o = np.empty((rows.size, D), dtype=np.float64)
         lse = np.empty((rows.size,), dtype=np.float64)
         rp, n = rows.ctypes.data, rows.size
-    rc = _load().oracle_attn_fwd(q.ctypes.data, k.ctypes.data, v.ctypes.data,
-                                 _DT[dtype], B, H, S, D, float(scale), int(bool(causal)),
-                                 rp, n, o.ctypes.data, lse.ctypes.data)
+    rc = _load().oracle_attn_fwd_qk(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                    _DT[dtype], B, H, Sq, Skv, D, float(scale),
+                                    int(bool(causal)), rp, n, o.ctypes.data, lse.ctypes.data)
     if rc != 0:
         raise MemoryError("oracle scratch allocation failed")
     return o, lse

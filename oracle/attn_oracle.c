@@ -11,7 +11,7 @@
  * FlashAttention3Plan::generate_forward, and the `causal` field of
  * FlashAttention3Config): for every batch b, head h and query row i,
  *
- *   A_i  = { j : 0 <= j < S, and j <= i when causal }
+ *   A_i  = { j : 0 <= j < Skv, and j <= i + (Skv - Sq) when causal }
  *   s_ij = scale * sum_d q[b,h,i,d] * k[b,h,j,d]
  *   m_i  = max_{j in A_i} s_ij
  *   l_i  = sum_{j in A_i} exp(s_ij - m_i)
@@ -19,8 +19,12 @@
  *   LSE_i = m_i + ln(l_i)
  *
  * Readings where the page is silent: the log-sum-exp is the natural logarithm
- * of the scaled, masked scores; causal keeps key j for query i iff j <= i;
- * tensors are contiguous [B,H,S,D] (LSE [B,H,S]); inputs are the 16-bit
+ * of the scaled, masked scores; queries and keys may differ in length (the
+ * page's kernel takes separate query and key/value lengths), and causal then
+ * aligns the last query with the last key: query i (of Sq) keeps key j (of
+ * Skv) iff j <= i + (Skv - Sq), which is j <= i when Sq == Skv; a query with
+ * no key left (Sq > Skv) gets O = 0 and LSE = -inf; tensors are contiguous
+ * Q, O [B,H,Sq,D], K, V [B,H,Skv,D], LSE [B,H,Sq]; inputs are the 16-bit
  * words the GPU receives (fp16 or bf16), widened exactly to float64.
  *
  * Three routines:
@@ -94,18 +98,20 @@ void oracle_decode(const uint16_t* bits, int dtype, int64_t n, double* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = t[bits[i]];
 }
 
-/* Number of keys query i may attend to. */
-static int64_t allowed_keys(int64_t i, int64_t S, int causal) {
-  return causal ? (i + 1 < S ? i + 1 : S) : S;
+/* Number of keys query i may attend to (keys 0 .. n-1). */
+static int64_t allowed_keys(int64_t i, int64_t Sq, int64_t Skv, int causal) {
+  if (!causal) return Skv;
+  int64_t n = i + 1 + (Skv - Sq);
+  return n < 0 ? 0 : (n < Skv ? n : Skv);
 }
 
 static void scores_row(const double* tab, const uint16_t* q, const uint16_t* k,
-                       int64_t bh, int64_t i, int64_t S, int64_t D,
+                       int64_t bh, int64_t i, int64_t Sq, int64_t Skv, int64_t D,
                        double scale, int64_t n, double* qd, double* s) {
-  const uint16_t* qrow = q + (bh * S + i) * D;
+  const uint16_t* qrow = q + (bh * Sq + i) * D;
   for (int64_t d = 0; d < D; ++d) qd[d] = tab[qrow[d]];
   for (int64_t j = 0; j < n; ++j) {
-    const uint16_t* krow = k + (bh * S + j) * D;
+    const uint16_t* krow = k + (bh * Skv + j) * D;
     double acc = 0.0;
     for (int64_t d = 0; d < D; ++d) acc += qd[d] * tab[krow[d]];
     s[j] = scale * acc;
@@ -113,22 +119,23 @@ static void scores_row(const double* tab, const uint16_t* q, const uint16_t* k,
 }
 
 /*
- * rows: flat row indices r = (b*H + h)*S + i, or NULL for all B*H*S rows in
- * order.  o receives nrows*D values, lse nrows values.  Returns 0, or -1 when
+ * Queries of length Sq against keys/values of length Skv.  rows: flat query
+ * row indices r = (b*H + h)*Sq + i, or NULL for all B*H*Sq rows in order.
+ * o receives nrows*D values, lse nrows values.  Returns 0, or -1 when
  * scratch memory cannot be had.
  */
-int oracle_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                    int dtype, int64_t B, int64_t H, int64_t S, int64_t D,
-                    double scale, int causal, const int64_t* rows,
-                    int64_t nrows, double* o, double* lse) {
+int oracle_attn_fwd_qk(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                       int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
+                       int64_t D, double scale, int causal, const int64_t* rows,
+                       int64_t nrows, double* o, double* lse) {
   init_tables();
   const double* tab = table_for(dtype);
-  if (rows == NULL) nrows = B * H * S;
+  if (rows == NULL) nrows = B * H * Sq;
   int failed = 0;
 #pragma omp parallel
   {
     double* qd = (double*)malloc(sizeof(double) * (size_t)(D > 0 ? D : 1));
-    double* s = (double*)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+    double* s = (double*)malloc(sizeof(double) * (size_t)(Skv > 0 ? Skv : 1));
     double* acc = (double*)malloc(sizeof(double) * (size_t)(D > 0 ? D : 1));
     if (!qd || !s || !acc) {
 #pragma omp atomic write
@@ -137,15 +144,15 @@ int oracle_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 #pragma omp for schedule(dynamic, 8)
       for (int64_t t = 0; t < nrows; ++t) {
         int64_t r = rows ? rows[t] : t;
-        int64_t bh = r / S, i = r % S;
-        int64_t n = allowed_keys(i, S, causal);
+        int64_t bh = r / Sq, i = r % Sq;
+        int64_t n = allowed_keys(i, Sq, Skv, causal);
         double* orow = o + t * D;
         if (n <= 0) {
           for (int64_t d = 0; d < D; ++d) orow[d] = 0.0;
           lse[t] = -INFINITY;
           continue;
         }
-        scores_row(tab, q, k, bh, i, S, D, scale, n, qd, s);
+        scores_row(tab, q, k, bh, i, Sq, Skv, D, scale, n, qd, s);
         /* pass 1: the row maximum */
         double m = s[0];
         for (int64_t j = 1; j < n; ++j) m = s[j] > m ? s[j] : m;
@@ -155,7 +162,7 @@ int oracle_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
         for (int64_t j = 0; j < n; ++j) {
           double p = exp(s[j] - m);
           l += p;
-          const uint16_t* vrow = v + (bh * S + j) * D;
+          const uint16_t* vrow = v + (bh * Skv + j) * D;
           for (int64_t d = 0; d < D; ++d) acc[d] += p * tab[vrow[d]];
         }
         for (int64_t d = 0; d < D; ++d) orow[d] = acc[d] / l;
@@ -167,6 +174,14 @@ int oracle_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     free(acc);
   }
   return failed ? -1 : 0;
+}
+
+/* Equal query and key lengths S. */
+int oracle_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                    int dtype, int64_t B, int64_t H, int64_t S, int64_t D,
+                    double scale, int causal, const int64_t* rows,
+                    int64_t nrows, double* o, double* lse) {
+  return oracle_attn_fwd_qk(q, k, v, dtype, B, H, S, S, D, scale, causal, rows, nrows, o, lse);
 }
 
 /*
@@ -195,9 +210,9 @@ int oracle_attn_fwd_online(const uint16_t* q, const uint16_t* k,
 #pragma omp for schedule(dynamic, 8)
       for (int64_t r = 0; r < nrows; ++r) {
         int64_t bh = r / S, i = r % S;
-        int64_t n = allowed_keys(i, S, causal);
+        int64_t n = allowed_keys(i, S, S, causal);
         double* orow = o + r * D;
-        scores_row(tab, q, k, bh, i, S, D, scale, n, qd, s);
+        scores_row(tab, q, k, bh, i, S, S, D, scale, n, qd, s);
         double m = -INFINITY, l = 0.0;
         for (int64_t d = 0; d < D; ++d) acc[d] = 0.0;
         for (int64_t j0 = 0; j0 < n; j0 += block) {
@@ -248,10 +263,10 @@ int oracle_attn_probs(const uint16_t* q, const uint16_t* k, int dtype,
   for (int64_t bh = 0; bh < B * H; ++bh) {
     for (int64_t i = 0; i < S; ++i) {
       double* prow = p + (bh * S + i) * S;
-      int64_t n = allowed_keys(i, S, causal);
+      int64_t n = allowed_keys(i, S, S, causal);
       for (int64_t j = 0; j < S; ++j) prow[j] = 0.0;
       if (n <= 0) continue;
-      scores_row(tab, q, k, bh, i, S, D, scale, n, qd, s);
+      scores_row(tab, q, k, bh, i, S, S, D, scale, n, qd, s);
       double m = s[0];
       for (int64_t j = 1; j < n; ++j) m = s[j] > m ? s[j] : m;
       double l = 0.0;

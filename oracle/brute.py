@@ -23,20 +23,26 @@ def decode(word: int, dtype: str) -> float:
 
 
 def attention(q, k, v, dtype: str, scale: float, causal: bool):
-    """q, k, v: nested lists [B][H][S][D] of 16-bit words.
+    """q: nested lists [B][H][Sq][D], k, v: [B][H][Skv][D] of 16-bit words.
 
+    Causal keeps key j for query i iff j <= i + Skv - Sq (the last query sees
+    the last key); a query with no key gets O = 0 and LSE = -inf.
     Returns (O, LSE) as nested lists of Python floats.
     """
-    B, H, S, D = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
-    O = [[[[0.0] * D for _ in range(S)] for _ in range(H)] for _ in range(B)]
-    L = [[[0.0] * S for _ in range(H)] for _ in range(B)]
+    B, H, Sq, D = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    Skv = len(k[0][0])
+    O = [[[[0.0] * D for _ in range(Sq)] for _ in range(H)] for _ in range(B)]
+    L = [[[0.0] * Sq for _ in range(H)] for _ in range(B)]
     for b in range(B):
         for h in range(H):
             Q = [[decode(w, dtype) for w in row] for row in q[b][h]]
             K = [[decode(w, dtype) for w in row] for row in k[b][h]]
             V = [[decode(w, dtype) for w in row] for row in v[b][h]]
-            for i in range(S):
-                keys = range(i + 1) if causal else range(S)
+            for i in range(Sq):
+                keys = range(max(0, min(Skv, i + 1 + Skv - Sq))) if causal else range(Skv)
+                if not keys:
+                    L[b][h][i] = -math.inf
+                    continue
                 s = {j: scale * math.fsum(Q[i][d] * K[j][d] for d in range(D))
                      for j in keys}
                 m = max(s.values())

@@ -242,3 +242,88 @@ def test_decoder_matches_torch(oracle_mod):
         fin = np.isfinite(ref)
         assert np.array_equal(got[fin], ref[fin])
         assert np.array_equal(np.isnan(got), np.isnan(ref))
+
+
+# --------------------------------------------------------------------------
+# Unequal query and key lengths (Sq != Skv).  Reading: causal aligns the last
+# query with the last key (query i keeps key j iff j <= i + Skv - Sq); a query
+# with no key left gets O = 0 and LSE = -inf.
+# --------------------------------------------------------------------------
+QK_TINY = [(1, 1, 1, 5, 3), (1, 2, 3, 7, 2), (2, 1, 6, 2, 4), (1, 1, 4, 4, 5), (1, 2, 5, 1, 3),
+           (2, 2, 2, 9, 8)]
+
+
+def gen_qk(B, H, Sq, Skv, D, dtype, seed, mult=1.0):
+    q, _, _ = inputs.gen_qkv(B, H, Sq, D, dtype, seed=seed, qk_mult=mult)
+    _, k, v = inputs.gen_qkv(B, H, Skv, D, dtype, seed=seed + 1, qk_mult=mult)
+    return q, k, v
+
+
+@pytest.mark.parametrize("shape", QK_TINY)
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_qk_brute_force(oracle_mod, shape, causal, dtype):
+    B, H, Sq, Skv, D = shape
+    seed = zlib.crc32(repr((shape, causal, dtype)).encode()) & 0xFFFF
+    q, k, v = gen_qk(B, H, Sq, Skv, D, dtype, seed, mult=2.0)
+    scale = 1 / math.sqrt(D)
+    o, lse = oracle_mod.attn_fwd(q, k, v, dtype, scale, causal)
+    ob, lb = brute.attention(q.tolist(), k.tolist(), v.tolist(), dtype, scale, causal)
+    assert np.allclose(o, np.array(ob), rtol=1e-13, atol=1e-13)
+    assert np.allclose(lse, np.array(lb), rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("Sq,Skv", [(37, 101), (101, 37), (64, 64)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_qk_matches_torch_float64_sdpa(oracle_mod, Sq, Skv, causal):
+    B, H, D, dtype = 2, 2, 64, "bf16"
+    scale = 0.125
+    q, k, v = gen_qk(B, H, Sq, Skv, D, dtype, seed=5, mult=2.0)
+    o, lse = oracle_mod.attn_fwd(q, k, v, dtype, scale, causal)
+    tq, tk, tv = (torch.from_numpy(exact(x, dtype)) for x in (q, k, v))
+    i = torch.arange(Sq)[:, None]
+    j = torch.arange(Skv)[None, :]
+    keep = (j <= i + (Skv - Sq)) if causal else torch.ones(Sq, Skv, dtype=torch.bool)
+    live = keep.any(dim=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=keep, scale=scale)
+    s = (scale * (tq @ tk.transpose(-1, -2))).masked_fill(~keep, float("-inf"))
+    ref_lse = torch.logsumexp(s, dim=-1)
+    assert np.allclose(o[:, :, live.numpy()], ref[:, :, live].numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(lse[:, :, live.numpy()], ref_lse[:, :, live].numpy(), rtol=1e-12, atol=1e-12)
+    assert np.all(o[:, :, ~live.numpy()] == 0.0)
+    assert np.all(lse[:, :, ~live.numpy()] == -np.inf)
+
+
+@pytest.mark.parametrize("Sq", [1, 9, 40])
+def test_qk_causal_queries_are_the_last_rows_of_the_square_problem(oracle_mod, Sq):
+    # Sq queries against Skv keys, causal, is the same as the last Sq query
+    # rows of the square causal problem over the Skv positions
+    B, H, Skv, D, dtype = 1, 2, 48, 16, "fp16"
+    qf, k, v = inputs.gen_qkv(B, H, Skv, D, dtype, seed=9, qk_mult=2.0)
+    o_sq, l_sq = oracle_mod.attn_fwd(qf, k, v, dtype, 0.3, True)
+    o, lse = oracle_mod.attn_fwd(qf[:, :, Skv - Sq:], k, v, dtype, 0.3, True)
+    assert np.array_equal(o, o_sq[:, :, Skv - Sq:])
+    assert np.array_equal(lse, l_sq[:, :, Skv - Sq:])
+
+
+def test_qk_single_query_sees_every_key(oracle_mod):
+    q, k, v = gen_qk(2, 3, 1, 77, 32, "fp16", seed=21)
+    oc, lc = oracle_mod.attn_fwd(q, k, v, "fp16", 0.2, True)
+    on, ln = oracle_mod.attn_fwd(q, k, v, "fp16", 0.2, False)
+    assert np.array_equal(oc, on) and np.array_equal(lc, ln)
+
+
+def test_qk_more_queries_than_keys(oracle_mod):
+    B, H, Sq, Skv, D, dtype = 1, 2, 10, 4, 8, "bf16"
+    q, k, v = gen_qk(B, H, Sq, Skv, D, dtype, seed=31)
+    o, lse = oracle_mod.attn_fwd(q, k, v, dtype, 0.5, True)
+    first = Sq - Skv
+    assert np.all(o[:, :, :first] == 0.0) and np.all(lse[:, :, :first] == -np.inf)
+    # the first query with a key sees key 0 only
+    qq, kk, vv = exact(q, dtype), exact(k, dtype), exact(v, dtype)
+    assert np.array_equal(o[:, :, first], vv[:, :, 0])
+    s00 = 0.5 * (qq[:, :, first] * kk[:, :, 0]).sum(-1)
+    assert np.allclose(lse[:, :, first], s00, rtol=0, atol=1e-14)
+    # and the last query sees every key
+    on, ln = oracle_mod.attn_fwd(q, k, v, dtype, 0.5, False)
+    assert np.array_equal(o[:, :, -1], on[:, :, -1]) and np.array_equal(lse[:, :, -1], ln[:, :, -1])
