@@ -1,10 +1,11 @@
 """Exact attention forward for MI355X (gfx950).
 
-``fwd(q, k, v, scale=None, causal=False)`` returns ``(o, lse)`` for contiguous
-[B,H,S,D] fp16/bf16 CUDA tensors: O = softmax(scale * Q K^T [causal]) V and
-the natural-log LSE per row (fp32).  PyTorch only provides device memory and
-the stream; the computation is the libattn.so gfx950 kernel behind the C ABI
-of include/attn.h.  ``inputs`` holds the seeded synthetic-input generator.
+``fwd(q, k, v, scale=None, causal=False)`` returns ``(o, lse)`` for fp16/bf16
+CUDA tensors q [B,H,Sq,D] and k, v [B,H,Skv,D] (any strides with the last
+dimension contiguous): O = softmax(scale * Q K^T [causal]) V and the
+natural-log LSE per row (fp32).  PyTorch only provides device memory and the
+stream; the computation is the libattn.so gfx950 kernel behind the C ABI of
+include/attn.h.  ``inputs`` holds the seeded synthetic-input generator.
 """
 from __future__ import annotations
 
@@ -13,9 +14,11 @@ import math
 from . import _lib
 from ._lib import ATTN_BF16, ATTN_F16, AttnError  # noqa: F401
 
-__all__ = ["fwd", "attn_fwd", "attn_fwd_plan", "attn_fwd_workgroup_tile", "AttnError"]
+__all__ = ["fwd", "attn_fwd", "attn_fwd_strided", "attn_fwd_plan", "attn_fwd_workgroup_tile",
+           "AttnError"]
 
 attn_fwd = _lib.attn_fwd
+attn_fwd_strided = _lib.attn_fwd_strided
 attn_fwd_plan = _lib.attn_fwd_plan
 attn_fwd_workgroup_tile = _lib.attn_fwd_workgroup_tile
 
@@ -32,35 +35,48 @@ def _dtype_code(t):
 def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
     """Run the attention forward on the current (or given) stream.
 
-    q, k, v: contiguous CUDA tensors [B,H,S,D] of one dtype (fp16 or bf16).
-    scale defaults to 1/sqrt(D).  out / lse may be passed preallocated.
-    Returns (o, lse) with o [B,H,S,D] in the input dtype and lse [B,H,S] fp32.
+    q: CUDA tensor [B,H,Sq,D]; k, v: [B,H,Skv,D]; one dtype (fp16 or bf16);
+    any strides with the last dimension contiguous (e.g. views of [B,S,H,D]).
+    Causal keeps key j for query i iff j <= i + Skv - Sq.  scale defaults to
+    1/sqrt(D).  out ([B,H,Sq,D], input dtype, any such strides) and lse
+    (contiguous fp32 [B,H,Sq]) may be passed preallocated.  Returns (o, lse).
     """
     import torch
-    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must all be [B,H,S,D] with one shape")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D: [B,H,Sq,D], [B,H,Skv,D], [B,H,Skv,D]")
+    B, H, Sq, D = q.shape
+    Skv = k.shape[2]
+    if k.shape != (B, H, Skv, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [B,H,Skv,D] with q's B, H and D")
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k, v must be GPU tensors")
-    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
-        raise ValueError("q, k, v must be contiguous")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share one dtype")
     dt = _dtype_code(q)
-    B, H, S, D = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty((B, H, Sq, D), dtype=q.dtype, device=q.device)
     if lse is None:
-        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
-    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor like q")
-    if lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B,H,S] tensor")
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must be [B,H,Sq,D] in the input dtype")
+    if lse.shape != (B, H, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B,H,Sq] tensor")
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if D > 1 and t.stride(3) != 1:
+            raise ValueError(f"{name} must have its last dimension contiguous")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    plain = Sq == Skv and all(t.is_contiguous() for t in (q, k, v, out))
     with torch.cuda.device(q.device):
-        st = _lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                           lse.data_ptr(), B, H, S, D, scale, causal, dt, stream.cuda_stream)
+        if plain:
+            st = _lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                               lse.data_ptr(), B, H, Sq, D, scale, causal, dt, stream.cuda_stream)
+        else:
+            st = _lib.attn_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                       lse.data_ptr(), B, H, Sq, Skv, D, q.stride()[:3], k.stride()[:3],
+                                       v.stride()[:3], out.stride()[:3], scale, causal, dt,
+                                       stream.cuda_stream)
     _lib.check(st)
     return out, lse

@@ -16,8 +16,8 @@ STATUS = {
     5: "ATTN_ERR_MISALIGNED", 6: "ATTN_ERR_BAD_SCALE", 7: "ATTN_ERR_ALIASING",
     8: "ATTN_ERR_UNSUPPORTED_DEVICE", 9: "ATTN_ERR_LAUNCH", 10: "ATTN_ERR_BAD_ARGUMENT",
 }
-EXPORTS = ("attn_fwd", "attn_fwd_plan", "attn_fwd_workgroup_tile", "attn_status_string",
-           "attn_last_error", "attn_abi_version")
+EXPORTS = ("attn_fwd", "attn_fwd_strided", "attn_fwd_plan", "attn_fwd_workgroup_tile",
+           "attn_status_string", "attn_last_error", "attn_abi_version")
 
 
 class AttnError(RuntimeError):
@@ -52,6 +52,10 @@ def load():
     i64, vp, ci, cf = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, cf, ci, ci, vp]
     lib.attn_fwd.restype = ci
+    p64 = ctypes.POINTER(i64)
+    lib.attn_fwd_strided.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, p64, p64, p64, p64,
+                                     cf, ci, ci, vp]
+    lib.attn_fwd_strided.restype = ci
     lib.attn_fwd_plan.argtypes = [i64, i64, i64, i64, ci, ci, ctypes.POINTER(Plan)]
     lib.attn_fwd_plan.restype = ci
     lib.attn_fwd_workgroup_tile.argtypes = [i64, i64, i64, i64, ci, ci, i64,
@@ -87,6 +91,25 @@ def attn_fwd(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, S: int, D
     """Raw call: device pointers as ints; returns the status code."""
     return load().attn_fwd(q, k, v, o, lse, B, H, S, D, float(scale), int(bool(causal)),
                            int(dtype), stream)
+
+
+def _strides(st):
+    if st is None:
+        return None
+    st = tuple(int(x) for x in st)
+    if len(st) != 3:
+        raise ValueError("strides are (batch, head, row) in elements")
+    return (ctypes.c_int64 * 3)(*st)
+
+
+def attn_fwd_strided(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Sq: int, Skv: int,
+                     D: int, q_strides, k_strides, v_strides, o_strides, scale: float, causal: bool,
+                     dtype: int, stream: int) -> int:
+    """Raw call: device pointers as ints, strides as (batch, head, row) element
+    triples or None (contiguous); returns the status code."""
+    return load().attn_fwd_strided(q, k, v, o, lse, B, H, Sq, Skv, D, _strides(q_strides),
+                                   _strides(k_strides), _strides(v_strides), _strides(o_strides),
+                                   float(scale), int(bool(causal)), int(dtype), stream)
 
 
 def attn_fwd_plan(B: int, H: int, S: int, D: int, causal: bool, dtype: int) -> dict:

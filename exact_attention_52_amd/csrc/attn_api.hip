@@ -7,6 +7,7 @@
 // per (query tile, batch*head), ceil(S / block_m) query tiles.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdarg>
 #include <cfloat>
@@ -135,31 +136,137 @@ int check_device() {
 }
 
 template <class C, bool CAUSAL, int DT>
-int launch(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-           int64_t S, float c, hipStream_t stream) {
-  const int64_t nq = (S + C::BM - 1) / C::BM;
-  const int64_t G = nq * B * H;
+int launch(const attn::Problem& pr, hipStream_t stream) {
   if constexpr (C::PINGPONG)
-    hipLaunchKernelGGL((attn::attn_fwd_pingpong_kernel<C, CAUSAL, DT>), dim3((unsigned)G), dim3(C::NT), 0,
-                       stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
-                       (int)S, (int)nq, G, c);
+    hipLaunchKernelGGL((attn::attn_fwd_pingpong_kernel<C, CAUSAL, DT>), dim3((unsigned)pr.G), dim3(C::NT), 0,
+                       stream, pr);
   else
-    hipLaunchKernelGGL((attn::attn_fwd_kernel<C, CAUSAL, DT>), dim3((unsigned)G), dim3(C::NT), 0, stream,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, (int)S,
-                       (int)nq, G, c);
+    hipLaunchKernelGGL((attn::attn_fwd_kernel<C, CAUSAL, DT>), dim3((unsigned)pr.G), dim3(C::NT), 0, stream, pr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(ATTN_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 
 template <class C>
-int dispatch(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-             int64_t S, float c, bool causal, int dtype, hipStream_t st) {
+int dispatch(const attn::Problem& pr, bool causal, int dtype, hipStream_t st) {
   if (dtype == ATTN_F16)
-    return causal ? launch<C, true, attn::DT_F16>(q, k, v, o, lse, B, H, S, c, st)
-                  : launch<C, false, attn::DT_F16>(q, k, v, o, lse, B, H, S, c, st);
-  return causal ? launch<C, true, attn::DT_BF16>(q, k, v, o, lse, B, H, S, c, st)
-                : launch<C, false, attn::DT_BF16>(q, k, v, o, lse, B, H, S, c, st);
+    return causal ? launch<C, true, attn::DT_F16>(pr, st) : launch<C, false, attn::DT_F16>(pr, st);
+  return causal ? launch<C, true, attn::DT_BF16>(pr, st) : launch<C, false, attn::DT_BF16>(pr, st);
+}
+
+// One 4-D tensor [B,H,rows,D] with the last dimension contiguous.
+struct View {
+  const void* p;
+  int64_t sb, sh, ss;  // elements
+  int64_t rows;
+  const char* name;
+};
+
+// Strides of dimensions of size <= 1 never address anything: normalise them
+// so that the checks and the kernel see the contiguous value.
+void normalise(View& t, int64_t B, int64_t H, int64_t D) {
+  if (t.rows <= 1) t.ss = D;
+  if (H <= 1) t.sh = 0;
+  if (B <= 1) t.sb = 0;
+}
+
+int check_view(const View& t, int64_t B, int64_t H, int64_t D) {
+  if (t.sb < 0 || t.sh < 0 || t.ss < 0)
+    return fail(ATTN_ERR_BAD_ARGUMENT, "%s strides must be >= 0", t.name);
+  if (t.ss < D)
+    return fail(ATTN_ERR_BAD_ARGUMENT, "%s row stride %lld is shorter than a row (%lld)", t.name, (long long)t.ss,
+                (long long)D);
+  if ((t.sb | t.sh | t.ss) & 7)
+    return fail(ATTN_ERR_MISALIGNED, "%s strides must be multiples of 8 elements (16 bytes)", t.name);
+  // one head's rows are addressed with 32-bit byte offsets
+  const int64_t lim = (int64_t)1 << 30;
+  if (t.ss > lim || (t.rows > 0 && (t.rows - 1) > (lim - D) / t.ss))
+    return fail(ATTN_ERR_BAD_SHAPE, "%s: one head spans more than 2 GiB", t.name);
+  // the whole tensor within int64
+  const int64_t big = (int64_t)1 << 60;
+  if ((B > 0 && t.sb > big / B) || (H > 0 && t.sh > big / H))
+    return fail(ATTN_ERR_BAD_SHAPE, "%s strides overflow", t.name);
+  return ATTN_OK;
+}
+
+// Bytes from the tensor's base pointer to one past its last element.
+int64_t extent_bytes(const View& t, int64_t B, int64_t H, int64_t D) {
+  if (B == 0 || H == 0 || t.rows == 0) return 0;
+  return 2 * ((B - 1) * t.sb + (H - 1) * t.sh + (t.rows - 1) * t.ss + D);
+}
+
+// The output must not address one element twice: with the dimensions of
+// size > 1 sorted by stride, each stride must step over the whole previous
+// dimension.
+bool self_disjoint(const View& t, int64_t B, int64_t H, int64_t D) {
+  int64_t dims[4][2] = {{D, 1}, {t.rows, t.ss}, {H, t.sh}, {B, t.sb}};
+  int n = 0;
+  int64_t d[4][2];
+  for (auto& x : dims)
+    if (x[0] > 1) d[n][0] = x[0], d[n][1] = x[1], ++n;
+  for (int i = 1; i < n; ++i)
+    for (int j = i; j > 0 && d[j][1] < d[j - 1][1]; --j) std::swap(d[j], d[j - 1]);
+  for (int i = 1; i < n; ++i)
+    if (d[i][1] < d[i - 1][1] * d[i - 1][0]) return false;
+  return true;
+}
+
+int run(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t Sq,
+        int64_t Skv, int64_t D, View vq, View vk, View vv, View vo, float scale, int causal, int dtype,
+        void* stream) {
+  if (B < 0 || H < 0 || Sq < 0 || Skv < 0)
+    return fail(ATTN_ERR_BAD_SHAPE, "B, H, Sq and Skv must be >= 0 (got B=%lld H=%lld Sq=%lld Skv=%lld)",
+                (long long)B, (long long)H, (long long)Sq, (long long)Skv);
+  int st = check_sizes(B, H, Sq > Skv ? Sq : Skv, D, dtype);
+  if (st != ATTN_OK) return st;
+  if (!(std::isfinite(scale) && scale >= 0.f))
+    return fail(ATTN_ERR_BAD_SCALE, "scale must be finite and >= 0 (got %g)", (double)scale);
+  if (B == 0 || H == 0 || Sq == 0) return ok();  // empty: nothing to compute
+  // with no keys nothing is read from k or v, which may then be NULL
+  if (!q || !o || !lse || (Skv > 0 && (!k || !v)))
+    return fail(ATTN_ERR_NULL_PTR, "q, k, v, o and lse must be non-NULL");
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15)
+    return fail(ATTN_ERR_MISALIGNED, "q, k, v and o must be 16-byte aligned");
+  if ((uintptr_t)lse & 3) return fail(ATTN_ERR_MISALIGNED, "lse must be 4-byte aligned");
+  for (View* t : {&vq, &vk, &vv, &vo}) {
+    normalise(*t, B, H, D);
+    st = check_view(*t, B, H, D);
+    if (st != ATTN_OK) return st;
+  }
+  if (!self_disjoint(vo, B, H, D)) return fail(ATTN_ERR_ALIASING, "o strides make rows overlap");
+  const int64_t nq_ = extent_bytes(vq, B, H, D), nk = extent_bytes(vk, B, H, D), nv = extent_bytes(vv, B, H, D);
+  const int64_t no = extent_bytes(vo, B, H, D), nl = B * H * Sq * 4;
+  if (overlaps(o, no, q, nq_) || overlaps(o, no, k, nk) || overlaps(o, no, v, nv) || overlaps(o, no, lse, nl))
+    return fail(ATTN_ERR_ALIASING, "o overlaps q, k, v or lse");
+  if (overlaps(lse, nl, q, nq_) || overlaps(lse, nl, k, nk) || overlaps(lse, nl, v, nv))
+    return fail(ATTN_ERR_ALIASING, "lse overlaps q, k or v");
+  attn_fwd_plan_t plan;
+  st = plan_for(B, H, Sq, D, &plan);
+  if (st != ATTN_OK) return st;
+  st = check_device();
+  if (st != ATTN_OK) return st;
+
+  attn::Problem pr;
+  pr.q = (const uint16_t*)q, pr.k = (const uint16_t*)k, pr.v = (const uint16_t*)v;
+  pr.o = (uint16_t*)o, pr.lse = lse;
+  pr.q_sb = vq.sb, pr.q_sh = vq.sh, pr.k_sb = vk.sb, pr.k_sh = vk.sh;
+  pr.v_sb = vv.sb, pr.v_sh = vv.sh, pr.o_sb = vo.sb, pr.o_sh = vo.sh;
+  pr.q_ss = (int)vq.ss, pr.k_ss = (int)vk.ss, pr.v_ss = (int)vv.ss, pr.o_ss = (int)vo.ss;
+  pr.Sq = (int)Sq, pr.Skv = (int)Skv, pr.H = (int)H, pr.nq = (int)plan.num_q_tiles;
+  pr.G = plan.num_workgroups;
+  // scale * log2(e), kept >= FLT_MIN: a masked score (-inf) times c must stay
+  // -inf, never NaN, and for scale == 0 every kept score times FLT_MIN is far
+  // below one ulp of the row max, so the softmax is exactly uniform.
+  float c = (float)((double)scale * 1.4426950408889634074);
+  if (c < FLT_MIN) c = FLT_MIN;
+  pr.c = c;
+  hipStream_t hs = (hipStream_t)stream;
+  const bool cz = causal != 0;
+  switch (D) {
+    case 64: return dispatch<Cfg64>(pr, cz, dtype, hs);
+    case 128: return dispatch<Cfg128>(pr, cz, dtype, hs);
+    default: return dispatch<Cfg256>(pr, cz, dtype, hs);
+  }
 }
 
 }  // namespace
@@ -168,39 +275,34 @@ extern "C" {
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
              int64_t S, int64_t D, float scale, int causal, int dtype, void* stream) {
-  int st = check_sizes(B, H, S, D, dtype);
+  // contiguous [B,H,S,D]; the sizes are checked before any stride is formed
+  const int st = check_sizes(B, H, S, D, dtype);
   if (st != ATTN_OK) return st;
-  if (!(std::isfinite(scale) && scale >= 0.f))
-    return fail(ATTN_ERR_BAD_SCALE, "scale must be finite and >= 0 (got %g)", (double)scale);
-  if (B == 0 || H == 0 || S == 0) return ok();  // empty: nothing to compute
-  if (!q || !k || !v || !o || !lse) return fail(ATTN_ERR_NULL_PTR, "q, k, v, o and lse must be non-NULL");
-  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15)
-    return fail(ATTN_ERR_MISALIGNED, "q, k, v and o must be 16-byte aligned");
-  if ((uintptr_t)lse & 3) return fail(ATTN_ERR_MISALIGNED, "lse must be 4-byte aligned");
-  const int64_t nbytes = B * H * S * D * 2, lbytes = B * H * S * 4;
-  if (overlaps(o, nbytes, q, nbytes) || overlaps(o, nbytes, k, nbytes) || overlaps(o, nbytes, v, nbytes) ||
-      overlaps(o, nbytes, lse, lbytes))
-    return fail(ATTN_ERR_ALIASING, "o overlaps q, k, v or lse");
-  if (overlaps(lse, lbytes, q, nbytes) || overlaps(lse, lbytes, k, nbytes) || overlaps(lse, lbytes, v, nbytes))
-    return fail(ATTN_ERR_ALIASING, "lse overlaps q, k or v");
-  attn_fwd_plan_t plan;
-  st = plan_for(B, H, S, D, &plan);
-  if (st != ATTN_OK) return st;
-  st = check_device();
-  if (st != ATTN_OK) return st;
+  const int64_t sh = S * D, sb = H * S * D;
+  const View c4 = {nullptr, sb, sh, D, S, "q"};
+  View vq = c4, vk = c4, vv = c4, vo = c4;
+  vk.name = "k", vv.name = "v", vo.name = "o";
+  return run(q, k, v, o, lse, B, H, S, S, D, vq, vk, vv, vo, scale, causal, dtype, stream);
+}
 
-  // scale * log2(e), kept >= FLT_MIN: a masked score (-inf) times c must stay
-  // -inf, never NaN, and for scale == 0 every kept score times FLT_MIN is far
-  // below one ulp of the row max, so the softmax is exactly uniform.
-  float c = (float)((double)scale * 1.4426950408889634074);
-  if (c < FLT_MIN) c = FLT_MIN;
-  hipStream_t hs = (hipStream_t)stream;
-  const bool cz = causal != 0;
-  switch (D) {
-    case 64: return dispatch<Cfg64>(q, k, v, o, lse, B, H, S, c, cz, dtype, hs);
-    case 128: return dispatch<Cfg128>(q, k, v, o, lse, B, H, S, c, cz, dtype, hs);
-    default: return dispatch<Cfg256>(q, k, v, o, lse, B, H, S, c, cz, dtype, hs);
-  }
+int attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                     int64_t Sq, int64_t Skv, int64_t D, const int64_t* q_strides, const int64_t* k_strides,
+                     const int64_t* v_strides, const int64_t* o_strides, float scale, int causal, int dtype,
+                     void* stream) {
+  // NULL strides mean contiguous [B,H,rows,D]; the sizes are checked before
+  // any stride is formed
+  if (Sq < 0 || Skv < 0)
+    return fail(ATTN_ERR_BAD_SHAPE, "Sq and Skv must be >= 0 (got Sq=%lld Skv=%lld)", (long long)Sq,
+                (long long)Skv);
+  const int st0 = check_sizes(B, H, Sq > Skv ? Sq : Skv, D, dtype);
+  if (st0 != ATTN_OK) return st0;
+  auto view = [&](const int64_t* st, int64_t rows, const char* name) {
+    View t = {nullptr, H * rows * D, rows * D, D, rows, name};
+    if (st) t.sb = st[0], t.sh = st[1], t.ss = st[2];
+    return t;
+  };
+  return run(q, k, v, o, lse, B, H, Sq, Skv, D, view(q_strides, Sq, "q"), view(k_strides, Skv, "k"),
+             view(v_strides, Skv, "v"), view(o_strides, Sq, "o"), scale, causal, dtype, stream);
 }
 
 int attn_fwd_plan(int64_t B, int64_t H, int64_t S, int64_t D, int causal, int dtype, attn_fwd_plan_t* out) {

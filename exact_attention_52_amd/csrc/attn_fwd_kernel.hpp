@@ -296,6 +296,56 @@ __host__ __device__ inline void workgroup_tile(int64_t g, int64_t G, int64_t nq,
 }
 
 // ---------------------------------------------------------------------------
+// The problem in global memory
+// ---------------------------------------------------------------------------
+// Q, O [B,H,Sq,D] and K, V [B,H,Skv,D] of 16-bit elements, each row of D
+// elements contiguous and addressed by batch, head and row strides (in
+// elements); LSE [B,H,Sq] contiguous fp32.  Causal keeps key j for query i iff
+// j <= i + (Skv - Sq): the last query sees the last key.
+struct Problem {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int64_t q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;  // batch, head strides
+  int q_ss, k_ss, v_ss, o_ss;                              // row strides (>= D)
+  int Sq, Skv, H, nq;                                      // nq query tiles per head
+  int64_t G;                                               // workgroups
+  float c;                                                 // scale * log2(e), > 0
+};
+
+// One (b, h) of the problem.
+struct HeadView {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int q_ss, k_ss, v_ss, o_ss;
+  int Sq, Skv, koff;  // koff = Skv - Sq
+};
+
+__device__ __forceinline__ HeadView head_view(const Problem& p, int64_t bh) {
+  const int64_t b = bh / p.H, h = bh % p.H;
+  HeadView hv;
+  hv.q = p.q + b * p.q_sb + h * p.q_sh;
+  hv.k = p.k + b * p.k_sb + h * p.k_sh;
+  hv.v = p.v + b * p.v_sb + h * p.v_sh;
+  hv.o = p.o + b * p.o_sb + h * p.o_sh;
+  hv.lse = p.lse + bh * p.Sq;
+  hv.q_ss = p.q_ss, hv.k_ss = p.k_ss, hv.v_ss = p.v_ss, hv.o_ss = p.o_ss;
+  hv.Sq = p.Sq, hv.Skv = p.Skv, hv.koff = p.Skv - p.Sq;
+  return hv;
+}
+
+// Bytes spanned by n rows of D 16-bit elements at row stride ss (0 if none):
+// a buffer descriptor of this size returns 0 for every row >= n.
+__device__ __forceinline__ uint32_t rows_bytes(int n, int ss, int D) {
+  return n > 0 ? (uint32_t)((n - 1) * ss + D) * 2u : 0u;
+}
+
+// ---------------------------------------------------------------------------
 // Per-wave state and the three steps of one key tile
 // ---------------------------------------------------------------------------
 // A wave owns 32 query rows (one per lane column) and the kw-th slice of
@@ -321,11 +371,10 @@ struct Wave {
   float l_run;       // partial running sum of the fp32 P over this lane's keys
   float lr4[4];      // the same sum over the P as rounded to 16 bits, in
                      // four chains (one per word of a packed P register)
-  int lane, half, wq_first, wq_last, my_q, kbase, S, k_lane, v_lane;
+  int lane, half, wq_first, wq_last, my_q, kbase, Sq, Skv, koff, k_lane, v_lane;
   float c;
 
-  __device__ __forceinline__ void init(const uint16_t* q, int64_t head, int q_first, int kbase_, int S_,
-                                       float c_) {
+  __device__ __forceinline__ void init(const HeadView& hv, int q_first, int kbase_, float c_) {
     lane = threadIdx.x & 63;
     const int col = lane & 31;
     half = lane >> 5;
@@ -333,13 +382,15 @@ struct Wave {
     wq_last = q_first + 31;
     my_q = q_first + col;
     kbase = kbase_;
-    S = S_;
+    Sq = hv.Sq;
+    Skv = hv.Skv;
+    koff = hv.koff;
     c = c_;
     // lane parts of the operand read addresses (the rest are immediates)
     k_lane = C::k_off(kbase + col) + half * 16;
     v_lane = C::v_off(kbase + 4 * half + ((lane & 15) >> 2)) + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(q + head, (uint32_t)S * D * 2);
-    const uint32_t off = (uint32_t)(my_q * D + half * 8) * 2;  // rows >= S read 0
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(hv.q, rows_bytes(Sq, hv.q_ss, D));
+    const uint32_t off = (uint32_t)(my_q * hv.q_ss + half * 8) * 2;  // rows >= Sq read 0
 #pragma unroll
     for (int kc = 0; kc < DK; ++kc) qf[kc] = load16(qr, off + kc * 32);
 #pragma unroll
@@ -361,7 +412,7 @@ struct Wave {
   // does this wave have any unmasked key in tile j?
   __device__ __forceinline__ bool active(int j) const {
     const int kv0 = j * BN + kbase;
-    return kv0 < S && (!CAUSAL || kv0 <= wq_last) && wq_first < S;
+    return kv0 < Skv && (!CAUSAL || kv0 <= wq_last + koff) && wq_first < Sq;
   }
 
   __device__ __forceinline__ void qk(const uint8_t* kt) {
@@ -380,12 +431,12 @@ struct Wave {
   __device__ __forceinline__ void softmax(int j) {
     const int kv0 = j * BN + kbase;
     // mask keys past the end or after the query (diagonal / ragged tiles)
-    const bool need_mask = (kv0 + C::KSUB > S) || (CAUSAL && kv0 + C::KSUB - 1 > wq_first);
+    const bool need_mask = (kv0 + C::KSUB > Skv) || (CAUSAL && kv0 + C::KSUB - 1 > wq_first + koff);
     if (need_mask) {
       // score i of block kb is key kv0 + 4*half + off(kb, i); it is kept iff
-      // key <= min(my_q, S-1) (causal) or key <= S-1: one compare of a
-      // constant offset against a per-lane limit
-      const int last = CAUSAL ? (my_q < S - 1 ? my_q : S - 1) : S - 1;
+      // key <= min(my_q + koff, Skv-1) (causal) or key <= Skv-1: one compare
+      // of a constant offset against a per-lane limit
+      const int last = CAUSAL ? (my_q + koff < Skv - 1 ? my_q + koff : Skv - 1) : Skv - 1;
       const int lim = last - kv0 - 4 * half;
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb) {
@@ -527,12 +578,13 @@ struct Wave {
   }
 
   // O = O_acc / l (RNE to 16 bits), LSE = (m + log2 l) ln 2.
-  __device__ __forceinline__ void epilogue(uint16_t* o, float* lse, int64_t head, int64_t bh) {
+  // A row with no key (causal, Sq > Skv) has l = 0: O = 0 and LSE = -inf.
+  __device__ __forceinline__ void epilogue(const HeadView& hv) {
     const float l_tot = sum_halves(l_run);
     const float lr_tot = sum_halves(lr_sum());
-    if (my_q < S) {
-      const float inv = 1.0f / lr_tot;
-      uint16_t* orow = o + head + (int64_t)my_q * D;
+    if (my_q < Sq) {
+      const float inv = lr_tot > 0.f ? 1.0f / lr_tot : 0.f;
+      uint16_t* orow = hv.o + (int64_t)my_q * hv.o_ss;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -545,31 +597,40 @@ struct Wave {
         }
       }
       if (half == 0)
-        lse[bh * (int64_t)S + my_q] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f;
+        hv.lse[my_q] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f;
     }
   }
 };
 
-// HBM -> LDS copy of this wave's share of the lines of one K or V tile.
-// Lane i of line n carries row (first row of line n) + step*(i / (D/8)) and
-// 16-byte chunk i % (D/8); keys >= S fall outside the buffer and read as 0.
-template <class C, bool IS_K, int LOADERS = C::NW>
-__device__ __forceinline__ void fetch_tile(const uint16_t* src_head, int S, int kv0, uint8_t* tile, int wave,
-                                           int lane) {
-  constexpr int D = C::D;
-  constexpr int PER_WAVE = C::LINES / LOADERS;
-  static_assert(C::LINES % LOADERS == 0, "load lines must split evenly over the loading waves");
-  const __amdgpu_buffer_rsrc_t r = make_rsrc(src_head + (int64_t)kv0 * D, (uint32_t)(S - kv0) * D * 2);
-  const int lrow = lane / (D / 8), lchunk = lane % (D / 8);
-#pragma unroll
-  for (int i = 0; i < PER_WAVE; ++i) {
-    const int n = wave * PER_WAVE + i;
-    if constexpr (IS_K)
-      load16_lds(r, tile + n * C::K_LINE, (C::k_line_row(n) + 16 * lrow) * C::ROW_BYTES + lchunk * 16);
-    else
-      load16_lds(r, tile + n * C::V_LINE, (C::v_line_row(n) + 4 * lrow) * C::ROW_BYTES + lchunk * 16);
+// HBM -> LDS copies of K or V tiles of one head.  Line n of a tile holds rows
+// (first row of line n) + STEP*m (STEP 16 for K, 4 for V); lane i of a copy
+// instruction carries row STEP*(i / (D/8)) of the line and 16-byte chunk
+// i % (D/8).  Rows at or past `rows` (the key length) fall outside the buffer
+// descriptor and read as 0, as does a whole tile the caller marks invalid.
+template <class C, bool IS_K>
+struct TileCopier {
+  static constexpr int D = C::D, STEP = IS_K ? 16 : 4, LINE = IS_K ? C::K_LINE : C::V_LINE;
+  const uint16_t* src;  // the head's first row
+  int ss;               // row stride (elements)
+  int rows;             // key length
+  uint32_t lane_off;    // this lane's part of a line's source offset (bytes)
+
+  __device__ __forceinline__ void init(const uint16_t* src_, int ss_, int rows_, int lane) {
+    src = src_;
+    ss = ss_;
+    rows = rows_;
+    lane_off = (uint32_t)(STEP * (lane / (D / 8)) * ss) * 2u + (uint32_t)(lane % (D / 8)) * 16u;
   }
-}
+  // descriptor over the rows of the tile that starts at key kv0
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile(int kv0, bool valid) const {
+    return make_rsrc(src + (int64_t)kv0 * ss, (valid && kv0 < rows) ? rows_bytes(rows - kv0, ss, D) : 0u);
+  }
+  // the copy instruction of line ln of that tile into the LDS tile at dst
+  __device__ __forceinline__ void line(__amdgpu_buffer_rsrc_t r, uint8_t* dst, int ln) const {
+    const int row0 = IS_K ? C::k_line_row(ln) : C::v_line_row(ln);
+    load16_lds(r, dst + ln * LINE, lane_off, (uint32_t)(row0 * ss) * 2u);
+  }
+};
 
 // Workgroup barrier that does not drain outstanding memory operations (the
 // HBM -> LDS prefetch stays in flight).  The memory clobber keeps LDS accesses
@@ -610,10 +671,7 @@ __device__ __forceinline__ void wait_loads_but() {
 // Supports key-split waves (KW > 1), merged at the end through LDS.
 // ---------------------------------------------------------------------------
 template <class C, bool CAUSAL, int DT>
-__global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
-    int S, int nq, int64_t G, float c /* scale * log2(e), > 0 */) {
+__global__ __launch_bounds__(C::NT) void attn_fwd_kernel(const Problem p) {
   constexpr int D = C::D, BN = C::BN, BM = C::BM, DB = C::DB;
   constexpr int LPW = C::LINES / C::NW;              // copy lines per wave per operand
   constexpr int NQK = C::DK * C::NB, NPV = 2 * C::NB * DB;  // MFMAs of qk, pv
@@ -633,40 +691,36 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
   const int kw = wave / C::QW;
 
   int64_t tile64, bh64;
-  workgroup_tile(blockIdx.x, G, nq, CAUSAL, &tile64, &bh64);
+  workgroup_tile(blockIdx.x, p.G, p.nq, CAUSAL, &tile64, &bh64);
   const int q0 = (int)tile64 * BM;
-  const int64_t head = bh64 * (int64_t)S * D;
-  const uint16_t* kh = k + head;
-  const uint16_t* vh = v + head;
+  const HeadView hv = head_view(p, bh64);
 
   Wave<C, CAUSAL, DT> w;
-  w.init(q, head, q0 + qw * 32, kw * C::KSUB, S, c);
+  w.init(hv, q0 + qw * 32, kw * C::KSUB, p.c);
 
-  const int q_end = (q0 + BM < S) ? q0 + BM : S;
-  const int n = CAUSAL ? (q_end + BN - 1) / BN : (S + BN - 1) / BN;  // >= 1
+  // key tiles this workgroup needs (none when causal leaves its rows no key)
+  const int q_end = (q0 + BM < hv.Sq) ? q0 + BM : hv.Sq;
+  const int kv_end = CAUSAL ? (q_end + hv.koff < 0 ? 0 : (q_end + hv.koff < hv.Skv ? q_end + hv.koff : hv.Skv))
+                            : hv.Skv;
+  const int n = (kv_end + BN - 1) / BN;
+  if (n == 0) {  // uniform over the workgroup
+    w.epilogue(hv);
+    return;
+  }
 
-  // lane part of a copy: row step*(lane / (D/8)) of the line, 16-byte chunk
-  // lane % (D/8); a tile past the last one this workgroup needs reads through
-  // an empty descriptor (no fetch; it fills a stage no later step reads)
-  const uint32_t k_lane_src = (16 * (lane / (D / 8))) * C::ROW_BYTES + (lane % (D / 8)) * 16;
-  const uint32_t v_lane_src = (4 * (lane / (D / 8))) * C::ROW_BYTES + (lane % (D / 8)) * 16;
-  auto tile_rsrc = [&](const uint16_t* src, int t) __attribute__((always_inline)) {
-    const int kv0 = t * BN;
-    return make_rsrc(src + (int64_t)kv0 * D, (t < n && kv0 < S) ? (uint32_t)(S - kv0) * D * 2 : 0u);
-  };
+  // a tile past the last one this workgroup needs reads through an empty
+  // descriptor (no fetch; it fills a stage no later step reads)
+  TileCopier<C, true> kcp;
+  TileCopier<C, false> vcp;
+  kcp.init(hv.k, hv.k_ss, hv.Skv, lane);
+  vcp.init(hv.v, hv.v_ss, hv.Skv, lane);
   auto k_copier = [&](int t, uint8_t* dst) __attribute__((always_inline)) {
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(kh, t);
-    return [=](int i) __attribute__((always_inline)) {
-      const int ln = wave * LPW + i;
-      load16_lds(r, dst + ln * C::K_LINE, k_lane_src, C::k_line_row(ln) * C::ROW_BYTES);
-    };
+    const __amdgpu_buffer_rsrc_t r = kcp.tile(t * BN, t < n);
+    return [=](int i) __attribute__((always_inline)) { kcp.line(r, dst, wave * LPW + i); };
   };
   auto v_copier = [&](int t, uint8_t* dst) __attribute__((always_inline)) {
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(vh, t);
-    return [=](int i) __attribute__((always_inline)) {
-      const int ln = wave * LPW + i;
-      load16_lds(r, dst + ln * C::V_LINE, v_lane_src, C::v_line_row(ln) * C::ROW_BYTES);
-    };
+    const __amdgpu_buffer_rsrc_t r = vcp.tile(t * BN, t < n);
+    return [=](int i) __attribute__((always_inline)) { vcp.line(r, dst, wave * LPW + i); };
   };
 
   if constexpr (C::STAGGER) {
@@ -776,7 +830,7 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
     }
   }
 
-  w.epilogue(o, lse, head, bh64);
+  w.epilogue(hv);
 }
 
 // ---------------------------------------------------------------------------
@@ -804,12 +858,9 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(
 #define ATTN_LSTRIDE 3
 #endif
 template <class C, bool CAUSAL, int DT>
-__global__ __launch_bounds__(C::NT) void attn_fwd_pingpong_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
-    int S, int nq, int64_t G, float c /* scale * log2(e), > 0 */) {
+__global__ __launch_bounds__(C::NT) void attn_fwd_pingpong_kernel(const Problem p) {
   static_assert(C::NW == 8 && C::KW == 1, "ping-pong needs 8 query waves");
-  constexpr int D = C::D, BN = C::BN, BM = C::BM;
+  constexpr int BN = C::BN, BM = C::BM;
   constexpr int LPW = C::LINES / 4;  // copy instructions per loading wave and operand
   constexpr int ST = 3 * (C::K_TILE + C::V_TILE) <= 160 * 1024 ? 3 : 2;  // LDS stages
   static_assert(2 * (C::K_TILE + C::V_TILE) <= 160 * 1024, "two stages must fit in LDS");
@@ -827,26 +878,27 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_pingpong_kernel(
   const int group = wave >> 2;
 
   int64_t tile64, bh64;
-  workgroup_tile(blockIdx.x, G, nq, CAUSAL, &tile64, &bh64);
+  workgroup_tile(blockIdx.x, p.G, p.nq, CAUSAL, &tile64, &bh64);
   const int q0 = (int)tile64 * BM;
-  const int64_t head = bh64 * (int64_t)S * D;
-  const uint16_t* kh = k + head;
-  const uint16_t* vh = v + head;
+  const HeadView hv = head_view(p, bh64);
 
   Wave<C, CAUSAL, DT> w;
-  w.init(q, head, q0 + wave * 32, 0, S, c);
+  w.init(hv, q0 + wave * 32, 0, p.c);
 
-  const int q_end = (q0 + BM < S) ? q0 + BM : S;
-  const int n = CAUSAL ? (q_end + BN - 1) / BN : (S + BN - 1) / BN;  // >= 1
+  // key tiles this workgroup needs (none when causal leaves its rows no key)
+  const int q_end = (q0 + BM < hv.Sq) ? q0 + BM : hv.Sq;
+  const int kv_end = CAUSAL ? (q_end + hv.koff < 0 ? 0 : (q_end + hv.koff < hv.Skv ? q_end + hv.koff : hv.Skv))
+                            : hv.Skv;
+  const int n = (kv_end + BN - 1) / BN;
+  if (n == 0) {  // uniform over the workgroup
+    w.epilogue(hv);
+    return;
+  }
 
-  // lane part of a copy: row step*(lane / (D/8)) of the line, 16-byte chunk
-  // lane % (D/8)
-  const uint32_t k_lane_src = (16 * (lane / (D / 8))) * C::ROW_BYTES + (lane % (D / 8)) * 16;
-  const uint32_t v_lane_src = (4 * (lane / (D / 8))) * C::ROW_BYTES + (lane % (D / 8)) * 16;
-  // descriptor over the rows of the key tile starting at kv0 (empty past S)
-  auto tile_rsrc = [&](const uint16_t* src, int kv0) __attribute__((always_inline)) {
-    return make_rsrc(src + (int64_t)kv0 * D, kv0 < S ? (uint32_t)(S - kv0) * D * 2 : 0u);
-  };
+  TileCopier<C, true> kcp;
+  TileCopier<C, false> vcp;
+  kcp.init(hv.k, hv.k_ss, hv.Skv, lane);
+  vcp.init(hv.v, hv.v_ss, hv.Skv, lane);
 
   // One iteration of this wave.  PV, QK select the halves of the MFMA block;
   // group 0 (COPIES) also copies the next tiles.  kt_j holds K_j, vt_prev
@@ -859,16 +911,13 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_pingpong_kernel(
     constexpr bool PV = decltype(pv)::value, QK = decltype(qk)::value;
     constexpr bool LAST = !QK;  // j = n: pv(n-1) only
     if constexpr (COPIES && !LAST) {
-      const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kh, (j + ST - 1) * BN);
-      const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vh, (j + ST - 2) * BN);
+      const __amdgpu_buffer_rsrc_t rk = kcp.tile((j + ST - 1) * BN, j + ST - 1 < n);
+      const __amdgpu_buffer_rsrc_t rv = vcp.tile((j + ST - 2) * BN, j + ST - 2 < n);
       auto copy = [&](int i) __attribute__((always_inline)) {
-        if (i < LPW) {
-          const int ln = wave * LPW + i;
-          load16_lds(rk, kt_ld + ln * C::K_LINE, k_lane_src, C::k_line_row(ln) * C::ROW_BYTES);
-        } else {
-          const int ln = wave * LPW + i - LPW;
-          load16_lds(rv, vt_ld + ln * C::V_LINE, v_lane_src, C::v_line_row(ln) * C::ROW_BYTES);
-        }
+        if (i < LPW)
+          kcp.line(rk, kt_ld, wave * LPW + i);
+        else
+          vcp.line(rv, vt_ld, wave * LPW + i - LPW);
       };
       constexpr int LS = (PV && QK) ? ATTN_LSTRIDE : 2;
       w.template mfma_ops<PV, QK, 2 * LPW, LS>(vt_prev, kt_j, copy);
@@ -910,10 +959,14 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_pingpong_kernel(
   };
 
   if (group == 0) {
-    fetch_tile<C, true, 4>(kh, S, 0, kt0, wave, lane);
+    const __amdgpu_buffer_rsrc_t rk0 = kcp.tile(0, true);
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) kcp.line(rk0, kt0, wave * LPW + i);
     if constexpr (ST == 3) {
-      if (n > 1) fetch_tile<C, true, 4>(kh, S, BN, kt1, wave, lane);
-      fetch_tile<C, false, 4>(vh, S, 0, vt0, wave, lane);
+      const __amdgpu_buffer_rsrc_t rk1 = kcp.tile(BN, n > 1);
+      const __amdgpu_buffer_rsrc_t rv0 = vcp.tile(0, true);
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) kcp.line(rk1, kt1, wave * LPW + i), vcp.line(rv0, vt0, wave * LPW + i);
     }
   }
   wait_loads();
@@ -925,7 +978,7 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_pingpong_kernel(
     loop(std::false_type{});
   }
 
-  w.epilogue(o, lse, head, bh64);
+  w.epilogue(hv);
 }
 
 }  // namespace attn

@@ -14,7 +14,8 @@
  *     of 16-bit elements (fp16 or bf16, chosen by `dtype`); LSE is [B, H, S]
  *     of fp32.  The caller owns every buffer; the library allocates no device
  *     memory and keeps no pointer after a call returns.
- *   - Causal keeps key j for query i iff j <= i (Sq == Skv == S).
+ *   - Causal keeps key j for query i iff j <= i (attn_fwd: Sq == Skv == S;
+ *     attn_fwd_strided aligns the last query with the last key).
  *   - LSE is the natural logarithm of sum_j exp(scale * q_i . k_j) over the
  *     kept keys.
  *   - Status codes are returned, never thrown; attn_last_error() gives a
@@ -85,6 +86,40 @@ typedef enum {
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int64_t B, int64_t H, int64_t S, int64_t D, float scale,
              int causal, int dtype, void* stream);
+
+/*
+ * attn_fwd_strided -- attn_fwd for queries and keys of different lengths and
+ * for strided tensors.
+ *
+ * The page's kernel takes separate query and key/value sequence lengths and
+ * per-tensor batch/head strides (doc comment of
+ * FlashAttention3Plan::generate_forward and its kernel parameter list); this
+ * entry point takes both, plus row strides.
+ *
+ *   q        [B,H,Sq,D]  element (b,h,i,d) at q + b*qs[0] + h*qs[1] + i*qs[2] + d
+ *   k, v     [B,H,Skv,D] likewise with k_strides / v_strides
+ *   o        [B,H,Sq,D]  likewise with o_strides (written in full)
+ *   lse      [B,H,Sq] fp32, contiguous (written in full)
+ *   *_strides  host arrays of 3 int64 (batch, head, row strides in elements)
+ *              or NULL for contiguous [B,H,rows,D].  Every stride of a
+ *              dimension longer than 1 must be a multiple of 8 elements
+ *              (16 bytes) and >= 0; row strides >= D; o's strides must not
+ *              make two elements share an address; one head of any tensor
+ *              must span less than 2 GiB.
+ *   Sq, Skv  >= 0.  B*H*Sq == 0 is a valid empty call.  With Skv == 0 no
+ *            key is read and k, v may be NULL.
+ *   causal   keeps key j for query i iff j <= i + (Skv - Sq): the last query
+ *            sees the last key (j <= i when Sq == Skv).  A query with no key
+ *            left (causal, Sq > Skv; or Skv == 0) gets O = 0 and LSE = -inf.
+ * Everything else (pointer alignment, dtype, head dim, scale, aliasing,
+ * stream, errors) is as for attn_fwd; aliasing is judged on each tensor's
+ * byte extent from its first to its last element.
+ */
+int attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
+                     const int64_t* q_strides, const int64_t* k_strides,
+                     const int64_t* v_strides, const int64_t* o_strides, float scale,
+                     int causal, int dtype, void* stream);
 
 /*
  * attn_fwd_plan -- the launch geometry attn_fwd would use (host only, no HIP

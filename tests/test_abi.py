@@ -202,3 +202,59 @@ def test_no_gpu_reports_unsupported_device():
         pytest.skip("a GPU is present")
     assert call() == 8
     assert "device" in _lib.last_error()
+
+
+# --------------------------------------------------------------------------
+# attn_fwd_strided: argument checks (all before any HIP call)
+# --------------------------------------------------------------------------
+def scall(q=FAKE, k=FAKE + 0x1000000, v=FAKE + 0x2000000, o=FAKE + 0x3000000, lse=FAKE + 0x4000000,
+          B=1, H=2, Sq=16, Skv=24, D=64, qs=None, ks=None, vs=None, os_=None, scale=0.125, causal=0,
+          dtype=0):
+    return _lib.attn_fwd_strided(q, k, v, o, lse, B, H, Sq, Skv, D, qs, ks, vs, os_, scale, causal,
+                                 dtype, 0)
+
+
+@pytest.mark.parametrize("kwargs,status,word", [
+    (dict(Sq=-1), 2, "Sq and Skv"),
+    (dict(Skv=-3), 2, "Sq and Skv"),
+    (dict(Skv=1 << 30), 2, "too large"),
+    (dict(D=96), 3, "head_dim"),
+    (dict(dtype=7), 4, "dtype"),
+    (dict(k=0), 1, "NULL"),
+    (dict(qs=(2048, 1024, 56)), 10, "shorter than a row"),
+    (dict(vs=(3072, -1536, 64)), 10, ">= 0"),
+    (dict(ks=(3072, 1536, 68)), 5, "multiples of 8"),
+    (dict(os_=(2048, 1028, 64)), 5, "multiples of 8"),
+    (dict(qs=(0, 0, 1 << 31)), 2, "2 gib"),
+    (dict(os_=(2048, 512, 64)), 7, "o strides"),        # head 1 starts inside head 0's 16 rows
+    (dict(os_=(2048, 32, 128)), 7, "o strides"),        # head 1 starts in the middle of a row of head 0
+    (dict(o=FAKE + 64), 7, "overlaps"),
+    (dict(lse=FAKE + 0x2000000 + 64), 7, "overlaps"),
+    (dict(scale=-1.0), 6, "scale"),
+])
+def test_strided_invalid_arguments_rejected_before_launch(kwargs, status, word):
+    st = scall(**kwargs)
+    assert st == status, (st, _lib.last_error())
+    assert word.lower() in _lib.last_error().lower()
+
+
+def test_strided_empty_query_is_a_noop():
+    assert scall(q=0, k=0, v=0, o=0, lse=0, Sq=0) == 0
+    assert scall(q=0, k=0, v=0, o=0, lse=0, B=0) == 0
+
+
+def test_strided_valid_layouts_reach_the_device_check():
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("would launch on a real GPU with fake pointers")
+    # [B,S,H,D] views (row stride H*D), padded rows, a size-1 batch whose
+    # (unaligned) batch stride never addresses anything, and Skv = 0
+    B, H, Sq, Skv, D = 2, 4, 16, 24, 64
+    for kw in (dict(qs=(Sq * H * D, D, H * D), ks=(Skv * H * D, D, H * D), vs=(Skv * H * D, D, H * D),
+                    os_=(Sq * H * D, D, H * D)),
+               dict(qs=(H * Sq * 72, Sq * 72, 72), os_=(H * Sq * 72, Sq * 72, 72)),
+               dict(B=1, qs=(3, Sq * D, D)),
+               dict(Skv=0)):
+        args = dict(B=B, H=H, Sq=Sq, Skv=Skv, D=D)
+        args.update(kw)
+        assert scall(**args) == 8, _lib.last_error()
