@@ -4,7 +4,8 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The GPU library never loads it and it
 never loads the GPU library.
 
-``attn_fwd`` / ``attn_fwd_online`` / ``attn_probs`` wrap ``liboracle.so``
+``attn_fwd`` / ``attn_fwd_online`` / ``attn_probs`` / ``attn_bwd`` (and the
+float64-input ``attn_fwd_f64`` / ``attn_bwd_f64``) wrap ``liboracle.so``
 (built from ``attn_oracle.c`` by :func:`build`); ``brute`` holds a pure-Python
 brute force for tiny shapes.  Definitions and citations are in the C source.
 """
@@ -52,6 +53,14 @@ def _load():
         lib.oracle_attn_fwd_online.restype = ci
         lib.oracle_attn_probs.argtypes = [vp, vp, ci, i64, i64, i64, i64, dbl, ci, vp]
         lib.oracle_attn_probs.restype = ci
+        lib.oracle_attn_fwd_f64.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, dbl, ci, vp, vp]
+        lib.oracle_attn_fwd_f64.restype = ci
+        lib.oracle_attn_bwd_f64.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, dbl, ci,
+                                            vp, vp, vp, vp]
+        lib.oracle_attn_bwd_f64.restype = ci
+        lib.oracle_attn_bwd.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, i64, i64, dbl, ci,
+                                        vp, vp, vp, vp]
+        lib.oracle_attn_bwd.restype = ci
         lib.oracle_decode.argtypes = [vp, ci, i64, vp]
         lib.oracle_decode.restype = None
         lib.oracle_num_threads.argtypes = []
@@ -136,3 +145,68 @@ def attn_probs(q, k, dtype: str, scale: float, causal: bool):
     if rc != 0:
         raise MemoryError("oracle scratch allocation failed")
     return p
+
+
+def _f64(a):
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    if a.ndim != 4:
+        raise ValueError("expected [B,H,S,D] float64 arrays")
+    return a
+
+
+def _qkv_shapes(q, k, v, *more):
+    B, H, Sq, D = q.shape
+    Skv = k.shape[2]
+    if k.shape != (B, H, Skv, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [B,H,Skv,D] with q's B, H, D")
+    for t in more:
+        if t.shape != q.shape:
+            raise ValueError("dO must have q's shape")
+    return B, H, Sq, Skv, D
+
+
+def attn_fwd_f64(q, k, v, scale: float, causal: bool):
+    """The forward definition on float64 arrays: O [B,H,Sq,D], LSE [B,H,Sq]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, Sq, Skv, D = _qkv_shapes(q, k, v)
+    o = np.empty((B, H, Sq, D), dtype=np.float64)
+    lse = np.empty((B, H, Sq), dtype=np.float64)
+    rc = _load().oracle_attn_fwd_f64(q.ctypes.data, k.ctypes.data, v.ctypes.data, B, H, Sq, Skv,
+                                     D, float(scale), int(bool(causal)), o.ctypes.data,
+                                     lse.ctypes.data)
+    if rc != 0:
+        raise MemoryError("oracle scratch allocation failed")
+    return o, lse
+
+
+def _bwd_out(B, H, Sq, Skv, D):
+    return (np.empty((B, H, Sq, D)), np.empty((B, H, Skv, D)), np.empty((B, H, Skv, D)),
+            np.empty((B, H, Sq)))
+
+
+def attn_bwd_f64(q, k, v, do, scale: float, causal: bool):
+    """The backward on float64 arrays: dQ, dK, dV and D_i = rowsum(dP * P)."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, H, Sq, Skv, D = _qkv_shapes(q, k, v, do)
+    dq, dk, dv, delta = _bwd_out(B, H, Sq, Skv, D)
+    rc = _load().oracle_attn_bwd_f64(q.ctypes.data, k.ctypes.data, v.ctypes.data, do.ctypes.data,
+                                     B, H, Sq, Skv, D, float(scale), int(bool(causal)),
+                                     dq.ctypes.data, dk.ctypes.data, dv.ctypes.data,
+                                     delta.ctypes.data)
+    if rc != 0:
+        raise MemoryError("oracle scratch allocation failed")
+    return dq, dk, dv, delta
+
+
+def attn_bwd(q, k, v, do, dtype: str, scale: float, causal: bool):
+    """The backward of 16-bit inputs q, k, v, dO (uint16 words of `dtype`),
+    computed in float64: dQ [B,H,Sq,D], dK, dV [B,H,Skv,D], D_i [B,H,Sq]."""
+    q, k, v, do = _words(q), _words(k), _words(v), _words(do)
+    B, H, Sq, Skv, D = _qkv_shapes(q, k, v, do)
+    dq, dk, dv, delta = _bwd_out(B, H, Sq, Skv, D)
+    rc = _load().oracle_attn_bwd(q.ctypes.data, k.ctypes.data, v.ctypes.data, do.ctypes.data,
+                                 _DT[dtype], B, H, Sq, Skv, D, float(scale), int(bool(causal)),
+                                 dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, delta.ctypes.data)
+    if rc != 0:
+        raise MemoryError("oracle scratch allocation failed")
+    return dq, dk, dv, delta

@@ -34,6 +34,9 @@
  *                          (the page's "online softmax with running max (m)
  *                          and sum (l)"); used to show tiling is exact
  *   oracle_attn_probs      the softmax matrix P itself, for small S
+ * and, on float64 inputs, the same forward (oracle_attn_fwd_f64) and the
+ * backward of the page's doc comment of generate_backward
+ * (oracle_attn_bwd_f64; oracle_attn_bwd widens 16-bit inputs first).
  */
 #include <math.h>
 #include <stdint.h>
@@ -277,4 +280,174 @@ int oracle_attn_probs(const uint16_t* q, const uint16_t* k, int dtype,
   free(qd);
   free(s);
   return 0;
+}
+
+/*
+ * ---------------------------------------------------------------------------
+ * Float64 inputs.  The same forward definition on float64 arrays (contiguous
+ * Q [B,H,Sq,D], K, V [B,H,Skv,D]), so that the backward below can be checked
+ * by finite differences of it, and the backward itself.
+ * ---------------------------------------------------------------------------
+ */
+static void scores_row_f64(const double* q, const double* k, int64_t bh, int64_t i,
+                           int64_t Sq, int64_t Skv, int64_t D, double scale, int64_t n,
+                           double* s) {
+  const double* qrow = q + (bh * Sq + i) * D;
+  for (int64_t j = 0; j < n; ++j) {
+    const double* krow = k + (bh * Skv + j) * D;
+    double acc = 0.0;
+    for (int64_t d = 0; d < D; ++d) acc += qrow[d] * krow[d];
+    s[j] = scale * acc;
+  }
+}
+
+/* P_ij = exp(s_ij - m_i) / l_i over the n kept keys; returns LSE_i. */
+static double softmax_row(double* s, int64_t n) {
+  double m = s[0];
+  for (int64_t j = 1; j < n; ++j) m = s[j] > m ? s[j] : m;
+  double l = 0.0;
+  for (int64_t j = 0; j < n; ++j) l += exp(s[j] - m);
+  for (int64_t j = 0; j < n; ++j) s[j] = exp(s[j] - m) / l;
+  return m + log(l);
+}
+
+int oracle_attn_fwd_f64(const double* q, const double* k, const double* v, int64_t B,
+                        int64_t H, int64_t Sq, int64_t Skv, int64_t D, double scale,
+                        int causal, double* o, double* lse) {
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* p = (double*)malloc(sizeof(double) * (size_t)(Skv > 0 ? Skv : 1));
+    if (!p) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 8)
+      for (int64_t r = 0; r < B * H * Sq; ++r) {
+        const int64_t bh = r / Sq, i = r % Sq;
+        const int64_t n = allowed_keys(i, Sq, Skv, causal);
+        double* orow = o + r * D;
+        for (int64_t d = 0; d < D; ++d) orow[d] = 0.0;
+        if (n <= 0) {
+          lse[r] = -INFINITY;
+          continue;
+        }
+        scores_row_f64(q, k, bh, i, Sq, Skv, D, scale, n, p);
+        lse[r] = softmax_row(p, n);
+        for (int64_t j = 0; j < n; ++j) {
+          const double* vrow = v + (bh * Skv + j) * D;
+          for (int64_t d = 0; d < D; ++d) orow[d] += p[j] * vrow[d];
+        }
+      }
+    }
+    free(p);
+  }
+  return failed ? -1 : 0;
+}
+
+/*
+ * The backward (source: the same page, doc comment of
+ * FlashAttention3Plan::generate_backward): given the gradient dO of the
+ * loss with respect to O, with P recomputed from the scores,
+ *
+ *   P_ij  = exp(s_ij - LSE_i) for j in A_i, 0 otherwise
+ *   dV_j  = sum_i P_ij dO_i                 (dV = P^T dO)
+ *   dP_ij = dO_i . v_j                      (dP = dO V^T)
+ *   D_i   = sum_j dP_ij P_ij                (the page's rowsum(dP * P))
+ *   dS_ij = P_ij (dP_ij - D_i)
+ *   dQ_i  = scale * sum_j dS_ij k_j         (dQ = dS K)
+ *   dK_j  = scale * sum_i dS_ij q_i         (dK = dS^T Q)
+ *
+ * dS is the gradient with respect to the scaled scores s = scale * q.k, so
+ * the chain rule puts the factor `scale` on dQ and dK (the page lists
+ * sm_scale among the kernel's parameters and leaves it out of the formulas).
+ * A query with no key has P = 0: dQ_i = 0, D_i = 0.  delta receives D_i
+ * [B,H,Sq]; dq [B,H,Sq,D], dk and dv [B,H,Skv,D].  Parallel over heads, each
+ * head's rows in order.  Returns 0, or -1 when scratch memory cannot be had.
+ */
+int oracle_attn_bwd_f64(const double* q, const double* k, const double* v, const double* dO,
+                        int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
+                        double scale, int causal, double* dq, double* dk, double* dv,
+                        double* delta) {
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* p = (double*)malloc(sizeof(double) * (size_t)(Skv > 0 ? Skv : 1));
+    double* ds = (double*)malloc(sizeof(double) * (size_t)(Skv > 0 ? Skv : 1));
+    if (!p || !ds) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t bh = 0; bh < B * H; ++bh) {
+        double* dkh = dk + bh * Skv * D;
+        double* dvh = dv + bh * Skv * D;
+        for (int64_t e = 0; e < Skv * D; ++e) dkh[e] = dvh[e] = 0.0;
+        for (int64_t i = 0; i < Sq; ++i) {
+          const int64_t r = bh * Sq + i;
+          const double* qrow = q + r * D;
+          const double* dorow = dO + r * D;
+          double* dqrow = dq + r * D;
+          for (int64_t d = 0; d < D; ++d) dqrow[d] = 0.0;
+          const int64_t n = allowed_keys(i, Sq, Skv, causal);
+          if (n <= 0) {
+            delta[r] = 0.0;
+            continue;
+          }
+          scores_row_f64(q, k, bh, i, Sq, Skv, D, scale, n, p);
+          softmax_row(p, n);
+          /* dP_ij, then D_i = sum_j dP_ij P_ij */
+          double di = 0.0;
+          for (int64_t j = 0; j < n; ++j) {
+            const double* vrow = v + (bh * Skv + j) * D;
+            double dp = 0.0;
+            for (int64_t d = 0; d < D; ++d) dp += dorow[d] * vrow[d];
+            ds[j] = dp;
+            di += dp * p[j];
+          }
+          delta[r] = di;
+          for (int64_t j = 0; j < n; ++j) {
+            ds[j] = p[j] * (ds[j] - di);
+            const double* krow = k + (bh * Skv + j) * D;
+            double* dkrow = dkh + j * D;
+            double* dvrow = dvh + j * D;
+            for (int64_t d = 0; d < D; ++d) {
+              dqrow[d] += scale * ds[j] * krow[d];
+              dkrow[d] += scale * ds[j] * qrow[d];
+              dvrow[d] += p[j] * dorow[d];
+            }
+          }
+        }
+      }
+    }
+    free(p);
+    free(ds);
+  }
+  return failed ? -1 : 0;
+}
+
+/* The backward of 16-bit inputs (widened exactly to float64 first). */
+int oracle_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                    const uint16_t* dO, int dtype, int64_t B, int64_t H, int64_t Sq,
+                    int64_t Skv, int64_t D, double scale, int causal, double* dq,
+                    double* dk, double* dv, double* delta) {
+  const int64_t nq = B * H * Sq * D, nk = B * H * Skv * D;
+  double* qd = (double*)malloc(sizeof(double) * (size_t)(nq > 0 ? nq : 1));
+  double* dod = (double*)malloc(sizeof(double) * (size_t)(nq > 0 ? nq : 1));
+  double* kd = (double*)malloc(sizeof(double) * (size_t)(nk > 0 ? nk : 1));
+  double* vd = (double*)malloc(sizeof(double) * (size_t)(nk > 0 ? nk : 1));
+  int rc = -1;
+  if (qd && dod && kd && vd) {
+    oracle_decode(q, dtype, nq, qd);
+    oracle_decode(dO, dtype, nq, dod);
+    oracle_decode(k, dtype, nk, kd);
+    oracle_decode(v, dtype, nk, vd);
+    rc = oracle_attn_bwd_f64(qd, kd, vd, dod, B, H, Sq, Skv, D, scale, causal, dq, dk, dv,
+                             delta);
+  }
+  free(qd);
+  free(dod);
+  free(kd);
+  free(vd);
+  return rc;
 }
