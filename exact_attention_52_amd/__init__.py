@@ -3,7 +3,9 @@
 ``fwd(q, k, v, scale=None, causal=False)`` returns ``(o, lse)`` for fp16/bf16
 CUDA tensors q [B,H,Sq,D] and k, v [B,H,Skv,D] (any strides with the last
 dimension contiguous): O = softmax(scale * Q K^T [causal]) V and the
-natural-log LSE per row (fp32).  PyTorch only provides device memory and the
+natural-log LSE per row (fp32).  ``bwd(q, k, v, o, lse, do, ...)`` returns
+``(dq, dk, dv, delta)``, the gradients for a given dO (contiguous tensors).
+PyTorch only provides device memory and the
 stream; the computation is the libattn.so gfx950 kernel behind the C ABI of
 include/attn.h.  ``inputs`` holds the seeded synthetic-input generator.
 """
@@ -14,11 +16,12 @@ import math
 from . import _lib
 from ._lib import ATTN_BF16, ATTN_F16, AttnError  # noqa: F401
 
-__all__ = ["fwd", "attn_fwd", "attn_fwd_strided", "attn_fwd_plan", "attn_fwd_workgroup_tile",
-           "AttnError"]
+__all__ = ["fwd", "bwd", "attn_fwd", "attn_fwd_strided", "attn_bwd", "attn_fwd_plan",
+           "attn_fwd_workgroup_tile", "AttnError"]
 
 attn_fwd = _lib.attn_fwd
 attn_fwd_strided = _lib.attn_fwd_strided
+attn_bwd = _lib.attn_bwd
 attn_fwd_plan = _lib.attn_fwd_plan
 attn_fwd_workgroup_tile = _lib.attn_fwd_workgroup_tile
 
@@ -80,3 +83,47 @@ def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
                                        stream.cuda_stream)
     _lib.check(st)
     return out, lse
+
+
+def bwd(q, k, v, o, lse, do, scale=None, causal=False, dq=None, dk=None, dv=None, delta=None,
+        stream=None):
+    """Gradients of ``fwd`` for the output gradient ``do``.
+
+    q, o, do: contiguous [B,H,Sq,D]; k, v: contiguous [B,H,Skv,D]; one dtype
+    (fp16 or bf16); lse: contiguous fp32 [B,H,Sq], with o and lse from ``fwd``
+    on the same inputs.  Returns (dq, dk, dv, delta): dq [B,H,Sq,D], dk, dv
+    [B,H,Skv,D] in the input dtype and delta = rowsum(do * o) fp32 [B,H,Sq].
+    Outputs may be passed preallocated (contiguous).
+    """
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        if t.dim() != 4 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-D GPU tensor")
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v, o, do must share one dtype")
+    B, H, Sq, D = q.shape
+    Skv = k.shape[2]
+    if k.shape != (B, H, Skv, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [B,H,Skv,D] with q's B, H and D")
+    if o.shape != q.shape or do.shape != q.shape:
+        raise ValueError("o and do must have q's shape")
+    if lse.shape != (B, H, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B,H,Sq] tensor")
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    delta = torch.empty_like(lse) if delta is None else delta
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v), ("delta", delta, lse)):
+        if t.shape != ref.shape or t.dtype != ref.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous with the shape and dtype of its input")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        st = _lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                           do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                           B, H, Sq, Skv, D, scale, causal, dt, stream.cuda_stream)
+    _lib.check(st)
+    return dq, dk, dv, delta

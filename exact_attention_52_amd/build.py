@@ -4,6 +4,7 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -12,25 +13,29 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = [os.path.join(CSRC, "attn_api.hip")]
-HEADERS = [os.path.join(CSRC, "attn_fwd_kernel.hpp"), os.path.join(INCLUDE, "attn.h")]
+SOURCES = [os.path.join(CSRC, "attn_api.hip"), os.path.join(CSRC, "attn_bwd.hip")]
+HEADERS = [os.path.join(CSRC, "attn_fwd_kernel.hpp"), os.path.join(CSRC, "attn_bwd_kernel.hpp"),
+           os.path.join(CSRC, "attn_bwd.hpp"), os.path.join(INCLUDE, "attn.h")]
 
 FLAGS = [
-    "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
+    "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",
     "-Wall", "-Wno-unused-command-line-argument",
     # keep the compiler from emitting packed-fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA accumulators in VGPRs: left to its heuristics the compiler parks the
-    # D=256 output accumulator in AGPRs and copies all of it to VGPRs and back
-    # on every key tile (the rescale multiplies it on the VALU, which cannot
-    # address AGPRs); in VGPR form the kernel fits in 249 VGPRs with no copies
-    "-mllvm", "--amdgpu-mfma-vgpr-form=1",
 ]
+# Per-source flags.  Forward: MFMA accumulators in VGPRs; left to its
+# heuristics the compiler parks the D=256 output accumulator in AGPRs and
+# copies all of it to VGPRs and back on every key tile (the rescale multiplies
+# it on the VALU, which cannot address AGPRs); in VGPR form the kernel fits in
+# 249 VGPRs with no copies.  Backward: its accumulators are only ever MFMA
+# operands, so they stay in AGPRs and free the VGPRs.
+SOURCE_FLAGS = {
+    "attn_api.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form=1"],
+    "attn_bwd.hip": [],
+}
 
 
-def build(out: str = LIB, extra_flags=()) -> str:
-    tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *extra_flags, "-I" + INCLUDE, "-I" + CSRC, "-o", tmp, *SOURCES]
+def _run(cmd):
     proc = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [ln for ln in (proc.stdout + proc.stderr).splitlines()
             if "packed-fp32-ops' is not a recognized feature" not in ln]
@@ -39,6 +44,19 @@ def build(out: str = LIB, extra_flags=()) -> str:
         raise RuntimeError("hipcc failed building libattn.so")
     if msgs:
         sys.stderr.write("\n".join(msgs) + "\n")
+
+
+def build(out: str = LIB, extra_flags=()) -> str:
+    """Compile each source to an object (with its own flags) and link them."""
+    tmp = out + ".tmp"
+    with tempfile.TemporaryDirectory() as d:
+        objs = []
+        for src in SOURCES:
+            obj = os.path.join(d, os.path.basename(src) + ".o")
+            _run([HIPCC, *FLAGS, *SOURCE_FLAGS[os.path.basename(src)], *extra_flags,
+                  "-I" + INCLUDE, "-I" + CSRC, "-c", "-o", obj, src])
+            objs.append(obj)
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, out)
     return out
 

@@ -17,6 +17,7 @@
 #include <string>
 
 #include "attn.h"
+#include "attn_bwd.hpp"
 #include "attn_fwd_kernel.hpp"
 
 namespace {
@@ -303,6 +304,61 @@ int attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float
   };
   return run(q, k, v, o, lse, B, H, Sq, Skv, D, view(q_strides, Sq, "q"), view(k_strides, Skv, "k"),
              view(v_strides, Skv, "v"), view(o_strides, Sq, "o"), scale, causal, dtype, stream);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+             void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
+             int64_t D, float scale, int causal, int dtype, void* stream) {
+  if (B < 0 || H < 0 || Sq < 0 || Skv < 0)
+    return fail(ATTN_ERR_BAD_SHAPE, "B, H, Sq and Skv must be >= 0 (got B=%lld H=%lld Sq=%lld Skv=%lld)",
+                (long long)B, (long long)H, (long long)Sq, (long long)Skv);
+  int st = check_sizes(B, H, Sq > Skv ? Sq : Skv, D, dtype);
+  if (st != ATTN_OK) return st;
+  if (!(std::isfinite(scale) && scale >= 0.f))
+    return fail(ATTN_ERR_BAD_SCALE, "scale must be finite and >= 0 (got %g)", (double)scale);
+  if (B == 0 || H == 0 || (Sq == 0 && Skv == 0)) return ok();
+  const bool has_q = Sq > 0, has_k = Skv > 0;
+  if ((has_q && (!q || !o || !dO || !lse || !dq || !delta)) || (has_k && (!k || !v || !dk || !dv)))
+    return fail(ATTN_ERR_NULL_PTR, "q, k, v, o, lse, dO, dq, dk, dv and delta must be non-NULL");
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dO | (uintptr_t)dq |
+       (uintptr_t)dk | (uintptr_t)dv) & 15)
+    return fail(ATTN_ERR_MISALIGNED, "q, k, v, o, dO, dq, dk and dv must be 16-byte aligned");
+  if (((uintptr_t)lse | (uintptr_t)delta) & 3) return fail(ATTN_ERR_MISALIGNED, "lse and delta must be 4-byte aligned");
+  const int64_t nq = B * H * Sq * D * 2, nk = B * H * Skv * D * 2, nr = B * H * Sq * 4;
+  struct Buf {
+    const void* p;
+    int64_t n;
+  };
+  const Buf outs[4] = {{dq, nq}, {dk, nk}, {dv, nk}, {delta, nr}};
+  const Buf ins[6] = {{q, nq}, {k, nk}, {v, nk}, {o, nq}, {dO, nq}, {lse, nr}};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n))
+        return fail(ATTN_ERR_ALIASING, "dq, dk, dv and delta must not overlap each other");
+    for (const Buf& b : ins)
+      if (overlaps(outs[i].p, outs[i].n, b.p, b.n))
+        return fail(ATTN_ERR_ALIASING, "dq, dk, dv and delta must not overlap q, k, v, o, dO or lse");
+  }
+  const attn::BwdPlan plan = attn::bwd_plan((int)D);
+  const int64_t gq = B * H * ((Sq + plan.dq_queries_per_workgroup - 1) / plan.dq_queries_per_workgroup);
+  const int64_t gk = B * H * ((Skv + plan.dkdv_keys_per_workgroup - 1) / plan.dkdv_keys_per_workgroup);
+  const int64_t gd = (B * H * Sq + plan.delta_rows_per_workgroup - 1) / plan.delta_rows_per_workgroup;
+  if (gq > 0x7FFFFFFF || gk > 0x7FFFFFFF || gd > 0x7FFFFFFF)
+    return fail(ATTN_ERR_BAD_SHAPE, "grid exceeds the launch limit");
+  st = check_device();
+  if (st != ATTN_OK) return st;
+
+  attn::BwdProblem p;
+  p.q = (const uint16_t*)q, p.k = (const uint16_t*)k, p.v = (const uint16_t*)v, p.o = (const uint16_t*)o;
+  p.dO = (const uint16_t*)dO, p.lse = lse, p.delta = delta;
+  p.dq = (uint16_t*)dq, p.dk = (uint16_t*)dk, p.dv = (uint16_t*)dv;
+  p.Sq = (int)Sq, p.Skv = (int)Skv, p.nq = 0, p.nk = 0, p.BH = B * H;
+  float c = (float)((double)scale * 1.4426950408889634074);
+  p.c = c < FLT_MIN ? FLT_MIN : c;
+  p.scale = scale;
+  const hipError_t e = attn::bwd_launch(p, (int)D, causal != 0, dtype, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(ATTN_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
 }
 
 int attn_fwd_plan(int64_t B, int64_t H, int64_t S, int64_t D, int causal, int dtype, attn_fwd_plan_t* out) {

@@ -1,0 +1,48 @@
+// attn_bwd.hpp -- host-side view of the backward kernels: the problem they
+// read and the launcher that plans and enqueues them (attn_bwd.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+// Contiguous Q, O, dO, dQ [B,H,Sq,D] and K, V, dK, dV [B,H,Skv,D] of 16-bit
+// elements; LSE and delta [B,H,Sq] fp32.  Causal keeps key j for query i iff
+// j <= i + (Skv - Sq), as in the forward.
+struct BwdProblem {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dO;
+  const float* lse;
+  float* delta;  // written by the first kernel: D_i = rowsum(dO_i * O_i)
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  int Sq, Skv;
+  int nq, nk;  // query tiles per head (dQ kernel), key tiles per head (dK/dV kernel)
+  int64_t BH;  // B * H
+  float c;     // scale * log2(e), kept >= FLT_MIN
+  float scale;
+};
+
+// Launch geometry of the three backward kernels for head dim D.
+struct BwdPlan {
+  int delta_rows_per_workgroup;
+  int dkdv_keys_per_workgroup;  // key tile of the dK/dV kernel
+  int dkdv_query_step;          // queries per step of its loop
+  int dq_queries_per_workgroup;  // query tile of the dQ kernel
+  int dq_key_step;               // keys per step of its loop
+  int threads_per_workgroup;
+  int lds_bytes;                 // per workgroup, either kernel
+};
+
+BwdPlan bwd_plan(int D);
+
+// Enqueue the delta, dK/dV and dQ kernels on `stream` (p.nq, p.nk are filled
+// in here).  D is 64, 128 or 256; the caller has validated everything.
+hipError_t bwd_launch(BwdProblem p, int D, bool causal, int dtype, hipStream_t stream);
+
+}  // namespace attn

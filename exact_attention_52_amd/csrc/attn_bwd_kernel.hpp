@@ -1,0 +1,500 @@
+// attn_bwd_kernel.hpp -- gfx950 (CDNA4) kernels of the exact attention
+// backward.
+//
+// Gradients of O = softmax(scale * Q K^T, causal mask) V for a given dO, with
+// the probabilities recomputed from the LSE the forward saved (docs.rs page
+// "oxicuda-dnn 0.1.8, src/attn/flash_attn/hopper.rs", doc comment of
+// FlashAttention3Plan::generate_backward):
+//   P_ij = exp(scale q_i.k_j - LSE_i)  (0 where masked)
+//   D_i  = rowsum(dO_i * O_i)                        kernel attn_bwd_delta
+//   dV = P^T dO, dP = dO V^T, dS = P * (dP - D_i),
+//   dK = scale dS^T Q                                kernel attn_bwd_dkdv
+//   dQ = scale dS K                                  kernel attn_bwd_dq
+// (dS is the gradient of the scaled scores, so the chain rule puts `scale`
+// on dK and dQ.)
+//
+// MI355X mapping:
+//   * dK/dV: one workgroup per (key tile, b*H + h); wave w owns 32 keys and
+//     keeps their K and V rows in VGPRs as the B operands of S = Q K^T and
+//     dP = dO V^T, and their dK^T, dV^T in MFMA accumulators.  Q and dO tiles
+//     stream through two LDS stages.  In S and dP (v_mfma_f32_32x32x16) lane
+//     l holds key l%32 and 16 query rows in registers, which is exactly the
+//     B operand layout of dV^T += dO^T P and dK^T += Q^T dS once packed to 16
+//     bits: the A operands dO^T and Q^T come from ds_read_b64_tr_b16.
+//   * dQ: one workgroup per (query tile, b*H + h), the forward's shape: Q and
+//     dO of 32 queries per wave in VGPRs (B operands of S^T = K Q^T and
+//     dP^T = V dO^T: lane l holds query l%32, so LSE_i and D_i are one scalar
+//     per lane), K and V tiles stream through LDS, dQ^T += K^T dS^T with K^T
+//     read transposed.  This recomputes S and dP once more instead of the
+//     page's atomic dQ accumulation: dQ is written once, deterministically.
+//   * The LDS tiles are read both ways (16-byte row reads and transposing
+//     reads), so their rows are spread over 1 KiB copy lines in an order that
+//     keeps both kinds of read free of bank conflicts (XTile below).
+#pragma once
+
+#include "attn_bwd.hpp"
+#include "attn_fwd_kernel.hpp"
+
+namespace attn {
+namespace bwd {
+
+// LDS tile of ROWS rows of D 16-bit elements, filled by 1 KiB HBM -> LDS copy
+// lines (RPL = 512/D rows each) and read two ways:
+//   row reads: a 16-lane quarter of a 16-byte read takes the same 16 bytes of
+//     16 consecutive rows;
+//   transposing reads: 32 lanes take 64 bytes of each of 4 consecutive rows
+//     (4 aligned rows 4a..4a+3).
+// Line n of a 16-line block holds rows r(n) + 16m (m < RPL) with
+// r(n) = 4*(n%4) + n/4, and lines are 1040 bytes apart, so row r (mod 16)
+// starts at 16*(4*(r%4) + r/4) modulo the 256-byte bank sweep: 16 consecutive
+// rows take 16 distinct 16-byte bank groups, and rows 4a..4a+3 start 64
+// bytes apart.  r(n) is its own inverse: row r sits in line r(r).
+template <int D_, int ROWS_>
+struct XTile {
+  static constexpr int D = D_, ROWS = ROWS_;
+  static constexpr int ROW_BYTES = 2 * D;
+  static constexpr int RPL = 1024 / ROW_BYTES;
+  static constexpr int BLOCK_ROWS = 16 * RPL;  // rows of a 16-line block
+  static constexpr int LINE = 1024 + 16;
+  static constexpr int LINES = ROWS * ROW_BYTES / 1024;
+  static constexpr int BYTES = LINES * LINE;
+  static constexpr __host__ __device__ int perm(int r16) { return 4 * (r16 % 4) + r16 / 4; }
+  static constexpr __host__ __device__ int off(int row) {
+    return (row / BLOCK_ROWS) * 16 * LINE + perm(row % 16) * LINE + ((row % BLOCK_ROWS) / 16) * ROW_BYTES;
+  }
+  // first tile row of copy line n
+  static constexpr __host__ __device__ int line_row(int n) { return (n / 16) * BLOCK_ROWS + perm(n % 16); }
+  static_assert(ROWS % BLOCK_ROWS == 0, "a tile holds whole 16-line blocks");
+};
+
+// The operand addresses below split off(row) into a per-lane part and a
+// compile-time part; that is exact when the parts are aligned as checked here.
+template <class X>
+constexpr bool offsets_split() {
+  for (int base = 0; base < X::ROWS; base += 16)
+    for (int r = 0; r < 16; ++r)
+      if (X::off(base + r) != X::off(base) + X::off(r)) return false;
+  for (int base = 0; base < X::ROWS; base += 32)
+    for (int r = 0; r < 32; ++r)
+      if (X::off(base + r) != X::off(base) + X::off(r)) return false;
+  for (int a = 0; a < 16; a += 8)
+    for (int r = 0; r < 8; ++r)
+      if (X::off(a + r) != X::off(a) + X::off(r)) return false;
+  return true;
+}
+
+// HBM -> LDS copies of XTile tiles of one head (contiguous rows of D).  Lane i
+// of a copy instruction carries row slot i / (D/8) of the line and 16-byte
+// chunk i % (D/8).  Rows at or past `rows` read as 0.
+template <class X>
+struct XCopier {
+  static constexpr int D = X::D;
+  const uint16_t* src;
+  int rows;
+  uint32_t lane_off;
+  __device__ __forceinline__ void init(const uint16_t* src_, int rows_, int lane) {
+    src = src_;
+    rows = rows_;
+    lane_off = (uint32_t)(16 * (lane / (D / 8)) * D + (lane % (D / 8)) * 8) * 2u;
+  }
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile(int r0) const {
+    return make_rsrc(src + (int64_t)r0 * D, r0 < rows ? rows_bytes(rows - r0, D, D) : 0u);
+  }
+  __device__ __forceinline__ void line(__amdgpu_buffer_rsrc_t r, uint8_t* dst, int n) const {
+    load16_lds(r, dst + n * X::LINE, lane_off, (uint32_t)(X::line_row(n) * D) * 2u);
+  }
+};
+
+// 4 bytes per lane from global memory straight into LDS at lds + 4*lane; a
+// lane whose dword lies past the buffer descriptor's end writes 0.
+__device__ __forceinline__ void load4_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t byte_off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, (int)byte_off, 0, 0, 0);
+}
+
+template <int DT>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc);
+template <>
+__device__ __forceinline__ float dot2<DT_F16>(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), acc, false);
+}
+template <>
+__device__ __forceinline__ float dot2<DT_BF16>(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc, false);
+}
+
+constexpr float kLog2e = 1.4426950408889634074f;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// D_i = sum_d dO[i,d] * O[i,d] in fp32, D/8 lanes per row.
+// ---------------------------------------------------------------------------
+template <int D, int DT>
+__global__ __launch_bounds__(256) void attn_bwd_delta(const BwdProblem p) {
+  constexpr int LPR = D / 8, RPB = 256 / LPR;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int part = threadIdx.x % LPR;
+  float acc = 0.f;
+  if (row < p.BH * p.Sq) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(p.o + row * D + part * 8);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(p.dO + row * D + part * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = dot2<DT>(a[e], b[e], acc);
+  }
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m /= 2) acc += __shfl_xor(acc, m, 64);
+  if (row < p.BH * p.Sq && part == 0) p.delta[row] = acc;
+}
+
+// Tile shapes per head dim: every tile is one 16-line block of XTile.
+template <int D_>
+struct BwdCfg {
+  static constexpr int D = D_;
+  static constexpr int NW = 4;                  // waves per workgroup
+  static constexpr int NT = 64 * NW;
+  static constexpr int STEP = 16 * (512 / D);   // rows of a streamed tile: 128 / 64 / 32
+  static constexpr int BN = 32 * NW;            // keys per dK/dV workgroup
+  static constexpr int BM = 32 * NW;            // queries per dQ workgroup
+  static constexpr int DK = D / 16, DB = D / 32;
+  using X = XTile<D, STEP>;
+  static constexpr int LDS_BYTES = 4 * X::BYTES + 4 * 4 * (STEP > 64 ? STEP : 64);  // 2 stages x 2 tiles (+ row values)
+  static_assert(offsets_split<X>(), "operand offsets must split into lane and constant parts");
+  static_assert(X::LINES % NW == 0, "copy lines must split evenly over the waves");
+};
+
+// Lane part of a transposing read (ds_read_b64_tr_b16) of an XTile: in each
+// 16-lane group lane i reads row i/4 of 4 consecutive rows (4*half + i/4
+// after the k-slot order of the packed 16-bit operands) at columns
+// 4*(i%4)..+3; the second 16-lane group of each half reads 16 columns on.
+template <class X>
+__device__ __forceinline__ int tr_lane_off(int lane) {
+  return X::off(4 * (lane >> 5) + ((lane & 15) >> 2)) + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+}
+
+// A operand (32 rows x 16 head-dim columns) from the transposing reads of
+// rows 16*ks + {8r + 4*half + 0..3 : r = 0, 1} at head-dim block db.
+template <class X>
+__device__ __forceinline__ u32x4 tr_operand(const uint8_t* t, int trl, int ks, int db) {
+  const uint8_t* p = t + trl + 64 * db;
+  const u32x2 lo = lds_read_tr16(p + X::off(16 * ks));
+  const u32x2 hi = lds_read_tr16(p + X::off(16 * ks + 8));
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one workgroup per (key tile of BN keys, b*H + h).
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL, int DT>
+__global__ __launch_bounds__(BwdCfg<D>::NT) void attn_bwd_dkdv(const BwdProblem p) {
+  using C = BwdCfg<D>;
+  using X = typename C::X;
+  using E = Elem<DT>;
+  constexpr int BQ = C::STEP, MB = BQ / 32, DK = C::DK, DB = C::DB, BN = C::BN;
+  constexpr int LPW = X::LINES / C::NW;
+  // LSE and D_i of a step's queries go to LDS too, 64 rows per copy
+  // instruction (one dword per lane), one instruction per wave
+  constexpr int LR = BQ > 64 ? BQ : 64;
+  static_assert(2 * (LR / 64) <= C::NW, "one row-value copy per wave");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t qt0[X::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t qt1[X::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t ot0[X::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t ot1[X::BYTES];
+  __shared__ __attribute__((aligned(16))) float ls0[LR];
+  __shared__ __attribute__((aligned(16))) float ls1[LR];
+  __shared__ __attribute__((aligned(16))) float dl0[LR];
+  __shared__ __attribute__((aligned(16))) float dl1[LR];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 31, half = lane >> 5;
+
+  // key tiles in order of decreasing cost when causal (key tile 0 is seen by
+  // the most queries); otherwise contiguous runs per XCD as in the forward
+  int64_t kt64, bh;
+  if (CAUSAL) {
+    bh = (int64_t)blockIdx.x % p.BH;
+    kt64 = (int64_t)blockIdx.x / p.BH;
+  } else {
+    workgroup_tile(blockIdx.x, p.BH * p.nk, p.nk, 0, &kt64, &bh);
+  }
+  const int Sq = p.Sq, Skv = p.Skv, koff = Skv - Sq;
+  const int k0 = (int)kt64 * BN, kbase = k0 + 32 * wave, my_k = kbase + col;
+  const uint16_t* qh = p.q + bh * Sq * D;
+  const uint16_t* doh = p.dO + bh * Sq * D;
+  const uint16_t* kh = p.k + bh * Skv * D;
+  const uint16_t* vh = p.v + bh * Skv * D;
+  const float* lseh = p.lse + bh * Sq;
+  const float* delh = p.delta + bh * Sq;
+  const __amdgpu_buffer_rsrc_t lse_r = make_rsrc(lseh, (uint32_t)Sq * 4u);
+  const __amdgpu_buffer_rsrc_t del_r = make_rsrc(delh, (uint32_t)Sq * 4u);
+
+  // this wave's keys: B operands of S = Q K^T and dP = dO V^T (rows past Skv read 0)
+  u32x4 kf[DK], vf[DK];
+  {
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kh, rows_bytes(Skv, D, D));
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vh, rows_bytes(Skv, D, D));
+    const uint32_t off = (uint32_t)(my_k * D + 8 * half) * 2u;
+#pragma unroll
+    for (int kc = 0; kc < DK; ++kc) {
+      kf[kc] = load16(kr, off + 32 * kc);
+      vf[kc] = load16(vr, off + 32 * kc);
+    }
+  }
+  f32x16 dka[DB], dva[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dka[db] = dva[db] = f32x16{};
+
+  // queries that see any key of the tile: i >= k0 - koff when causal
+  int qs = CAUSAL ? k0 - koff : 0;
+  qs = qs < 0 ? 0 : qs / BQ * BQ;
+  const int n = qs < Sq ? (Sq - qs + BQ - 1) / BQ : 0;
+
+  XCopier<X> qc, oc;
+  qc.init(qh, Sq, lane);
+  oc.init(doh, Sq, lane);
+  auto fetch = [&](int s, uint8_t* dq_, uint8_t* do_, float* ls_, float* dl_) __attribute__((always_inline)) {
+    const int r0 = qs + s * BQ;
+    const __amdgpu_buffer_rsrc_t rq = qc.tile(r0), ro = oc.tile(r0);
+#pragma unroll
+    for (int l = 0; l < LPW; ++l) {
+      qc.line(rq, dq_, wave * LPW + l);
+      oc.line(ro, do_, wave * LPW + l);
+    }
+    // rows past Sq (or past the step) land as 0 or as unused values
+#pragma unroll
+    for (int m = 0; m < LR / 64; ++m) {
+      const uint32_t off = (uint32_t)(r0 + 64 * m + lane) * 4u;
+      if (wave == 2 * m) load4_lds(lse_r, ls_ + 64 * m, off);
+      if (wave == 2 * m + 1) load4_lds(del_r, dl_ + 64 * m, off);
+    }
+  };
+
+  const int xrow = X::off(col) + 16 * half;  // lane part of a row read
+  const int trl = tr_lane_off<X>(lane);      // lane part of a transposing read
+  const float c = p.c;
+
+  auto step = [&](int s, const uint8_t* qt, const uint8_t* ot, const float* ls, const float* dl)
+                  __attribute__((always_inline)) {
+    const int q0 = qs + s * BQ;
+    // every (query, key) pair of this wave masked: nothing to add
+    if (CAUSAL && kbase > q0 + BQ - 1 + koff) return;
+    const bool need_mask = CAUSAL && kbase + 31 > q0 + koff;
+    // score (query q0 + 32mb + 8g + 4half + t, key my_k) is kept iff
+    // 32mb + 8g + t >= my_k - koff - q0 - 4half
+    const int lim = my_k - koff - q0 - 4 * half;
+    u32x4 pf[2 * MB], sf[2 * MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      f32x16 sa = f32x16{}, dpa = f32x16{};
+#pragma unroll
+      for (int kc = 0; kc < DK; ++kc) {
+        const int a_off = xrow + X::off(32 * mb) + 32 * kc;
+        sa = E::mfma(*reinterpret_cast<const u32x4*>(qt + a_off), kf[kc], sa);
+        dpa = E::mfma(*reinterpret_cast<const u32x4*>(ot + a_off), vf[kc], dpa);
+      }
+      float pr[16], ds[16];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        // the 4 rows of this register group (one broadcast LDS read per half)
+        const int rr = 32 * mb + 8 * g + 4 * half;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + rr);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dl + rr);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int i = 4 * g + t;
+          const float nl = -l4[t] * kLog2e;
+          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[i], c, nl));
+          if (need_mask) pv = (32 * mb + 8 * g + t) >= lim ? pv : 0.f;
+          pr[i] = pv;
+          ds[i] = pv * (dpa[i] - d4[t]);
+        }
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int b = 8 * s2;
+        pf[2 * mb + s2] = u32x4{E::pack2(pr[b], pr[b + 1]), E::pack2(pr[b + 2], pr[b + 3]),
+                                E::pack2(pr[b + 4], pr[b + 5]), E::pack2(pr[b + 6], pr[b + 7])};
+        sf[2 * mb + s2] = u32x4{E::pack2(ds[b], ds[b + 1]), E::pack2(ds[b + 2], ds[b + 3]),
+                                E::pack2(ds[b + 4], ds[b + 5]), E::pack2(ds[b + 6], ds[b + 7])};
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2 * MB; ++ks) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        dva[db] = E::mfma(tr_operand<X>(ot, trl, ks, db), pf[ks], dva[db]);
+        dka[db] = E::mfma(tr_operand<X>(qt, trl, ks, db), sf[ks], dka[db]);
+      }
+    }
+  };
+
+  if (n > 0) fetch(0, qt0, ot0, ls0, dl0);
+  for (int s = 0; s < n; s += 2) {
+    wait_loads();
+    __syncthreads();
+    if (s + 1 < n) fetch(s + 1, qt1, ot1, ls1, dl1);
+    step(s, qt0, ot0, ls0, dl0);
+    if (s + 1 >= n) break;
+    wait_loads();
+    __syncthreads();
+    if (s + 2 < n) fetch(s + 2, qt0, ot0, ls0, dl0);
+    step(s + 1, qt1, ot1, ls1, dl1);
+  }
+
+  if (my_k < Skv) {
+    uint16_t* dkr = p.dk + (bh * Skv + my_k) * D;
+    uint16_t* dvr = p.dv + (bh * Skv + my_k) * D;
+    const float sc = p.scale;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * db + 8 * g + 4 * half;
+        u32x2 wk, wv;
+        wk[0] = E::pack2(dka[db][4 * g] * sc, dka[db][4 * g + 1] * sc);
+        wk[1] = E::pack2(dka[db][4 * g + 2] * sc, dka[db][4 * g + 3] * sc);
+        wv[0] = E::pack2(dva[db][4 * g], dva[db][4 * g + 1]);
+        wv[1] = E::pack2(dva[db][4 * g + 2], dva[db][4 * g + 3]);
+        *reinterpret_cast<u32x2*>(dkr + d) = wk;
+        *reinterpret_cast<u32x2*>(dvr + d) = wv;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup per (query tile of BM queries, b*H + h).
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL, int DT>
+__global__ __launch_bounds__(BwdCfg<D>::NT) void attn_bwd_dq(const BwdProblem p) {
+  using C = BwdCfg<D>;
+  using X = typename C::X;
+  using E = Elem<DT>;
+  constexpr int BNK = C::STEP, NB = BNK / 32, DK = C::DK, DB = C::DB, BM = C::BM;
+  constexpr int LPW = X::LINES / C::NW;
+
+  __shared__ __attribute__((aligned(1024))) uint8_t kt0[X::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t kt1[X::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vt0[X::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vt1[X::BYTES];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 31, half = lane >> 5;
+
+  int64_t tile64, bh;
+  workgroup_tile(blockIdx.x, p.BH * p.nq, p.nq, CAUSAL, &tile64, &bh);
+  const int Sq = p.Sq, Skv = p.Skv, koff = Skv - Sq;
+  const int q0 = (int)tile64 * BM, wq_first = q0 + 32 * wave, my_q = wq_first + col;
+  const uint16_t* kh = p.k + bh * Skv * D;
+  const uint16_t* vh = p.v + bh * Skv * D;
+
+  // this wave's queries: B operands of S^T = K Q^T and dP^T = V dO^T
+  u32x4 qf[DK], of[DK];
+  {
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(p.q + bh * Sq * D, rows_bytes(Sq, D, D));
+    const __amdgpu_buffer_rsrc_t orr = make_rsrc(p.dO + bh * Sq * D, rows_bytes(Sq, D, D));
+    const uint32_t off = (uint32_t)(my_q * D + 8 * half) * 2u;
+#pragma unroll
+    for (int kc = 0; kc < DK; ++kc) {
+      qf[kc] = load16(qr, off + 32 * kc);
+      of[kc] = load16(orr, off + 32 * kc);
+    }
+  }
+  const bool q_ok = my_q < Sq;
+  const float nl = q_ok ? -p.lse[bh * Sq + my_q] * kLog2e : 0.f;
+  const float dl = q_ok ? p.delta[bh * Sq + my_q] : 0.f;
+  f32x16 dqa[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dqa[db] = f32x16{};
+
+  const int q_end = q0 + BM < Sq ? q0 + BM : Sq;
+  int kv_end = CAUSAL ? q_end + koff : Skv;
+  kv_end = kv_end < Skv ? kv_end : Skv;
+  const int n = kv_end > 0 ? (kv_end + BNK - 1) / BNK : 0;
+
+  XCopier<X> kc_, vc_;
+  kc_.init(kh, Skv, lane);
+  vc_.init(vh, Skv, lane);
+  auto fetch = [&](int j, uint8_t* k_, uint8_t* v_) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rk = kc_.tile(j * BNK), rv = vc_.tile(j * BNK);
+#pragma unroll
+    for (int l = 0; l < LPW; ++l) {
+      kc_.line(rk, k_, wave * LPW + l);
+      vc_.line(rv, v_, wave * LPW + l);
+    }
+  };
+
+  const int xrow = X::off(col) + 16 * half;
+  const int trl = tr_lane_off<X>(lane);
+  const float c = p.c;
+  const int last = CAUSAL ? (my_q + koff < Skv - 1 ? my_q + koff : Skv - 1) : Skv - 1;
+
+  auto step = [&](int j, const uint8_t* kt, const uint8_t* vt) __attribute__((always_inline)) {
+    const int kv0 = j * BNK;
+    if (wq_first >= Sq || (CAUSAL && kv0 > wq_first + 31 + koff)) return;
+    const bool need_mask = (kv0 + BNK > Skv) || (CAUSAL && kv0 + BNK - 1 > wq_first + koff);
+    // score (key kv0 + 32kb + 8g + 4half + t, query my_q) kept iff key <= last
+    const int lim = last - kv0 - 4 * half;
+    u32x4 sf[2 * NB];
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) {
+      f32x16 sa = f32x16{}, dpa = f32x16{};
+#pragma unroll
+      for (int kc = 0; kc < DK; ++kc) {
+        const int a_off = xrow + X::off(32 * kb) + 32 * kc;
+        sa = E::mfma(*reinterpret_cast<const u32x4*>(kt + a_off), qf[kc], sa);
+        dpa = E::mfma(*reinterpret_cast<const u32x4*>(vt + a_off), of[kc], dpa);
+      }
+      float ds[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[i], c, nl));
+        if (need_mask) pv = (32 * kb + 8 * (i >> 2) + (i & 3)) <= lim ? pv : 0.f;
+        ds[i] = pv * (dpa[i] - dl);
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int b = 8 * s2;
+        sf[2 * kb + s2] = u32x4{E::pack2(ds[b], ds[b + 1]), E::pack2(ds[b + 2], ds[b + 3]),
+                                E::pack2(ds[b + 4], ds[b + 5]), E::pack2(ds[b + 6], ds[b + 7])};
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2 * NB; ++ks)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) dqa[db] = E::mfma(tr_operand<X>(kt, trl, ks, db), sf[ks], dqa[db]);
+  };
+
+  if (n > 0) fetch(0, kt0, vt0);
+  for (int j = 0; j < n; j += 2) {
+    wait_loads();
+    __syncthreads();
+    if (j + 1 < n) fetch(j + 1, kt1, vt1);
+    step(j, kt0, vt0);
+    if (j + 1 >= n) break;
+    wait_loads();
+    __syncthreads();
+    if (j + 2 < n) fetch(j + 2, kt0, vt0);
+    step(j + 1, kt1, vt1);
+  }
+
+  if (q_ok) {
+    uint16_t* dqr = p.dq + (bh * Sq + my_q) * D;
+    const float sc = p.scale;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * db + 8 * g + 4 * half;
+        u32x2 w;
+        w[0] = E::pack2(dqa[db][4 * g] * sc, dqa[db][4 * g + 1] * sc);
+        w[1] = E::pack2(dqa[db][4 * g + 2] * sc, dqa[db][4 * g + 3] * sc);
+        *reinterpret_cast<u32x2*>(dqr + d) = w;
+      }
+    }
+  }
+}
+
+}  // namespace bwd
+}  // namespace attn

@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 
 /* Element type of Q, K, V and O.  The page restricts the float type to F16 or
  * BF16 (validate_config, "float_type must be F16 or BF16"). */
@@ -120,6 +120,40 @@ int attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float
                      const int64_t* q_strides, const int64_t* k_strides,
                      const int64_t* v_strides, const int64_t* o_strides, float scale,
                      int causal, int dtype, void* stream);
+
+/*
+ * attn_bwd -- gradients of the attention forward for a given dO.
+ *
+ * The page's backward (doc comment of FlashAttention3Plan::generate_backward)
+ * recomputes P from the saved log-sum-exp and forms dV = P^T dO,
+ * dP = dO V^T, dS = P * (dP - D_i) with D_i = rowsum(dO * O), dQ = dS K and
+ * dK = dS^T Q; its kernel takes q, k, v, o, do, lse, di, dq, dk, dv, the
+ * query and key/value lengths and sm_scale, as this call does.  dS is the
+ * gradient of the scaled scores, so dQ and dK carry the factor `scale`.
+ * dQ is accumulated without atomics: one kernel per key tile writes dK, dV,
+ * another per query tile writes dQ, so the result is deterministic.
+ *
+ *   q, o, dO  [B,H,Sq,D] `dtype`, contiguous, read only (o and lse as the
+ *             forward returned them for the same q, k, v, scale, causal)
+ *   k, v      [B,H,Skv,D] `dtype`, contiguous, read only
+ *   lse       [B,H,Sq] fp32 natural-log LSE from the forward, read only
+ *   dq        [B,H,Sq,D] `dtype`, written in full
+ *   dk, dv    [B,H,Skv,D] `dtype`, written in full
+ *   delta     [B,H,Sq] fp32, written in full with D_i (the page's di)
+ *   Sq, Skv   >= 0; causal keeps key j for query i iff j <= i + (Skv - Sq),
+ *             as in attn_fwd_strided.  Keys no query sees get dK = dV = 0,
+ *             queries with no key dQ = 0 and D_i = 0.
+ *   D, scale, causal, dtype, stream   as for attn_fwd.
+ * Inputs may alias one another; dq, dk, dv and delta must not overlap each
+ * other or any input.  16-bit tensors 16-byte aligned, fp32 ones 4-byte.
+ * Pointers of tensors with no element (Sq == 0: q, o, dO, lse, dq, delta;
+ * Skv == 0: k, v, dk, dv) may be NULL.  B*H == 0, or Sq == Skv == 0, is a
+ * valid empty call.  Errors and asynchrony as for attn_fwd.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o,
+             const float* lse, const void* dO, void* dq, void* dk, void* dv,
+             float* delta, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
+             int64_t D, float scale, int causal, int dtype, void* stream);
 
 /*
  * attn_fwd_plan -- the launch geometry attn_fwd would use (host only, no HIP

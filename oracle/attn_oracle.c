@@ -362,14 +362,24 @@ int oracle_attn_fwd_f64(const double* q, const double* k, const double* v, int64
  * the chain rule puts the factor `scale` on dQ and dK (the page lists
  * sm_scale among the kernel's parameters and leaves it out of the formulas).
  * A query with no key has P = 0: dQ_i = 0, D_i = 0.  delta receives D_i
- * [B,H,Sq]; dq [B,H,Sq,D], dk and dv [B,H,Skv,D].  Parallel over heads, each
- * head's rows in order.  Returns 0, or -1 when scratch memory cannot be had.
+ * [B,H,Sq]; dq [B,H,Sq,D], dk and dv [B,H,Skv,D].
+ *
+ * Two passes, each over independent outputs (so the result does not depend
+ * on the thread count):
+ *   1. per query row i: P_i. from the scores, LSE_i, dP_i., D_i, dS_i., dQ_i;
+ *   2. per key row j: for every query i that keeps key j, P_ij recomputed as
+ *      exp(s_ij - LSE_i) (the page's recomputation from the saved
+ *      log-sum-exp), dP_ij and dS_ij as above, summed into dK_j and dV_j.
+ * Returns 0, or -1 when scratch memory cannot be had.
  */
 int oracle_attn_bwd_f64(const double* q, const double* k, const double* v, const double* dO,
                         int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
                         double scale, int causal, double* dq, double* dk, double* dv,
                         double* delta) {
   int failed = 0;
+  double* lse = (double*)malloc(sizeof(double) * (size_t)(B * H * Sq > 0 ? B * H * Sq : 1));
+  if (!lse) return -1;
+  /* pass 1: rows of dQ, D_i and LSE_i */
 #pragma omp parallel
   {
     double* p = (double*)malloc(sizeof(double) * (size_t)(Skv > 0 ? Skv : 1));
@@ -378,51 +388,70 @@ int oracle_attn_bwd_f64(const double* q, const double* k, const double* v, const
 #pragma omp atomic write
       failed = 1;
     } else {
-#pragma omp for schedule(dynamic, 1)
-      for (int64_t bh = 0; bh < B * H; ++bh) {
-        double* dkh = dk + bh * Skv * D;
-        double* dvh = dv + bh * Skv * D;
-        for (int64_t e = 0; e < Skv * D; ++e) dkh[e] = dvh[e] = 0.0;
-        for (int64_t i = 0; i < Sq; ++i) {
-          const int64_t r = bh * Sq + i;
-          const double* qrow = q + r * D;
-          const double* dorow = dO + r * D;
-          double* dqrow = dq + r * D;
-          for (int64_t d = 0; d < D; ++d) dqrow[d] = 0.0;
-          const int64_t n = allowed_keys(i, Sq, Skv, causal);
-          if (n <= 0) {
-            delta[r] = 0.0;
-            continue;
-          }
-          scores_row_f64(q, k, bh, i, Sq, Skv, D, scale, n, p);
-          softmax_row(p, n);
-          /* dP_ij, then D_i = sum_j dP_ij P_ij */
-          double di = 0.0;
-          for (int64_t j = 0; j < n; ++j) {
-            const double* vrow = v + (bh * Skv + j) * D;
-            double dp = 0.0;
-            for (int64_t d = 0; d < D; ++d) dp += dorow[d] * vrow[d];
-            ds[j] = dp;
-            di += dp * p[j];
-          }
-          delta[r] = di;
-          for (int64_t j = 0; j < n; ++j) {
-            ds[j] = p[j] * (ds[j] - di);
-            const double* krow = k + (bh * Skv + j) * D;
-            double* dkrow = dkh + j * D;
-            double* dvrow = dvh + j * D;
-            for (int64_t d = 0; d < D; ++d) {
-              dqrow[d] += scale * ds[j] * krow[d];
-              dkrow[d] += scale * ds[j] * qrow[d];
-              dvrow[d] += p[j] * dorow[d];
-            }
-          }
+#pragma omp for schedule(dynamic, 4)
+      for (int64_t r = 0; r < B * H * Sq; ++r) {
+        const int64_t bh = r / Sq, i = r % Sq;
+        const double* dorow = dO + r * D;
+        double* dqrow = dq + r * D;
+        for (int64_t d = 0; d < D; ++d) dqrow[d] = 0.0;
+        const int64_t n = allowed_keys(i, Sq, Skv, causal);
+        if (n <= 0) {
+          delta[r] = 0.0;
+          lse[r] = -INFINITY;
+          continue;
+        }
+        scores_row_f64(q, k, bh, i, Sq, Skv, D, scale, n, p);
+        lse[r] = softmax_row(p, n);
+        /* dP_ij, then D_i = sum_j dP_ij P_ij */
+        double di = 0.0;
+        for (int64_t j = 0; j < n; ++j) {
+          const double* vrow = v + (bh * Skv + j) * D;
+          double dp = 0.0;
+          for (int64_t d = 0; d < D; ++d) dp += dorow[d] * vrow[d];
+          ds[j] = dp;
+          di += dp * p[j];
+        }
+        delta[r] = di;
+        for (int64_t j = 0; j < n; ++j) {
+          const double dsj = p[j] * (ds[j] - di);
+          const double* krow = k + (bh * Skv + j) * D;
+          for (int64_t d = 0; d < D; ++d) dqrow[d] += scale * dsj * krow[d];
         }
       }
     }
     free(p);
     free(ds);
   }
+  /* pass 2: rows of dK and dV */
+  if (!failed) {
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t c = 0; c < B * H * Skv; ++c) {
+      const int64_t bh = c / Skv, j = c % Skv;
+      const double* krow = k + c * D;
+      const double* vrow = v + c * D;
+      double* dkrow = dk + c * D;
+      double* dvrow = dv + c * D;
+      for (int64_t d = 0; d < D; ++d) dkrow[d] = dvrow[d] = 0.0;
+      for (int64_t i = 0; i < Sq; ++i) {
+        if (j >= allowed_keys(i, Sq, Skv, causal)) continue;
+        const int64_t r = bh * Sq + i;
+        const double* qrow = q + r * D;
+        const double* dorow = dO + r * D;
+        double s = 0.0, dp = 0.0;
+        for (int64_t d = 0; d < D; ++d) {
+          s += qrow[d] * krow[d];
+          dp += dorow[d] * vrow[d];
+        }
+        const double pij = exp(scale * s - lse[r]);
+        const double dsij = pij * (dp - delta[r]);
+        for (int64_t d = 0; d < D; ++d) {
+          dkrow[d] += scale * dsij * qrow[d];
+          dvrow[d] += pij * dorow[d];
+        }
+      }
+    }
+  }
+  free(lse);
   return failed ? -1 : 0;
 }
 

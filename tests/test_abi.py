@@ -258,3 +258,52 @@ def test_strided_valid_layouts_reach_the_device_check():
         args = dict(B=B, H=H, Sq=Sq, Skv=Skv, D=D)
         args.update(kw)
         assert scall(**args) == 8, _lib.last_error()
+
+
+# --------------------------------------------------------------------------
+# attn_bwd: argument checks (all before any HIP call)
+# --------------------------------------------------------------------------
+MB_ = 0x1000000
+
+
+def bcall(q=FAKE, k=FAKE + MB_, v=FAKE + 2 * MB_, o=FAKE + 3 * MB_, lse=FAKE + 4 * MB_, do=FAKE + 5 * MB_,
+          dq=FAKE + 6 * MB_, dk=FAKE + 7 * MB_, dv=FAKE + 8 * MB_, delta=FAKE + 9 * MB_, B=1, H=2, Sq=16,
+          Skv=24, D=64, scale=0.125, causal=0, dtype=0):
+    return _lib.attn_bwd(q, k, v, o, lse, do, dq, dk, dv, delta, B, H, Sq, Skv, D, scale, causal, dtype, 0)
+
+
+@pytest.mark.parametrize("kwargs,status,word", [
+    (dict(Sq=-1), 2, ">= 0"),
+    (dict(Skv=1 << 30), 2, "too large"),
+    (dict(D=80), 3, "head_dim"),
+    (dict(dtype=2), 4, "dtype"),
+    (dict(scale=float("nan")), 6, "scale"),
+    (dict(do=0), 1, "NULL"),
+    (dict(delta=0), 1, "NULL"),
+    (dict(dk=0), 1, "NULL"),
+    (dict(dq=FAKE + 6 * MB_ + 8), 5, "16-byte"),
+    (dict(lse=FAKE + 4 * MB_ + 2), 5, "4-byte"),
+    (dict(dk=FAKE + 6 * MB_ + 64), 7, "each other"),           # dk inside dq
+    (dict(delta=FAKE + 8 * MB_), 7, "each other"),             # delta on dv
+    (dict(dv=FAKE + 5 * MB_ + 16), 7, "must not overlap q"),   # dv inside dO
+    (dict(dq=FAKE + 4 * MB_), 7, "must not overlap q"),        # dq on lse
+])
+def test_bwd_invalid_arguments_rejected_before_launch(kwargs, status, word):
+    st = bcall(**kwargs)
+    assert st == status, (st, _lib.last_error())
+    assert word.lower() in _lib.last_error().lower()
+
+
+def test_bwd_empty_calls():
+    assert bcall(B=0) == 0
+    assert bcall(Sq=0, Skv=0, q=0, k=0, v=0, o=0, lse=0, do=0, dq=0, dk=0, dv=0, delta=0) == 0
+
+
+def test_bwd_null_tensors_without_elements_reach_the_device_check():
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("would launch on a real GPU with fake pointers")
+    # no queries: q, o, dO, lse, dq, delta are never touched; no keys: k, v, dk, dv
+    assert bcall(Sq=0, q=0, o=0, lse=0, do=0, dq=0, delta=0) == 8, _lib.last_error()
+    assert bcall(Skv=0, k=0, v=0, dk=0, dv=0) == 8, _lib.last_error()
+    assert bcall(k=FAKE, v=FAKE, q=FAKE, o=FAKE, do=FAKE) == 8, _lib.last_error()  # inputs may alias
