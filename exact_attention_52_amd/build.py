@@ -23,15 +23,16 @@ FLAGS = [
     # keep the compiler from emitting packed-fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
-# Per-source flags.  Forward: MFMA accumulators in VGPRs; left to its
-# heuristics the compiler parks the D=256 output accumulator in AGPRs and
-# copies all of it to VGPRs and back on every key tile (the rescale multiplies
-# it on the VALU, which cannot address AGPRs); in VGPR form the kernel fits in
-# 249 VGPRs with no copies.  Backward: its accumulators are only ever MFMA
-# operands, so they stay in AGPRs and free the VGPRs.
+# Per-source flags.  MFMA accumulators in VGPRs: left to its heuristics the
+# compiler parks accumulators in AGPRs and copies them to VGPRs and back
+# around loop boundaries (the forward's D=256 output accumulator on every key
+# tile: the rescale multiplies it on the VALU, which cannot address AGPRs; the
+# backward's dK/dV accumulators at every loop header); in VGPR form the forward
+# D=256 kernel fits in 249 VGPRs with no copies and the D=64/128 dK/dV kernels
+# fit two waves per SIMD.
 SOURCE_FLAGS = {
     "attn_api.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form=1"],
-    "attn_bwd.hip": [],
+    "attn_bwd.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form=1"],
 }
 
 

@@ -97,8 +97,11 @@ struct XCopier {
     rows = rows_;
     lane_off = (uint32_t)(16 * (lane / (D / 8)) * D + (lane % (D / 8)) * 8) * 2u;
   }
+  // (the byte count is wave-uniform; readfirstlane keeps it in an SGPR, where
+  // a buffer descriptor must be, instead of a loop over distinct lane values)
   __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile(int r0) const {
-    return make_rsrc(src + (int64_t)r0 * D, r0 < rows ? rows_bytes(rows - r0, D, D) : 0u);
+    const uint32_t bytes = r0 < rows ? rows_bytes(rows - r0, D, D) : 0u;
+    return make_rsrc(src + (int64_t)r0 * D, (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes));
   }
   __device__ __forceinline__ void line(__amdgpu_buffer_rsrc_t r, uint8_t* dst, int n) const {
     load16_lds(r, dst + n * X::LINE, lane_off, (uint32_t)(X::line_row(n) * D) * 2u);
@@ -123,6 +126,16 @@ __device__ __forceinline__ float dot2<DT_BF16>(uint32_t a, uint32_t b, float acc
 }
 
 constexpr float kLog2e = 1.4426950408889634074f;
+
+// Wait for this wave's copies, then for every wave, with scheduling fences on
+// both sides: without them the scheduler moves MFMAs of one step across the
+// barrier into the next, which keeps two steps' registers live at once.
+__device__ __forceinline__ void fenced_sync() {
+  __builtin_amdgcn_sched_barrier(0);
+  wait_loads();
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+}
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
@@ -155,6 +168,9 @@ struct BwdCfg {
   static constexpr int BN = 32 * NW;            // keys per dK/dV workgroup
   static constexpr int BM = 32 * NW;            // queries per dQ workgroup
   static constexpr int DK = D / 16, DB = D / 32;
+  // two waves per SIMD (at most 256 registers each) where the registers
+  // allow it: one wave's MFMAs then run beside the other's VALU work
+  static constexpr int WAVES_PER_SIMD = D <= 128 ? 2 : 1;
   using X = XTile<D, STEP>;
   static constexpr int LDS_BYTES = 4 * X::BYTES + 4 * 4 * (STEP > 64 ? STEP : 64);  // 2 stages x 2 tiles (+ row values)
   static_assert(offsets_split<X>(), "operand offsets must split into lane and constant parts");
@@ -184,7 +200,8 @@ __device__ __forceinline__ u32x4 tr_operand(const uint8_t* t, int trl, int ks, i
 // dK, dV: one workgroup per (key tile of BN keys, b*H + h).
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, int DT>
-__global__ __launch_bounds__(BwdCfg<D>::NT) void attn_bwd_dkdv(const BwdProblem p) {
+__global__ __launch_bounds__(BwdCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(BwdCfg<D>::WAVES_PER_SIMD)))
+void attn_bwd_dkdv(const BwdProblem p) {
   using C = BwdCfg<D>;
   using X = typename C::X;
   using E = Elem<DT>;
@@ -276,21 +293,42 @@ __global__ __launch_bounds__(BwdCfg<D>::NT) void attn_bwd_dkdv(const BwdProblem 
   auto step = [&](int s, const uint8_t* qt, const uint8_t* ot, const float* ls, const float* dl)
                   __attribute__((always_inline)) {
     const int q0 = qs + s * BQ;
-    // every (query, key) pair of this wave masked: nothing to add
-    if (CAUSAL && kbase > q0 + BQ - 1 + koff) return;
+    // every (query, key) pair of this wave masked, or no key of the wave
+    // exists: nothing to add
+    if ((CAUSAL && kbase > q0 + BQ - 1 + koff) || kbase >= Skv) return;
     const bool need_mask = CAUSAL && kbase + 31 > q0 + koff;
     // score (query q0 + 32mb + 8g + 4half + t, key my_k) is kept iff
     // 32mb + 8g + t >= my_k - koff - q0 - 4half
     const int lim = my_k - koff - q0 - 4 * half;
-    u32x4 pf[2 * MB], sf[2 * MB];
+    // one 32-query block at a time (S, dP, then P, dS, then dV, dK), fenced,
+    // so that only one block's scores and packed operands are live; each MFMA
+    // run is a PIPE-deep operand pipeline (operand t+PIPE read from LDS while
+    // MFMA t runs), pinned by scheduling groups so that the reads are not all
+    // hoisted ahead of the MFMAs
+    constexpr int PIPE = 4;
+    constexpr int N1 = 2 * DK;      // S and dP MFMAs, alternating
+    constexpr int N3 = 2 * 2 * DB;  // dV and dK MFMAs, alternating
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       f32x16 sa = f32x16{}, dpa = f32x16{};
+      {
+        auto rd = [&](int t) __attribute__((always_inline)) -> u32x4 {
+          return *reinterpret_cast<const u32x4*>(((t & 1) ? ot : qt) + xrow + X::off(32 * mb) + 32 * (t >> 1));
+        };
+        u32x4 buf[PIPE];
 #pragma unroll
-      for (int kc = 0; kc < DK; ++kc) {
-        const int a_off = xrow + X::off(32 * mb) + 32 * kc;
-        sa = E::mfma(*reinterpret_cast<const u32x4*>(qt + a_off), kf[kc], sa);
-        dpa = E::mfma(*reinterpret_cast<const u32x4*>(ot + a_off), vf[kc], dpa);
+        for (int t = 0; t < PIPE; ++t) buf[t] = rd(t);
+#pragma unroll
+        for (int t = 0; t < N1; ++t) {
+          const u32x4 a = buf[t % PIPE];
+          if (t + PIPE < N1) buf[t % PIPE] = rd(t + PIPE);
+          if (t & 1)
+            dpa = E::mfma(a, vf[t >> 1], dpa);
+          else
+            sa = E::mfma(a, kf[t >> 1], sa);
+        }
+        sched_prologue<0, N1, 0, PIPE>();
+        sched_steady<0, N1, 0, PIPE, 0, 1>();
       }
       float pr[16], ds[16];
 #pragma unroll
@@ -309,34 +347,48 @@ __global__ __launch_bounds__(BwdCfg<D>::NT) void attn_bwd_dkdv(const BwdProblem 
           ds[i] = pv * (dpa[i] - d4[t]);
         }
       }
+      u32x4 pf[2], sf[2];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         const int b = 8 * s2;
-        pf[2 * mb + s2] = u32x4{E::pack2(pr[b], pr[b + 1]), E::pack2(pr[b + 2], pr[b + 3]),
-                                E::pack2(pr[b + 4], pr[b + 5]), E::pack2(pr[b + 6], pr[b + 7])};
-        sf[2 * mb + s2] = u32x4{E::pack2(ds[b], ds[b + 1]), E::pack2(ds[b + 2], ds[b + 3]),
-                                E::pack2(ds[b + 4], ds[b + 5]), E::pack2(ds[b + 6], ds[b + 7])};
+        pf[s2] = u32x4{E::pack2(pr[b], pr[b + 1]), E::pack2(pr[b + 2], pr[b + 3]), E::pack2(pr[b + 4], pr[b + 5]),
+                       E::pack2(pr[b + 6], pr[b + 7])};
+        sf[s2] = u32x4{E::pack2(ds[b], ds[b + 1]), E::pack2(ds[b + 2], ds[b + 3]), E::pack2(ds[b + 4], ds[b + 5]),
+                       E::pack2(ds[b + 6], ds[b + 7])};
       }
-    }
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        // op t: s2 = t / (2 DB), db = (t / 2) % DB; even t: dV^T += dO^T P, odd: dK^T += Q^T dS
+        auto rd = [&](int t) __attribute__((always_inline)) -> u32x4 {
+          return tr_operand<X>((t & 1) ? qt : ot, trl, 2 * mb + t / (2 * DB), (t / 2) % DB);
+        };
+        u32x4 buf[PIPE];
 #pragma unroll
-    for (int ks = 0; ks < 2 * MB; ++ks) {
+        for (int t = 0; t < PIPE; ++t) buf[t] = rd(t);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        dva[db] = E::mfma(tr_operand<X>(ot, trl, ks, db), pf[ks], dva[db]);
-        dka[db] = E::mfma(tr_operand<X>(qt, trl, ks, db), sf[ks], dka[db]);
+        for (int t = 0; t < N3; ++t) {
+          const u32x4 a = buf[t % PIPE];
+          if (t + PIPE < N3) buf[t % PIPE] = rd(t + PIPE);
+          const int s2 = t / (2 * DB), db = (t / 2) % DB;
+          if (t & 1)
+            dka[db] = E::mfma(a, sf[s2], dka[db]);
+          else
+            dva[db] = E::mfma(a, pf[s2], dva[db]);
+        }
+        sched_prologue<0, N3, N3, PIPE>();
+        sched_steady<0, N3, N3, PIPE, 0, 1>();
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   if (n > 0) fetch(0, qt0, ot0, ls0, dl0);
   for (int s = 0; s < n; s += 2) {
-    wait_loads();
-    __syncthreads();
+    fenced_sync();
     if (s + 1 < n) fetch(s + 1, qt1, ot1, ls1, dl1);
     step(s, qt0, ot0, ls0, dl0);
     if (s + 1 >= n) break;
-    wait_loads();
-    __syncthreads();
+    fenced_sync();
     if (s + 2 < n) fetch(s + 2, qt0, ot0, ls0, dl0);
     step(s + 1, qt1, ot1, ls1, dl1);
   }
@@ -366,7 +418,8 @@ __global__ __launch_bounds__(BwdCfg<D>::NT) void attn_bwd_dkdv(const BwdProblem 
 // dQ: one workgroup per (query tile of BM queries, b*H + h).
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, int DT>
-__global__ __launch_bounds__(BwdCfg<D>::NT) void attn_bwd_dq(const BwdProblem p) {
+__global__ __launch_bounds__(BwdCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(BwdCfg<D>::WAVES_PER_SIMD)))
+void attn_bwd_dq(const BwdProblem p) {
   using C = BwdCfg<D>;
   using X = typename C::X;
   using E = Elem<DT>;
@@ -468,13 +521,11 @@ __global__ __launch_bounds__(BwdCfg<D>::NT) void attn_bwd_dq(const BwdProblem p)
 
   if (n > 0) fetch(0, kt0, vt0);
   for (int j = 0; j < n; j += 2) {
-    wait_loads();
-    __syncthreads();
+    fenced_sync();
     if (j + 1 < n) fetch(j + 1, kt1, vt1);
     step(j, kt0, vt0);
     if (j + 1 >= n) break;
-    wait_loads();
-    __syncthreads();
+    fenced_sync();
     if (j + 2 < n) fetch(j + 2, kt0, vt0);
     step(j + 1, kt1, vt1);
   }
