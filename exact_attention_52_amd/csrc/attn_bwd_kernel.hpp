@@ -489,15 +489,32 @@ void attn_bwd_dq(const BwdProblem p) {
     const bool need_mask = (kv0 + BNK > Skv) || (CAUSAL && kv0 + BNK - 1 > wq_first + koff);
     // score (key kv0 + 32kb + 8g + 4half + t, query my_q) kept iff key <= last
     const int lim = last - kv0 - 4 * half;
-    u32x4 sf[2 * NB];
+    // one 32-key block at a time, each MFMA run a pinned PIPE-deep operand
+    // pipeline (as in the dK/dV kernel)
+    constexpr int PIPE = 4;
+    constexpr int N1 = 2 * DK;  // S^T and dP^T MFMAs, alternating
+    constexpr int N3 = 2 * DB;  // dQ^T MFMAs
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb) {
       f32x16 sa = f32x16{}, dpa = f32x16{};
+      {
+        auto rd = [&](int t) __attribute__((always_inline)) -> u32x4 {
+          return *reinterpret_cast<const u32x4*>(((t & 1) ? vt : kt) + xrow + X::off(32 * kb) + 32 * (t >> 1));
+        };
+        u32x4 buf[PIPE];
 #pragma unroll
-      for (int kc = 0; kc < DK; ++kc) {
-        const int a_off = xrow + X::off(32 * kb) + 32 * kc;
-        sa = E::mfma(*reinterpret_cast<const u32x4*>(kt + a_off), qf[kc], sa);
-        dpa = E::mfma(*reinterpret_cast<const u32x4*>(vt + a_off), of[kc], dpa);
+        for (int t = 0; t < PIPE; ++t) buf[t] = rd(t);
+#pragma unroll
+        for (int t = 0; t < N1; ++t) {
+          const u32x4 a = buf[t % PIPE];
+          if (t + PIPE < N1) buf[t % PIPE] = rd(t + PIPE);
+          if (t & 1)
+            dpa = E::mfma(a, of[t >> 1], dpa);
+          else
+            sa = E::mfma(a, qf[t >> 1], sa);
+        }
+        sched_prologue<0, N1, 0, PIPE>();
+        sched_steady<0, N1, 0, PIPE, 0, 1>();
       }
       float ds[16];
 #pragma unroll
@@ -506,17 +523,33 @@ void attn_bwd_dq(const BwdProblem p) {
         if (need_mask) pv = (32 * kb + 8 * (i >> 2) + (i & 3)) <= lim ? pv : 0.f;
         ds[i] = pv * (dpa[i] - dl);
       }
+      u32x4 sf[2];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         const int b = 8 * s2;
-        sf[2 * kb + s2] = u32x4{E::pack2(ds[b], ds[b + 1]), E::pack2(ds[b + 2], ds[b + 3]),
-                                E::pack2(ds[b + 4], ds[b + 5]), E::pack2(ds[b + 6], ds[b + 7])};
+        sf[s2] = u32x4{E::pack2(ds[b], ds[b + 1]), E::pack2(ds[b + 2], ds[b + 3]), E::pack2(ds[b + 4], ds[b + 5]),
+                       E::pack2(ds[b + 6], ds[b + 7])};
       }
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        // op t: s2 = t / DB, db = t % DB
+        auto rd = [&](int t) __attribute__((always_inline)) -> u32x4 {
+          return tr_operand<X>(kt, trl, 2 * kb + t / DB, t % DB);
+        };
+        u32x4 buf[PIPE];
+#pragma unroll
+        for (int t = 0; t < PIPE; ++t) buf[t] = rd(t);
+#pragma unroll
+        for (int t = 0; t < N3; ++t) {
+          const u32x4 a = buf[t % PIPE];
+          if (t + PIPE < N3) buf[t % PIPE] = rd(t + PIPE);
+          dqa[t % DB] = E::mfma(a, sf[t / DB], dqa[t % DB]);
+        }
+        sched_prologue<0, N3, N3, PIPE>();
+        sched_steady<0, N3, N3, PIPE, 0, 1>();
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int ks = 0; ks < 2 * NB; ++ks)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) dqa[db] = E::mfma(tr_operand<X>(kt, trl, ks, db), sf[ks], dqa[db]);
   };
 
   if (n > 0) fetch(0, kt0, vt0);
