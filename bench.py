@@ -11,6 +11,12 @@ causal) and the inputs already resident in HBM.  The roofline object uses the
 average kernel duration from HIP events recorded around every launch of the
 timed region on the stream the kernel runs on.  The CPU baseline times the
 fp64 oracle on a bounded sample of rows of the same workload.
+
+The `backward` object times attn_bwd (dQ, dK, dV and D_i for a seeded dO)
+on the same inputs, with the forward's O and LSE: TFLOP/s at the usual
+10*B*H*S^2*D (five S x S x D GEMMs, halved when causal) and at the 14*B*H*S^2*D
+the kernels execute (the dQ kernel recomputes S and dP), plus a parity spot
+check of one head against the oracle.
 """
 from __future__ import annotations
 
@@ -106,6 +112,57 @@ def time_workload(ea, shape, dev, steps, warmup):
     return total / steps, float(np.mean(per)), o, lse
 
 
+def bwd_flops(B, H, S, D, causal, gemms=5):
+    f = 2.0 * gemms * B * H * S * S * D
+    return f / 2 if causal else f
+
+
+def make_do(shape, seed=1):
+    import torch
+    from exact_attention_52_amd import inputs
+    B, H, S, D, dtype, causal = shape
+    do, _, _ = inputs.gen_qkv(B, H, S, D, dtype, seed=seed)
+    tdt = torch.float16 if dtype == "fp16" else torch.bfloat16
+    return do, torch.from_numpy(do.view(np.int16)).view(tdt).to("cuda:0")
+
+
+def time_backward(ea, shape, dev, ddo, steps, warmup):
+    """Mean ms per attn_bwd call (HIP events on the launch stream) and the outputs."""
+    import torch
+    B, H, S, D, dtype, causal = shape
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    q, k, v = dev
+    stream = torch.cuda.current_stream()
+    o, lse = ea.fwd(q, k, v, scale=scale, causal=causal, stream=stream)
+    outs = ea.bwd(q, k, v, o, lse, ddo, scale=scale, causal=causal, stream=stream)
+    kw = dict(scale=scale, causal=causal, dq=outs[0], dk=outs[1], dv=outs[2], delta=outs[3], stream=stream)
+    for _ in range(warmup):
+        ea.bwd(q, k, v, o, lse, ddo, **kw)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(steps):
+        ea.bwd(q, k, v, o, lse, ddo, **kw)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps, outs
+
+
+def bwd_spot_check(shape, words, do_words, outs, head=0):
+    """dQ, dK, dV, D_i of one head against the oracle (relative to each tensor's max)."""
+    import oracle
+    B, H, S, D, dtype, causal = shape
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    b, h = divmod(head, H)
+    sl = lambda a: np.ascontiguousarray(a[b:b + 1, h:h + 1])  # noqa: E731
+    ref = oracle.attn_bwd(*(sl(x) for x in words), sl(do_words), dtype, scale, causal)
+    got = [sl(t.float().cpu().numpy().astype(np.float64)) for t in outs]
+    u = 2.0 ** -11 if dtype == "fp16" else 2.0 ** -8
+    errs = {n: float(np.abs(g - r).max() / max(1.0, np.abs(r).max()))
+            for n, g, r in zip(("dq", "dk", "dv", "delta"), got, ref)}
+    return {"head": head, "rel_err": errs, "tol": 4 * u, "ok": all(e <= 4 * u for e in errs.values())}
+
+
 def reference_gemm(n, steps=50):
     """Context for the MFMA roofline: a plain fp16 n x n x n torch.matmul (the vendor
     GEMM library) on random N(0,1) data, timed back to back like the attention launches.
@@ -185,6 +242,7 @@ def main():
     ap.add_argument("--no-others", action="store_true", help="skip timing the other workloads")
     ap.add_argument("--ref-gemm", type=int, default=8192,
                     help="also time an fp16 N^3 torch.matmul as context for the MFMA roofline (0: skip)")
+    ap.add_argument("--no-backward", action="store_true", help="skip timing attn_bwd")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one element-wise add reading and writing this many MiB "
                          "(calibrates the HBM byte counters)")
@@ -227,6 +285,19 @@ def main():
     parity = parity_spot_check(shape, words, o, lse)
     print(f"# parity spot check: {parity}", file=sys.stderr, flush=True)
 
+    backward = None
+    if not args.no_backward:
+        do_words, ddo = make_do(shape)
+        ms_b, outs = time_backward(ea, shape, dev, ddo, max(5, args.steps // 2), max(2, args.warmup // 2))
+        conv = bwd_flops(B, H, S, D, causal) / (ms_b * 1e-3) / 1e12
+        executed = bwd_flops(B, H, S, D, causal, gemms=7) / (ms_b * 1e-3) / 1e12
+        backward = {"workload": args.workload, "us_per_call": round(ms_b * 1e3, 2),
+                    "tflops": round(conv, 1), "frac_of_peak": round(conv / PEAK_TFLOPS, 4),
+                    "executed_tflops": round(executed, 1),
+                    "parity_spot_check": bwd_spot_check(shape, words, do_words, outs)}
+        print(f"# backward: {backward}", file=sys.stderr, flush=True)
+        del outs, ddo
+
     others = {}
     if not args.no_others:
         for name in inputs.WORKLOADS:
@@ -238,6 +309,13 @@ def main():
             others[name] = {"us_per_call": round(ms_k * 1e3, 2),
                             "tflops": round(fl / (ms_k * 1e-3) / 1e12, 1),
                             "frac_of_peak": round(fl / (ms_k * 1e-3) / 1e12 / PEAK_TFLOPS, 4)}
+            if not args.no_backward:
+                _, ddo = make_do(shp)
+                ms_b, _ = time_backward(ea, shp, dv, ddo, max(5, args.steps // 5), 2)
+                flb = bwd_flops(shp[0], shp[1], shp[2], shp[3], shp[5])
+                others[name]["bwd_us_per_call"] = round(ms_b * 1e3, 2)
+                others[name]["bwd_tflops"] = round(flb / (ms_b * 1e-3) / 1e12, 1)
+                del ddo
             print(f"# {name}: {others[name]}", file=sys.stderr, flush=True)
             del dv
             torch.cuda.empty_cache()
@@ -272,6 +350,7 @@ def main():
                      "algorithmic_min_hbm_bytes": min_bytes(B, H, S, D)},
         "cpu_baseline": cpu,
         "parity_spot_check": parity,
+        "backward": backward,
         "other_workloads": others,
         "reference_gemm": gemm,
     }

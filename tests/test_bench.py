@@ -36,3 +36,10 @@ def test_traffic_is_used_only_for_the_profiled_kernel_source(tmp_path, monkeypat
     assert bench.read_traffic() is None  # taken on another kernel source
     f.write_text(f"kernel_source_sha256_16: {bench.kernel_source_hash()}\nhbm_bytes_per_launch: 123456\n")
     assert bench.read_traffic() == pytest.approx(123456.0)
+
+
+def test_backward_flop_convention():
+    # five S x S x D GEMMs (2 flops per multiply-add), halved when causal; the
+    # kernels execute seven (dQ recomputes S and dP)
+    assert bench.bwd_flops(2, 16, 4096, 128, False) == 10.0 * 2 * 16 * 4096 ** 2 * 128
+    assert bench.bwd_flops(2, 16, 4096, 128, True, gemms=7) == 7.0 * 2 * 16 * 4096 ** 2 * 128
