@@ -17,6 +17,11 @@ on the same inputs, with the forward's O and LSE: TFLOP/s at the usual
 10*B*H*S^2*D (five S x S x D GEMMs, halved when causal) and at the 14*B*H*S^2*D
 the kernels execute (the dQ kernel recomputes S and dP), plus a parity spot
 check of one head against the oracle.
+
+The `unfused` object times the comparator attn_fwd_unfused (S = scale Q K^T
+written to HBM in fp32, a row softmax writing P, then O = P V) on the same
+inputs, with the HBM bytes it must move at least and its speed against the
+fused kernel.
 """
 from __future__ import annotations
 
@@ -163,6 +168,35 @@ def bwd_spot_check(shape, words, do_words, outs, head=0):
     return {"head": head, "rel_err": errs, "tol": 4 * u, "ok": all(e <= 4 * u for e in errs.values())}
 
 
+def unfused_bytes(B, H, S, D):
+    """HBM bytes the unfused path moves at least: Q, K, V read, S written and
+    read (fp32), P written and read (16-bit), the fp32 O before normalisation
+    and the per-row factors written and read, O and LSE written."""
+    return min_bytes(B, H, S, D) + B * H * S * S * (4 + 4 + 2 + 2) + B * H * S * (D + 1) * 4 * 2
+
+
+def time_unfused(ea, shape, dev, steps, warmup):
+    import torch
+    B, H, S, D, dtype, causal = shape
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    q, k, v = dev
+    stream = torch.cuda.current_stream()
+    ws = torch.empty(ea.attn_fwd_unfused_workspace_bytes(B, H, S, D), dtype=torch.uint8, device=q.device)
+    o, lse = ea.fwd_unfused(q, k, v, scale=scale, causal=causal, workspace=ws, stream=stream)
+    for _ in range(warmup):
+        ea.fwd_unfused(q, k, v, scale=scale, causal=causal, out=o, lse=lse, workspace=ws, stream=stream)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(steps):
+        ea.fwd_unfused(q, k, v, scale=scale, causal=causal, out=o, lse=lse, workspace=ws, stream=stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    del ws
+    torch.cuda.empty_cache()
+    return t0.elapsed_time(t1) / steps, o, lse
+
+
 def reference_gemm(n, steps=50):
     """Context for the MFMA roofline: a plain fp16 n x n x n torch.matmul (the vendor
     GEMM library) on random N(0,1) data, timed back to back like the attention launches.
@@ -243,6 +277,7 @@ def main():
     ap.add_argument("--ref-gemm", type=int, default=8192,
                     help="also time an fp16 N^3 torch.matmul as context for the MFMA roofline (0: skip)")
     ap.add_argument("--no-backward", action="store_true", help="skip timing attn_bwd")
+    ap.add_argument("--no-unfused", action="store_true", help="skip timing the unfused comparator")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one element-wise add reading and writing this many MiB "
                          "(calibrates the HBM byte counters)")
@@ -298,6 +333,19 @@ def main():
         print(f"# backward: {backward}", file=sys.stderr, flush=True)
         del outs, ddo
 
+    unfused = None
+    if not args.no_unfused:
+        ms_u, o_u, lse_u = time_unfused(ea, shape, dev, max(5, args.steps // 5), 2)
+        nb = unfused_bytes(B, H, S, D)
+        unfused = {"workload": args.workload, "us_per_call": round(ms_u * 1e3, 2),
+                   "tflops": round(f / (ms_u * 1e-3) / 1e12, 1),
+                   "hbm_bytes_min": nb, "hbm_bound_us": round(nb / 8e12 * 1e6, 1),
+                   "achieved_gbps_of_min": round(nb / (ms_u * 1e-3) / 1e9, 1),
+                   "fused_speedup": round(ms_u / ms_kernel, 2),
+                   "parity_spot_check": parity_spot_check(shape, words, o_u, lse_u)}
+        print(f"# unfused comparator: {unfused}", file=sys.stderr, flush=True)
+        del o_u, lse_u
+
     others = {}
     if not args.no_others:
         for name in inputs.WORKLOADS:
@@ -351,6 +399,7 @@ def main():
         "cpu_baseline": cpu,
         "parity_spot_check": parity,
         "backward": backward,
+        "unfused": unfused,
         "other_workloads": others,
         "reference_gemm": gemm,
     }

@@ -16,12 +16,14 @@ import math
 from . import _lib
 from ._lib import ATTN_BF16, ATTN_F16, AttnError  # noqa: F401
 
-__all__ = ["fwd", "bwd", "attn_fwd", "attn_fwd_strided", "attn_bwd", "attn_fwd_plan",
-           "attn_fwd_workgroup_tile", "AttnError"]
+__all__ = ["fwd", "bwd", "fwd_unfused", "attn_fwd", "attn_fwd_strided", "attn_bwd", "attn_fwd_unfused",
+           "attn_fwd_unfused_workspace_bytes", "attn_fwd_plan", "attn_fwd_workgroup_tile", "AttnError"]
 
 attn_fwd = _lib.attn_fwd
 attn_fwd_strided = _lib.attn_fwd_strided
 attn_bwd = _lib.attn_bwd
+attn_fwd_unfused = _lib.attn_fwd_unfused
+attn_fwd_unfused_workspace_bytes = _lib.attn_fwd_unfused_workspace_bytes
 attn_fwd_plan = _lib.attn_fwd_plan
 attn_fwd_workgroup_tile = _lib.attn_fwd_workgroup_tile
 
@@ -127,3 +129,40 @@ def bwd(q, k, v, o, lse, do, scale=None, causal=False, dq=None, dk=None, dv=None
                            B, H, Sq, Skv, D, scale, causal, dt, stream.cuda_stream)
     _lib.check(st)
     return dq, dk, dv, delta
+
+
+def fwd_unfused(q, k, v, scale=None, causal=False, out=None, lse=None, workspace=None, stream=None):
+    """The unfused comparator of ``fwd``: S = scale Q K^T in HBM (fp32), a row
+    softmax writing P, then O = P V.  q, k, v contiguous [B,H,S,D] of one
+    dtype.  ``workspace`` (a uint8 CUDA tensor of at least
+    ``attn_fwd_unfused_workspace_bytes(B, H, S, D)`` bytes) may be passed in.
+    Returns (o, lse)."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dim() != 4 or not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be a contiguous 4-D GPU tensor of q's dtype")
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [B,H,S,D] shape")
+    B, H, S, D = q.shape
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device) if lse is None else lse
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be contiguous [B,H,S,D] in the input dtype")
+    if lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B,H,S] tensor")
+    need = _lib.attn_fwd_unfused_workspace_bytes(B, H, S, D)
+    if need < 0:
+        raise ValueError("shape too large for the unfused path")
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        st = _lib.attn_fwd_unfused(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                   workspace.data_ptr(), workspace.numel() * workspace.element_size(), B, H, S,
+                                   D, scale, causal, dt, stream.cuda_stream)
+    _lib.check(st)
+    return out, lse

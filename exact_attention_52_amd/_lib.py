@@ -7,7 +7,7 @@ import ctypes
 import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 ATTN_F16, ATTN_BF16 = 0, 1
 STATUS = {
@@ -16,7 +16,8 @@ STATUS = {
     5: "ATTN_ERR_MISALIGNED", 6: "ATTN_ERR_BAD_SCALE", 7: "ATTN_ERR_ALIASING",
     8: "ATTN_ERR_UNSUPPORTED_DEVICE", 9: "ATTN_ERR_LAUNCH", 10: "ATTN_ERR_BAD_ARGUMENT",
 }
-EXPORTS = ("attn_fwd", "attn_fwd_strided", "attn_bwd", "attn_fwd_plan", "attn_fwd_workgroup_tile",
+EXPORTS = ("attn_fwd", "attn_fwd_strided", "attn_bwd", "attn_fwd_unfused",
+           "attn_fwd_unfused_workspace_bytes", "attn_fwd_plan", "attn_fwd_workgroup_tile",
            "attn_status_string", "attn_last_error", "attn_abi_version")
 
 
@@ -58,6 +59,10 @@ def load():
     lib.attn_fwd_strided.restype = ci
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, cf, ci, ci, vp]
     lib.attn_bwd.restype = ci
+    lib.attn_fwd_unfused.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, cf, ci, ci, vp]
+    lib.attn_fwd_unfused.restype = ci
+    lib.attn_fwd_unfused_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    lib.attn_fwd_unfused_workspace_bytes.restype = i64
     lib.attn_fwd_plan.argtypes = [i64, i64, i64, i64, ci, ci, ctypes.POINTER(Plan)]
     lib.attn_fwd_plan.restype = ci
     lib.attn_fwd_workgroup_tile.argtypes = [i64, i64, i64, i64, ci, ci, i64,
@@ -120,6 +125,17 @@ def attn_bwd(q: int, k: int, v: int, o: int, lse: int, do: int, dq: int, dk: int
     """Raw call: device pointers as ints; returns the status code."""
     return load().attn_bwd(q, k, v, o, lse, do, dq, dk, dv, delta, B, H, Sq, Skv, D, float(scale),
                            int(bool(causal)), int(dtype), stream)
+
+
+def attn_fwd_unfused(q: int, k: int, v: int, o: int, lse: int, workspace: int, workspace_bytes: int, B: int,
+                     H: int, S: int, D: int, scale: float, causal: bool, dtype: int, stream: int) -> int:
+    """Raw call: device pointers as ints; returns the status code."""
+    return load().attn_fwd_unfused(q, k, v, o, lse, workspace, workspace_bytes, B, H, S, D, float(scale),
+                                   int(bool(causal)), int(dtype), stream)
+
+
+def attn_fwd_unfused_workspace_bytes(B: int, H: int, S: int, D: int) -> int:
+    return int(load().attn_fwd_unfused_workspace_bytes(B, H, S, D))
 
 
 def attn_fwd_plan(B: int, H: int, S: int, D: int, causal: bool, dtype: int) -> dict:

@@ -13,9 +13,11 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = [os.path.join(CSRC, "attn_api.hip"), os.path.join(CSRC, "attn_bwd.hip")]
+SOURCES = [os.path.join(CSRC, "attn_api.hip"), os.path.join(CSRC, "attn_bwd.hip"),
+           os.path.join(CSRC, "attn_unfused.hip")]
 HEADERS = [os.path.join(CSRC, "attn_fwd_kernel.hpp"), os.path.join(CSRC, "attn_bwd_kernel.hpp"),
-           os.path.join(CSRC, "attn_bwd.hpp"), os.path.join(INCLUDE, "attn.h")]
+           os.path.join(CSRC, "attn_bwd.hpp"), os.path.join(CSRC, "attn_unfused.hpp"),
+           os.path.join(INCLUDE, "attn.h")]
 
 FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",
@@ -33,7 +35,10 @@ FLAGS = [
 SOURCE_FLAGS = {
     "attn_api.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form=1"],
     "attn_bwd.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form=1"],
+    "attn_unfused.hip": [],
 }
+# the unfused comparator's GEMMs are the vendor library's
+LINK_LIBS = ["-L/opt/rocm/lib", "-lrocblas"]
 
 
 def _run(cmd):
@@ -57,7 +62,7 @@ def build(out: str = LIB, extra_flags=()) -> str:
             _run([HIPCC, *FLAGS, *SOURCE_FLAGS[os.path.basename(src)], *extra_flags,
                   "-I" + INCLUDE, "-I" + CSRC, "-c", "-o", obj, src])
             objs.append(obj)
-        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs, *LINK_LIBS])
     os.replace(tmp, out)
     return out
 

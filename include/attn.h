@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 2
+#define ATTN_ABI_VERSION 3
 
 /* Element type of Q, K, V and O.  The page restricts the float type to F16 or
  * BF16 (validate_config, "float_type must be F16 or BF16"). */
@@ -154,6 +154,40 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
              const float* lse, const void* dO, void* dq, void* dk, void* dv,
              float* delta, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
              int64_t D, float scale, int causal, int dtype, void* stream);
+
+/*
+ * attn_fwd_unfused -- the same forward as attn_fwd, unfused: a comparator
+ * that shows the HBM traffic the fused kernels avoid.
+ *
+ * Steps: S = scale Q K^T as fp32 into the workspace (vendor strided-batched
+ * GEMM over the B*H heads, the batched 4-D GEMM of the docs.rs page
+ * "aprender-train 0.36.0, entrenar/autograd/cuda_forward/matmul.rs",
+ * batched_4d_gemm_forward); a row softmax kernel writing P in `dtype` and
+ * unnormalised P rounded to `dtype`, LSE and 1 / (sum of the rounded P); O =
+ * P V (vendor GEMM, fp32 accumulation), then scaled by that factor and
+ * rounded (the fused kernels normalise the same way).  Per head S*S*12 bytes
+ * go through HBM.
+ *
+ *   q, k, v, o, lse, B, H, S, D, scale, causal, dtype, stream: as attn_fwd.
+ *   workspace        device memory of at least
+ *                    attn_fwd_unfused_workspace_bytes(B, H, S, D) bytes,
+ *                    16-byte aligned, owned by the caller, overwritten; must
+ *                    not overlap q, k, v, o or lse.
+ *   workspace_bytes  its size.
+ * Returns as attn_fwd; ATTN_ERR_BAD_ARGUMENT if the workspace is too small.
+ * Not reentrant per device (a vendor-library handle per device is shared and
+ * created on first use, outside the caller's control of allocation).
+ */
+int attn_fwd_unfused(const void* q, const void* k, const void* v, void* o,
+                     float* lse, void* workspace, int64_t workspace_bytes,
+                     int64_t B, int64_t H, int64_t S, int64_t D, float scale,
+                     int causal, int dtype, void* stream);
+
+/* Workspace bytes attn_fwd_unfused needs (per head S rows of fp32 scores
+ * and of 16-bit probabilities, rows padded to 16 bytes, plus the fp32 output
+ * before normalisation and one fp32 factor per row); -1 for negative or
+ * overflowing sizes or an unsupported head dim. */
+int64_t attn_fwd_unfused_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t D);
 
 /*
  * attn_fwd_plan -- the launch geometry attn_fwd would use (host only, no HIP

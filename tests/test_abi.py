@@ -307,3 +307,48 @@ def test_bwd_null_tensors_without_elements_reach_the_device_check():
     assert bcall(Sq=0, q=0, o=0, lse=0, do=0, dq=0, delta=0) == 8, _lib.last_error()
     assert bcall(Skv=0, k=0, v=0, dk=0, dv=0) == 8, _lib.last_error()
     assert bcall(k=FAKE, v=FAKE, q=FAKE, o=FAKE, do=FAKE) == 8, _lib.last_error()  # inputs may alias
+
+
+# --------------------------------------------------------------------------
+# attn_fwd_unfused (the comparator): workspace size and argument checks
+# --------------------------------------------------------------------------
+def test_unfused_workspace_bytes():
+    # per head S rows of fp32 padded to 4 elements, then (256-byte aligned)
+    # S rows of 16-bit padded to 8, then (aligned) the fp32 O and one fp32 per row
+    p_end = 512 + 2 * 5 * 8 * 2
+    o_off = (p_end + 255) // 256 * 256
+    assert _lib.attn_fwd_unfused_workspace_bytes(1, 2, 5, 64) == o_off + 2 * 5 * 64 * 4 + 2 * 5 * 4
+    n = 2 * 16 * 4096
+    assert _lib.attn_fwd_unfused_workspace_bytes(2, 16, 4096, 128) == n * 4096 * 6 + n * 128 * 4 + n * 4
+    assert _lib.attn_fwd_unfused_workspace_bytes(0, 2, 5, 64) == 0
+    assert _lib.attn_fwd_unfused_workspace_bytes(-1, 2, 5, 64) == -1
+    assert _lib.attn_fwd_unfused_workspace_bytes(1, 2, 5, 96) == -1
+    assert _lib.attn_fwd_unfused_workspace_bytes(1 << 40, 1 << 10, 1 << 20, 64) == -1
+
+
+def ucall(q=FAKE, k=FAKE + MB_, v=FAKE + 2 * MB_, o=FAKE + 3 * MB_, lse=FAKE + 4 * MB_, ws=FAKE + 16 * MB_,
+          wsb=1 << 20, B=1, H=2, S=16, D=64, scale=0.125, causal=0, dtype=0):
+    return _lib.attn_fwd_unfused(q, k, v, o, lse, ws, wsb, B, H, S, D, scale, causal, dtype, 0)
+
+
+@pytest.mark.parametrize("kwargs,status,word", [
+    (dict(S=-2), 2, ">= 0"),
+    (dict(D=48), 3, "head_dim"),
+    (dict(ws=0), 1, "NULL"),
+    (dict(ws=FAKE + 16 * MB_ + 8), 5, "16-byte"),
+    (dict(wsb=100), 10, "needed"),
+    (dict(ws=FAKE + 3 * MB_), 7, "workspace overlaps"),
+    (dict(o=FAKE + 64), 7, "o overlaps"),
+])
+def test_unfused_invalid_arguments_rejected_before_launch(kwargs, status, word):
+    st = ucall(**kwargs)
+    assert st == status, (st, _lib.last_error())
+    assert word.lower() in _lib.last_error().lower()
+
+
+def test_unfused_valid_call_reaches_the_device_check():
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("would launch on a real GPU with fake pointers")
+    assert ucall() == 8, _lib.last_error()
+    assert ucall(B=0, q=0, k=0, v=0, o=0, lse=0, ws=0, wsb=0) == 0

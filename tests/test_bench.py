@@ -43,3 +43,11 @@ def test_backward_flop_convention():
     # kernels execute seven (dQ recomputes S and dP)
     assert bench.bwd_flops(2, 16, 4096, 128, False) == 10.0 * 2 * 16 * 4096 ** 2 * 128
     assert bench.bwd_flops(2, 16, 4096, 128, True, gemms=7) == 7.0 * 2 * 16 * 4096 ** 2 * 128
+
+
+def test_unfused_byte_convention():
+    # the fused minimum plus S written and read in fp32, P written and read in
+    # 16 bits, and the fp32 O and row factors written and read
+    n = 2 * 16 * 4096
+    assert bench.unfused_bytes(2, 16, 4096, 128) == (bench.min_bytes(2, 16, 4096, 128) + n * 4096 * 12
+                                                     + n * 129 * 8)
