@@ -16,12 +16,14 @@ import math
 from . import _lib
 from ._lib import ATTN_BF16, ATTN_F16, AttnError  # noqa: F401
 
-__all__ = ["fwd", "bwd", "fwd_unfused", "attn_fwd", "attn_fwd_strided", "attn_bwd", "attn_fwd_unfused",
+__all__ = ["fwd", "bwd", "fwd_unfused", "fwd_variant", "attn_fwd", "attn_fwd_strided", "attn_fwd_variant",
+           "attn_bwd", "attn_fwd_unfused",
            "attn_fwd_unfused_workspace_bytes", "attn_fwd_plan", "attn_fwd_workgroup_tile", "AttnError"]
 
 attn_fwd = _lib.attn_fwd
 attn_fwd_strided = _lib.attn_fwd_strided
 attn_bwd = _lib.attn_bwd
+attn_fwd_variant = _lib.attn_fwd_variant
 attn_fwd_unfused = _lib.attn_fwd_unfused
 attn_fwd_unfused_workspace_bytes = _lib.attn_fwd_unfused_workspace_bytes
 attn_fwd_plan = _lib.attn_fwd_plan
@@ -164,5 +166,32 @@ def fwd_unfused(q, k, v, scale=None, causal=False, out=None, lse=None, workspace
         st = _lib.attn_fwd_unfused(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                    workspace.data_ptr(), workspace.numel() * workspace.element_size(), B, H, S,
                                    D, scale, causal, dt, stream.cuda_stream)
+    _lib.check(st)
+    return out, lse
+
+
+def fwd_variant(q, k, v, variant, scale=None, causal=False, out=None, lse=None, stream=None):
+    """``fwd`` on contiguous [B,H,S,D] tensors with copy schedule ``variant``
+    (0: shipped; 1/2/3: K/V LDS stages; 4: 2 stages plus a producer wave).
+    Returns (o, lse)."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dim() != 4 or not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype or t.shape != q.shape:
+            raise ValueError(f"{name} must be a contiguous [B,H,S,D] GPU tensor like q")
+    B, H, S, D = q.shape
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device) if lse is None else lse
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be contiguous [B,H,S,D] in the input dtype")
+    if lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B,H,S] tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        st = _lib.attn_fwd_variant(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                   B, H, S, D, scale, causal, dt, int(variant), stream.cuda_stream)
     _lib.check(st)
     return out, lse

@@ -14,9 +14,10 @@ LIB = os.path.join(PKG, "libattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = [os.path.join(CSRC, "attn_api.hip"), os.path.join(CSRC, "attn_bwd.hip"),
-           os.path.join(CSRC, "attn_unfused.hip")]
+           os.path.join(CSRC, "attn_unfused.hip"), os.path.join(CSRC, "attn_variants.hip")]
 HEADERS = [os.path.join(CSRC, "attn_fwd_kernel.hpp"), os.path.join(CSRC, "attn_bwd_kernel.hpp"),
            os.path.join(CSRC, "attn_bwd.hpp"), os.path.join(CSRC, "attn_unfused.hpp"),
+           os.path.join(CSRC, "attn_variants.hpp"),
            os.path.join(INCLUDE, "attn.h")]
 
 FLAGS = [
@@ -36,6 +37,7 @@ SOURCE_FLAGS = {
     "attn_api.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form=1"],
     "attn_bwd.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form=1"],
     "attn_unfused.hip": [],
+    "attn_variants.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form=1"],
 }
 # the unfused comparator's GEMMs are the vendor library's
 LINK_LIBS = ["-L/opt/rocm/lib", "-lrocblas"]

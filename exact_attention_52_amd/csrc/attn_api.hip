@@ -20,6 +20,7 @@
 #include "attn_bwd.hpp"
 #include "attn_fwd_kernel.hpp"
 #include "attn_unfused.hpp"
+#include "attn_variants.hpp"
 
 namespace {
 
@@ -215,7 +216,7 @@ bool self_disjoint(const View& t, int64_t B, int64_t H, int64_t D) {
 
 int run(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t Sq,
         int64_t Skv, int64_t D, View vq, View vk, View vv, View vo, float scale, int causal, int dtype,
-        void* stream) {
+        void* stream, int variant = 0) {
   if (B < 0 || H < 0 || Sq < 0 || Skv < 0)
     return fail(ATTN_ERR_BAD_SHAPE, "B, H, Sq and Skv must be >= 0 (got B=%lld H=%lld Sq=%lld Skv=%lld)",
                 (long long)B, (long long)H, (long long)Sq, (long long)Skv);
@@ -264,6 +265,12 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int64_
   pr.c = c;
   hipStream_t hs = (hipStream_t)stream;
   const bool cz = causal != 0;
+  if (variant != 0) {
+    pr.G = B * H;  // the variant sets its own tile count and grid from B*H
+    const hipError_t e = attn::variant_launch(pr, (int)D, cz, dtype, variant, hs);
+    if (e != hipSuccess) return fail(ATTN_ERR_LAUNCH, "variant %d launch failed: %s", variant, hipGetErrorString(e));
+    return ok();
+  }
   switch (D) {
     case 64: return dispatch<Cfg64>(pr, cz, dtype, hs);
     case 128: return dispatch<Cfg128>(pr, cz, dtype, hs);
@@ -285,6 +292,23 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   View vq = c4, vk = c4, vv = c4, vo = c4;
   vk.name = "k", vv.name = "v", vo.name = "o";
   return run(q, k, v, o, lse, B, H, S, S, D, vq, vk, vv, vo, scale, causal, dtype, stream);
+}
+
+int attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                     int64_t S, int64_t D, float scale, int causal, int dtype, int variant, void* stream) {
+  const int st = check_sizes(B, H, S, D, dtype);
+  if (st != ATTN_OK) return st;
+  if (variant < 0 || variant >= attn::kNumVariants || (variant > 0 && attn::variant_block_m((int)D, variant) == 0))
+    return fail(ATTN_ERR_BAD_ARGUMENT, "variant %d not available for head_dim %lld (0..%d for D 64 and 128, 0 for 256)",
+                variant, (long long)D, attn::kNumVariants - 1);
+  if (variant > 0 && B * H * ((S + attn::variant_block_m((int)D, variant) - 1) / attn::variant_block_m((int)D, variant)) >
+                         0x7FFFFFFF)
+    return fail(ATTN_ERR_BAD_SHAPE, "grid exceeds the launch limit");
+  const int64_t sh = S * D, sb = H * S * D;
+  const View c4 = {nullptr, sb, sh, D, S, "q"};
+  View vq = c4, vk = c4, vv = c4, vo = c4;
+  vk.name = "k", vv.name = "v", vo.name = "o";
+  return run(q, k, v, o, lse, B, H, S, S, D, vq, vk, vv, vo, scale, causal, dtype, stream, variant);
 }
 
 int attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,

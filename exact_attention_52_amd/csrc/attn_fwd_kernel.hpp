@@ -109,17 +109,22 @@ struct Elem<DT_BF16> {
 //   V: line L of a 4-line block holds rows L, L+4, ... (pad 64 B), so the 4
 //      consecutive rows of a transposing read, 64 bytes wide across two
 //      16-lane groups, sit 64 bytes apart modulo 256.
-template <int D_, int QW_, int KW_, int BN_, bool PINGPONG_ = false, bool STAGGER_ = false>
+template <int D_, int QW_, int KW_, int BN_, bool PINGPONG_ = false, bool STAGGER_ = false, int STAGES_ = 2,
+          bool PRODUCER_ = false>
 struct TileCfg {
   static constexpr bool PINGPONG = PINGPONG_;  // use the two-group ping-pong kernel
   static constexpr bool STAGGER = STAGGER_;    // kernel 1: staggered K/V copies, two barriers per tile
+  // kernel 1 without STAGGER: LDS stages of K/V (1, 2 or 3), and whether one
+  // extra wave issues every HBM -> LDS copy while the others only compute
+  static constexpr int STAGES = STAGES_;
+  static constexpr bool PRODUCER = PRODUCER_;
   static constexpr int D = D_;
   static constexpr int QW = QW_;             // waves along query rows
   static constexpr int KW = KW_;             // waves along each key tile
   static constexpr int BN = BN_;             // keys per tile
   static constexpr int BM = 32 * QW;         // query rows per workgroup
-  static constexpr int NW = QW * KW;         // waves per workgroup
-  static constexpr int NT = 64 * NW;         // threads per workgroup
+  static constexpr int NW = QW * KW;         // computing waves per workgroup
+  static constexpr int NT = 64 * (NW + (PRODUCER ? 1 : 0));  // threads per workgroup
   static constexpr int KSUB = BN / KW;       // keys per wave per tile
   static constexpr int NB = KSUB / 32;       // 32-key blocks per wave per tile
   static constexpr int DK = D / 16;          // k-steps of the score MFMA
@@ -131,7 +136,6 @@ struct TileCfg {
   static constexpr int V_LINE = 1024 + 64;
   static constexpr int K_TILE = LINES * K_LINE;
   static constexpr int V_TILE = LINES * V_LINE;
-  static constexpr int STAGES = 2;
   static constexpr int KV_LDS_BYTES = STAGES * (K_TILE + V_TILE);
   static constexpr int LOADS_PER_WAVE = LINES / NW;      // K lines (and V lines) per wave
   static constexpr int LDS_BYTES = KV_LDS_BYTES;
@@ -152,6 +156,9 @@ struct TileCfg {
   static_assert(BN % (16 * RPL) == 0, "tile must hold whole K line blocks");
   static_assert(LINES % NW == 0, "load lines must split evenly over the waves");
   static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per CU");
+  static_assert(STAGES >= 1 && STAGES <= 3, "1 to 3 K/V stages");
+  static_assert(STAGES == 2 || (!PINGPONG && !STAGGER), "the ping-pong and staggered schedules use 2 stages");
+  static_assert(!PRODUCER || (!PINGPONG && !STAGGER && KW == 1), "a producer wave only in kernel 1, KW = 1");
 };
 
 typedef short s16x4 __attribute__((vector_size(8)));
@@ -681,14 +688,18 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(const Problem p) {
   // one array per stage and operand, so that the compiler can tell reads of
   // one stage from the asynchronous HBM->LDS copies into the other
   __shared__ __attribute__((aligned(1024))) uint8_t kt0[C::K_TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t kt1[C::K_TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t kt1[C::STAGES >= 2 ? C::K_TILE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t kt2[C::STAGES >= 3 ? C::K_TILE : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t vt0[C::V_TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t vt1[C::V_TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vt1[C::STAGES >= 2 ? C::V_TILE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t vt2[C::STAGES >= 3 ? C::V_TILE : 16];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int qw = wave % C::QW;
   const int kw = wave / C::QW;
+  // the copying wave of a PRODUCER workgroup (wave NW) computes nothing
+  const bool producer = C::PRODUCER && wave == C::NW;
 
   int64_t tile64, bh64;
   workgroup_tile(blockIdx.x, p.G, p.nq, CAUSAL, &tile64, &bh64);
@@ -696,7 +707,7 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(const Problem p) {
   const HeadView hv = head_view(p, bh64);
 
   Wave<C, CAUSAL, DT> w;
-  w.init(hv, q0 + qw * 32, kw * C::KSUB, p.c);
+  if (!producer) w.init(hv, q0 + qw * 32, kw * C::KSUB, p.c);
 
   // key tiles this workgroup needs (none when causal leaves its rows no key)
   const int q_end = (q0 + BM < hv.Sq) ? q0 + BM : hv.Sq;
@@ -704,7 +715,7 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(const Problem p) {
                             : hv.Skv;
   const int n = (kv_end + BN - 1) / BN;
   if (n == 0) {  // uniform over the workgroup
-    w.epilogue(hv);
+    if (!producer) w.epilogue(hv);
     return;
   }
 
@@ -761,30 +772,77 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(const Problem p) {
       if (j + 1 < n) iter(j + 1, kt1, vt1, vt0);
     }
   } else {
-    auto fetch = [&](int j, uint8_t* kt, uint8_t* vt) __attribute__((always_inline)) {
-      const auto ck = k_copier(j, kt);
-      const auto cv = v_copier(j, vt);
+    // copies of tile t (empty past the last tile) into (kt, vt): LPW lines of
+    // K and of V per wave, or all of them by the producer wave
+    constexpr int CPT = C::PRODUCER ? 2 * C::LINES : 2 * LPW;  // copy instructions per tile, copying wave
+    auto fetch = [&](int t, uint8_t* kt, uint8_t* vt) __attribute__((always_inline)) {
+      if constexpr (C::PRODUCER) {
+        if (!producer) return;
+        const auto ck = k_copier(t, kt);
+        const auto cv = v_copier(t, vt);
+        // the copiers address line wave * LPW + i, and the producer is wave NW
 #pragma unroll
-      for (int i = 0; i < LPW; ++i) ck(i), cv(i);
+        for (int i = 0; i < C::LINES; ++i) ck(i - C::NW * LPW), cv(i - C::NW * LPW);
+      } else {
+        const auto ck = k_copier(t, kt);
+        const auto cv = v_copier(t, vt);
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) ck(i), cv(i);
+      }
     };
     auto compute = [&](int j, const uint8_t* kt, const uint8_t* vt) __attribute__((always_inline)) {
-      if (!w.active(j)) return;
+      if (producer || !w.active(j)) return;
       w.qk(kt);
       w.softmax(j);
       w.pv(vt);
     };
-    fetch(0, kt0, vt0);
-    __syncthreads();
-    for (int j = 0; j < n; j += 2) {
-      if (j + 1 < n) fetch(j + 1, kt1, vt1);
-      compute(j, kt0, vt0);
-      __syncthreads();
-      if (j + 1 < n) {
-        if (j + 2 < n) fetch(j + 2, kt0, vt0);
-        compute(j + 1, kt1, vt1);
+    if constexpr (C::STAGES == 1) {
+      // copy, wait, compute, and wait until every wave is done reading
+      for (int j = 0; j < n; ++j) {
+        fetch(j, kt0, vt0);
+        __syncthreads();
+        compute(j, kt0, vt0);
         __syncthreads();
       }
+    } else if constexpr (C::STAGES == 2) {
+      // tile j+1 is copied while tile j is computed; one barrier per tile
+      fetch(0, kt0, vt0);
+      __syncthreads();
+      for (int j = 0; j < n; j += 2) {
+        if (j + 1 < n) fetch(j + 1, kt1, vt1);
+        compute(j, kt0, vt0);
+        __syncthreads();
+        if (j + 1 < n) {
+          if (j + 2 < n) fetch(j + 2, kt0, vt0);
+          compute(j + 1, kt1, vt1);
+          __syncthreads();
+        }
+      }
+    } else {
+      // tile j+2 is copied while tile j is computed, so every copy has two
+      // tiles' time to land; the counted wait lets tile j+2's copies stay in
+      // flight (tiles past the end are empty copies, so the count is uniform)
+      fetch(0, kt0, vt0);
+      fetch(1, kt1, vt1);
+      wait_loads_but<CPT>();
+      barrier_keep_loads();
+      auto step = [&](int j, const uint8_t* kt, const uint8_t* vt, uint8_t* kn, uint8_t* vn)
+                      __attribute__((always_inline)) {
+        fetch(j + 2, kn, vn);
+        compute(j, kt, vt);
+        wait_loads_but<CPT>();  // tile j+1 landed
+        barrier_keep_loads();
+      };
+      for (int j = 0; j < n; j += 3) {
+        step(j, kt0, vt0, kt2, vt2);
+        if (j + 1 < n) step(j + 1, kt1, vt1, kt0, vt0);
+        if (j + 2 < n) step(j + 2, kt2, vt2, kt1, vt1);
+      }
     }
+  }
+  if (producer) {
+    wait_loads();
+    return;
   }
   wait_loads();  // the (empty) copies issued past the last tile
   // the key-split merge below reuses the V stages: every wave's copies must

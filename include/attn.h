@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 3
+#define ATTN_ABI_VERSION 4
 
 /* Element type of Q, K, V and O.  The page restricts the float type to F16 or
  * BF16 (validate_config, "float_type must be F16 or BF16"). */
@@ -154,6 +154,26 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
              const float* lse, const void* dO, void* dq, void* dk, void* dv,
              float* delta, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
              int64_t D, float scale, int causal, int dtype, void* stream);
+
+/*
+ * attn_fwd_variant -- attn_fwd with another copy schedule, for A/B
+ * measurements of the pipeline depth and of a producer/consumer wave split
+ * (the page's FlashAttention3Config makes pingpong_stages and
+ * num_producer_warps first-class knobs).  Arguments, checks, results
+ * contract and errors as attn_fwd; `variant`:
+ *   0  the shipped configuration (identical to attn_fwd)
+ *   1  1 K/V stage in LDS: copy tile j, wait, compute it
+ *   2  2 stages: tile j+1 copied while tile j is computed
+ *   3  3 stages: tile j+2 copied while tile j is computed
+ *   4  2 stages and one extra producer wave that issues every HBM -> LDS
+ *      copy while the other waves only compute
+ * Variants 1-4 exist for D = 64 (8 computing waves, 128-key tiles) and
+ * D = 128 (4 computing waves, 64-key tiles); others return
+ * ATTN_ERR_BAD_ARGUMENT.
+ */
+int attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int64_t B, int64_t H, int64_t S, int64_t D, float scale,
+                     int causal, int dtype, int variant, void* stream);
 
 /*
  * attn_fwd_unfused -- the same forward as attn_fwd, unfused: a comparator

@@ -352,3 +352,27 @@ def test_unfused_valid_call_reaches_the_device_check():
         pytest.skip("would launch on a real GPU with fake pointers")
     assert ucall() == 8, _lib.last_error()
     assert ucall(B=0, q=0, k=0, v=0, o=0, lse=0, ws=0, wsb=0) == 0
+
+
+# --------------------------------------------------------------------------
+# attn_fwd_variant: the A/B schedules
+# --------------------------------------------------------------------------
+def vcall(variant, D=64, B=1, H=2, S=16, q=FAKE, o=FAKE + 3 * MB_, lse=FAKE + 4 * MB_):
+    return _lib.attn_fwd_variant(q, q, q, o, lse, B, H, S, D, 0.125, 0, 0, variant, 0)
+
+
+@pytest.mark.parametrize("variant,D", [(-1, 64), (5, 64), (1, 256), (4, 256)])
+def test_variant_out_of_range(variant, D):
+    assert vcall(variant, D) == 10
+    assert "variant" in _lib.last_error()
+
+
+def test_variants_reach_the_device_check():
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("would launch on a real GPU with fake pointers")
+    for v in range(5):
+        for D in (64, 128):
+            assert vcall(v, D) == 8, _lib.last_error()
+    assert vcall(0, 256) == 8
+    assert vcall(3, 64, B=0) == 0  # empty
