@@ -850,12 +850,17 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(const Problem p) {
   if constexpr (C::KW > 1) __syncthreads();
 
   // merge the key-split waves (KW > 1): partials of wave (kw, qw), kw > 0,
-  // go to V stage (kw - 1) * QW + qw
+  // go to slot (kw - 1) * QW + qw: the V stages, then the K stages
   if constexpr (C::KW > 1) {
     constexpr int FIELDS = D / 2 + 3;
-    static_assert((C::KW - 1) * C::QW <= 2 && FIELDS * 64 * 4 <= C::V_TILE, "merge area too small");
+    static_assert((C::KW - 1) * C::QW <= 4 && FIELDS * 64 * 4 <= C::V_TILE &&
+                      ((C::KW - 1) * C::QW <= 2 || FIELDS * 64 * 4 <= C::K_TILE),
+                  "merge area too small");
+    auto slot = [&](int i) __attribute__((always_inline)) -> uint8_t* {
+      return i == 0 ? vt0 : i == 1 ? vt1 : i == 2 ? kt0 : kt1;
+    };
     if (kw > 0) {
-      float* dst = reinterpret_cast<float*>(((kw - 1) * C::QW + qw) == 0 ? vt0 : vt1);
+      float* dst = reinterpret_cast<float*>(slot((kw - 1) * C::QW + qw));
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -868,7 +873,7 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(const Problem p) {
     if (kw > 0) return;
 #pragma unroll
     for (int ww = 1; ww < C::KW; ++ww) {
-      const float* src = reinterpret_cast<const float*>(((ww - 1) * C::QW + qw) == 0 ? vt0 : vt1);
+      const float* src = reinterpret_cast<const float*>(slot((ww - 1) * C::QW + qw));
       const float lb = src[(D / 2) * 64 + lane];
       const float mb = src[(D / 2 + 1) * 64 + lane];
       const float lrb = src[(D / 2 + 2) * 64 + lane];
