@@ -61,6 +61,12 @@ def _load():
         lib.oracle_attn_bwd.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, i64, i64, dbl, ci,
                                         vp, vp, vp, vp]
         lib.oracle_attn_bwd.restype = ci
+        lib.oracle_attn_bwd_rows.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, i64, i64, dbl, ci,
+                                             vp, i64, vp, vp]
+        lib.oracle_attn_bwd_rows.restype = ci
+        lib.oracle_attn_bwd_keys.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, i64, i64, dbl, ci,
+                                             vp, i64, vp, vp]
+        lib.oracle_attn_bwd_keys.restype = ci
         lib.oracle_decode.argtypes = [vp, ci, i64, vp]
         lib.oracle_decode.restype = None
         lib.oracle_num_threads.argtypes = []
@@ -210,3 +216,39 @@ def attn_bwd(q, k, v, do, dtype: str, scale: float, causal: bool):
     if rc != 0:
         raise MemoryError("oracle scratch allocation failed")
     return dq, dk, dv, delta
+
+
+def attn_bwd_rows(q, k, v, do, dtype: str, scale: float, causal: bool, rows):
+    """dQ [n,D] and D_i [n] of sampled query rows (flat indices (b*H + h)*Sq + i)
+    of 16-bit inputs, in float64; each row needs only its own scores."""
+    q, k, v, do = _words(q), _words(k), _words(v), _words(do)
+    B, H, Sq, Skv, D = _qkv_shapes(q, k, v, do)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    if rows.size and (rows.min() < 0 or rows.max() >= B * H * Sq):
+        raise ValueError("row index out of range")
+    dq = np.empty((rows.size, D))
+    delta = np.empty((rows.size,))
+    rc = _load().oracle_attn_bwd_rows(q.ctypes.data, k.ctypes.data, v.ctypes.data, do.ctypes.data,
+                                      _DT[dtype], B, H, Sq, Skv, D, float(scale), int(bool(causal)),
+                                      rows.ctypes.data, rows.size, dq.ctypes.data, delta.ctypes.data)
+    if rc != 0:
+        raise MemoryError("oracle scratch allocation failed")
+    return dq, delta
+
+
+def attn_bwd_keys(q, k, v, do, dtype: str, scale: float, causal: bool, keys):
+    """dK [n,D] and dV [n,D] of sampled keys (flat indices (b*H + h)*Skv + j) of
+    16-bit inputs, in float64 (cheap for keys few queries keep)."""
+    q, k, v, do = _words(q), _words(k), _words(v), _words(do)
+    B, H, Sq, Skv, D = _qkv_shapes(q, k, v, do)
+    keys = np.ascontiguousarray(keys, dtype=np.int64)
+    if keys.size and (keys.min() < 0 or keys.max() >= B * H * Skv):
+        raise ValueError("key index out of range")
+    dk = np.empty((keys.size, D))
+    dv = np.empty((keys.size, D))
+    rc = _load().oracle_attn_bwd_keys(q.ctypes.data, k.ctypes.data, v.ctypes.data, do.ctypes.data,
+                                      _DT[dtype], B, H, Sq, Skv, D, float(scale), int(bool(causal)),
+                                      keys.ctypes.data, keys.size, dk.ctypes.data, dv.ctypes.data)
+    if rc != 0:
+        raise MemoryError("oracle scratch allocation failed")
+    return dk, dv

@@ -480,3 +480,141 @@ int oracle_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   free(vd);
   return rc;
 }
+
+/*
+ * dQ_i and D_i of sampled query rows only (rows: flat indices (b*H + h)*Sq + i),
+ * the first pass of oracle_attn_bwd_f64 restricted to those rows: each needs
+ * only its own row of scores, so it runs at any length.  16-bit inputs.
+ * dq receives nrows*D values, delta nrows.  Returns 0, or -1 when scratch
+ * memory cannot be had.
+ */
+int oracle_attn_bwd_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         const uint16_t* dO, int dtype, int64_t B, int64_t H, int64_t Sq,
+                         int64_t Skv, int64_t D, double scale, int causal,
+                         const int64_t* rows, int64_t nrows, double* dq, double* delta) {
+  init_tables();
+  const double* tab = table_for(dtype);
+  (void)B;
+  (void)H;
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* p = (double*)malloc(sizeof(double) * (size_t)(Skv > 0 ? Skv : 1));
+    double* dp = (double*)malloc(sizeof(double) * (size_t)(Skv > 0 ? Skv : 1));
+    double* qd = (double*)malloc(sizeof(double) * (size_t)(D > 0 ? D : 1));
+    double* dod = (double*)malloc(sizeof(double) * (size_t)(D > 0 ? D : 1));
+    if (!p || !dp || !qd || !dod) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t t = 0; t < nrows; ++t) {
+        const int64_t r = rows[t], bh = r / Sq, i = r % Sq;
+        double* dqrow = dq + t * D;
+        for (int64_t d = 0; d < D; ++d) {
+          dqrow[d] = 0.0;
+          qd[d] = tab[q[r * D + d]];
+          dod[d] = tab[dO[r * D + d]];
+        }
+        const int64_t n = allowed_keys(i, Sq, Skv, causal);
+        if (n <= 0) {
+          delta[t] = 0.0;
+          continue;
+        }
+        for (int64_t j = 0; j < n; ++j) {
+          const uint16_t* krow = k + (bh * Skv + j) * D;
+          const uint16_t* vrow = v + (bh * Skv + j) * D;
+          double s = 0.0, g = 0.0;
+          for (int64_t d = 0; d < D; ++d) {
+            s += qd[d] * tab[krow[d]];
+            g += dod[d] * tab[vrow[d]];
+          }
+          p[j] = scale * s;
+          dp[j] = g;
+        }
+        softmax_row(p, n);
+        double di = 0.0;
+        for (int64_t j = 0; j < n; ++j) di += dp[j] * p[j];
+        delta[t] = di;
+        for (int64_t j = 0; j < n; ++j) {
+          const double dsj = p[j] * (dp[j] - di);
+          const uint16_t* krow = k + (bh * Skv + j) * D;
+          for (int64_t d = 0; d < D; ++d) dqrow[d] += scale * dsj * tab[krow[d]];
+        }
+      }
+    }
+    free(p);
+    free(dp);
+    free(qd);
+    free(dod);
+  }
+  return failed ? -1 : 0;
+}
+
+/*
+ * dK_j and dV_j of sampled keys only (keys: flat indices (b*H + h)*Skv + j):
+ * for every query i that keeps key j, LSE_i and D_i from a full pass over
+ * that query's row, then P_ij = exp(s_ij - LSE_i), dS_ij = P_ij (dP_ij - D_i),
+ * dK_j += scale dS_ij q_i, dV_j += P_ij dO_i (the same definition as
+ * oracle_attn_bwd_f64).  Cost: (queries keeping the key) x Skv x D per key,
+ * small for the last keys of a long causal sequence.  16-bit inputs; dk, dv
+ * receive nkeys*D values.  Returns 0, or -1 when scratch memory cannot be had.
+ */
+int oracle_attn_bwd_keys(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         const uint16_t* dO, int dtype, int64_t B, int64_t H, int64_t Sq,
+                         int64_t Skv, int64_t D, double scale, int causal,
+                         const int64_t* keys, int64_t nkeys, double* dk, double* dv) {
+  init_tables();
+  const double* tab = table_for(dtype);
+  (void)B;
+  (void)H;
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* p = (double*)malloc(sizeof(double) * (size_t)(Skv > 0 ? Skv : 1));
+    double* dp = (double*)malloc(sizeof(double) * (size_t)(Skv > 0 ? Skv : 1));
+    if (!p || !dp) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t t = 0; t < nkeys; ++t) {
+        const int64_t c = keys[t], bh = c / Skv, j = c % Skv;
+        double* dkrow = dk + t * D;
+        double* dvrow = dv + t * D;
+        for (int64_t d = 0; d < D; ++d) dkrow[d] = dvrow[d] = 0.0;
+        for (int64_t i = 0; i < Sq; ++i) {
+          const int64_t n = allowed_keys(i, Sq, Skv, causal);
+          if (j >= n) continue;
+          const uint16_t* qrow = q + (bh * Sq + i) * D;
+          const uint16_t* dorow = dO + (bh * Sq + i) * D;
+          /* the query's whole row: scores, dP, LSE_i, D_i */
+          for (int64_t jj = 0; jj < n; ++jj) {
+            const uint16_t* krow = k + (bh * Skv + jj) * D;
+            const uint16_t* vrow = v + (bh * Skv + jj) * D;
+            double s = 0.0, g = 0.0;
+            for (int64_t d = 0; d < D; ++d) {
+              s += tab[qrow[d]] * tab[krow[d]];
+              g += tab[dorow[d]] * tab[vrow[d]];
+            }
+            p[jj] = scale * s;
+            dp[jj] = g;
+          }
+          const double sj = p[j];
+          const double lse = softmax_row(p, n);
+          double di = 0.0;
+          for (int64_t jj = 0; jj < n; ++jj) di += dp[jj] * p[jj];
+          const double pij = exp(sj - lse);
+          const double dsij = pij * (dp[j] - di);
+          for (int64_t d = 0; d < D; ++d) {
+            dkrow[d] += scale * dsij * tab[qrow[d]];
+            dvrow[d] += pij * tab[dorow[d]];
+          }
+        }
+      }
+    }
+    free(p);
+    free(dp);
+  }
+  return failed ? -1 : 0;
+}

@@ -171,3 +171,30 @@ def test_16bit_entry_widens_exactly():
         b = oracle.attn_bwd_f64(*(oracle.decode(x, dtype) for x in (q, k, v, do)), 0.125, True)
         for x, y in zip(a, b):
             assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sampled_rows_equal_the_full_backward(causal):
+    from exact_attention_52_amd import inputs
+    q, _, _ = inputs.gen_qkv(2, 3, 41, 64, "bf16", seed=3)
+    _, k, v = inputs.gen_qkv(2, 3, 29, 64, "bf16", seed=4)
+    do, _, _ = inputs.gen_qkv(2, 3, 41, 64, "bf16", seed=5)
+    dq, _, _, delta = oracle.attn_bwd(q, k, v, do, "bf16", 0.125, causal)
+    rows = np.array([0, 5, 40, 41, 100, 2 * 3 * 41 - 1])
+    dq_r, delta_r = oracle.attn_bwd_rows(q, k, v, do, "bf16", 0.125, causal, rows)
+    assert np.abs(dq_r - dq.reshape(-1, 64)[rows]).max() <= 1e-13
+    assert np.abs(delta_r - delta.reshape(-1)[rows]).max() <= 1e-13
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Sq,Skv", [(41, 29), (29, 41), (33, 33)])
+def test_sampled_keys_equal_the_full_backward(causal, Sq, Skv):
+    from exact_attention_52_amd import inputs
+    q, _, _ = inputs.gen_qkv(2, 2, Sq, 64, "fp16", seed=6)
+    _, k, v = inputs.gen_qkv(2, 2, Skv, 64, "fp16", seed=7)
+    do, _, _ = inputs.gen_qkv(2, 2, Sq, 64, "fp16", seed=8)
+    _, dk, dv, _ = oracle.attn_bwd(q, k, v, do, "fp16", 0.125, causal)
+    keys = np.array([0, 7, Skv - 1, Skv, 2 * 2 * Skv - 1])
+    dk_s, dv_s = oracle.attn_bwd_keys(q, k, v, do, "fp16", 0.125, causal, keys)
+    assert np.abs(dk_s - dk.reshape(-1, 64)[keys]).max() <= 1e-13
+    assert np.abs(dv_s - dv.reshape(-1, 64)[keys]).max() <= 1e-13
