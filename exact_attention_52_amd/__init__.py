@@ -4,7 +4,7 @@
 CUDA tensors q [B,H,Sq,D] and k, v [B,H,Skv,D] (any strides with the last
 dimension contiguous): O = softmax(scale * Q K^T [causal]) V and the
 natural-log LSE per row (fp32).  ``bwd(q, k, v, o, lse, do, ...)`` returns
-``(dq, dk, dv, delta)``, the gradients for a given dO (contiguous tensors).
+``(dq, dk, dv, delta)``, the gradients for a given dO (any such strides).
 PyTorch only provides device memory and the
 stream; the computation is the libattn.so gfx950 kernel behind the C ABI of
 include/attn.h.  ``inputs`` holds the seeded synthetic-input generator.
@@ -17,12 +17,13 @@ from . import _lib
 from ._lib import ATTN_BF16, ATTN_F16, AttnError  # noqa: F401
 
 __all__ = ["fwd", "bwd", "fwd_unfused", "fwd_variant", "attn_fwd", "attn_fwd_strided", "attn_fwd_variant",
-           "attn_bwd", "attn_fwd_unfused",
+           "attn_bwd", "attn_bwd_strided", "attn_fwd_unfused",
            "attn_fwd_unfused_workspace_bytes", "attn_fwd_plan", "attn_fwd_workgroup_tile", "AttnError"]
 
 attn_fwd = _lib.attn_fwd
 attn_fwd_strided = _lib.attn_fwd_strided
 attn_bwd = _lib.attn_bwd
+attn_bwd_strided = _lib.attn_bwd_strided
 attn_fwd_variant = _lib.attn_fwd_variant
 attn_fwd_unfused = _lib.attn_fwd_unfused
 attn_fwd_unfused_workspace_bytes = _lib.attn_fwd_unfused_workspace_bytes
@@ -93,16 +94,17 @@ def bwd(q, k, v, o, lse, do, scale=None, causal=False, dq=None, dk=None, dv=None
         stream=None):
     """Gradients of ``fwd`` for the output gradient ``do``.
 
-    q, o, do: contiguous [B,H,Sq,D]; k, v: contiguous [B,H,Skv,D]; one dtype
-    (fp16 or bf16); lse: contiguous fp32 [B,H,Sq], with o and lse from ``fwd``
-    on the same inputs.  Returns (dq, dk, dv, delta): dq [B,H,Sq,D], dk, dv
-    [B,H,Skv,D] in the input dtype and delta = rowsum(do * o) fp32 [B,H,Sq].
-    Outputs may be passed preallocated (contiguous).
+    q, o, do: [B,H,Sq,D]; k, v: [B,H,Skv,D]; one dtype (fp16 or bf16); any
+    strides with the last dimension contiguous (e.g. views of [B,S,H,D]);
+    lse: contiguous fp32 [B,H,Sq], with o and lse from ``fwd`` on the same
+    inputs.  Returns (dq, dk, dv, delta): dq [B,H,Sq,D], dk, dv [B,H,Skv,D] in
+    the input dtype (fresh contiguous tensors unless passed in, with any such
+    strides) and delta = rowsum(do * o), contiguous fp32 [B,H,Sq].
     """
     import torch
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
-        if t.dim() != 4 or not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous 4-D GPU tensor")
+        if t.dim() != 4 or not t.is_cuda:
+            raise ValueError(f"{name} must be a 4-D GPU tensor")
         if t.dtype != q.dtype:
             raise TypeError("q, k, v, o, do must share one dtype")
     B, H, Sq, D = q.shape
@@ -116,19 +118,29 @@ def bwd(q, k, v, o, lse, do, scale=None, causal=False, dq=None, dk=None, dv=None
     dt = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
     delta = torch.empty_like(lse) if delta is None else delta
-    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v), ("delta", delta, lse)):
-        if t.shape != ref.shape or t.dtype != ref.dtype or not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous with the shape and dtype of its input")
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.shape != ref.shape or t.dtype != ref.dtype:
+            raise ValueError(f"{name} must have the shape and dtype of its input")
+    if delta.shape != lse.shape or delta.dtype != torch.float32 or not delta.is_contiguous():
+        raise ValueError("delta must be a contiguous float32 [B,H,Sq] tensor")
+    tensors = (q, k, v, o, do, dq, dk, dv)
+    for name, t in zip(("q", "k", "v", "o", "do", "dq", "dk", "dv"), tensors):
+        if D > 1 and t.stride(3) != 1:
+            raise ValueError(f"{name} must have its last dimension contiguous")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    ptrs = [t.data_ptr() for t in (q, k, v, o)] + [lse.data_ptr(), do.data_ptr()] + \
+        [t.data_ptr() for t in (dq, dk, dv)] + [delta.data_ptr()]
     with torch.cuda.device(q.device):
-        st = _lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                           do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
-                           B, H, Sq, Skv, D, scale, causal, dt, stream.cuda_stream)
+        if all(t.is_contiguous() for t in tensors):
+            st = _lib.attn_bwd(*ptrs, B, H, Sq, Skv, D, scale, causal, dt, stream.cuda_stream)
+        else:
+            st = _lib.attn_bwd_strided(*ptrs, B, H, Sq, Skv, D, [t.stride()[:3] for t in tensors], scale,
+                                       causal, dt, stream.cuda_stream)
     _lib.check(st)
     return dq, dk, dv, delta
 

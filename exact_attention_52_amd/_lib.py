@@ -7,7 +7,7 @@ import ctypes
 import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 ATTN_F16, ATTN_BF16 = 0, 1
 STATUS = {
@@ -16,7 +16,7 @@ STATUS = {
     5: "ATTN_ERR_MISALIGNED", 6: "ATTN_ERR_BAD_SCALE", 7: "ATTN_ERR_ALIASING",
     8: "ATTN_ERR_UNSUPPORTED_DEVICE", 9: "ATTN_ERR_LAUNCH", 10: "ATTN_ERR_BAD_ARGUMENT",
 }
-EXPORTS = ("attn_fwd", "attn_fwd_strided", "attn_fwd_variant", "attn_bwd", "attn_fwd_unfused",
+EXPORTS = ("attn_fwd", "attn_fwd_strided", "attn_fwd_variant", "attn_bwd", "attn_bwd_strided", "attn_fwd_unfused",
            "attn_fwd_unfused_workspace_bytes", "attn_fwd_plan", "attn_fwd_workgroup_tile",
            "attn_status_string", "attn_last_error", "attn_abi_version")
 
@@ -59,6 +59,9 @@ def load():
     lib.attn_fwd_strided.restype = ci
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, cf, ci, ci, vp]
     lib.attn_bwd.restype = ci
+    lib.attn_bwd_strided.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                     p64, p64, p64, p64, p64, p64, p64, p64, cf, ci, ci, vp]
+    lib.attn_bwd_strided.restype = ci
     lib.attn_fwd_variant.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, cf, ci, ci, ci, vp]
     lib.attn_fwd_variant.restype = ci
     lib.attn_fwd_unfused.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, cf, ci, ci, vp]
@@ -127,6 +130,18 @@ def attn_bwd(q: int, k: int, v: int, o: int, lse: int, do: int, dq: int, dk: int
     """Raw call: device pointers as ints; returns the status code."""
     return load().attn_bwd(q, k, v, o, lse, do, dq, dk, dv, delta, B, H, Sq, Skv, D, float(scale),
                            int(bool(causal)), int(dtype), stream)
+
+
+def attn_bwd_strided(q: int, k: int, v: int, o: int, lse: int, do: int, dq: int, dk: int, dv: int, delta: int,
+                     B: int, H: int, Sq: int, Skv: int, D: int, strides, scale: float, causal: bool,
+                     dtype: int, stream: int) -> int:
+    """Raw call: device pointers as ints; strides: 8 (batch, head, row) triples
+    or None for (q, k, v, o, do, dq, dk, dv); returns the status code."""
+    st = [_strides(x) for x in strides]
+    if len(st) != 8:
+        raise ValueError("8 stride triples: q, k, v, o, do, dq, dk, dv")
+    return load().attn_bwd_strided(q, k, v, o, lse, do, dq, dk, dv, delta, B, H, Sq, Skv, D, *st,
+                                   float(scale), int(bool(causal)), int(dtype), stream)
 
 
 def attn_fwd_variant(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, S: int, D: int,

@@ -331,9 +331,12 @@ int attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float
              view(v_strides, Skv, "v"), view(o_strides, Sq, "o"), scale, causal, dtype, stream);
 }
 
-int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
-             void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
-             int64_t D, float scale, int causal, int dtype, void* stream) {
+int attn_bwd_strided(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+                     void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
+                     int64_t D, const int64_t* q_strides, const int64_t* k_strides, const int64_t* v_strides,
+                     const int64_t* o_strides, const int64_t* do_strides, const int64_t* dq_strides,
+                     const int64_t* dk_strides, const int64_t* dv_strides, float scale, int causal, int dtype,
+                     void* stream) {
   if (B < 0 || H < 0 || Sq < 0 || Skv < 0)
     return fail(ATTN_ERR_BAD_SHAPE, "B, H, Sq and Skv must be >= 0 (got B=%lld H=%lld Sq=%lld Skv=%lld)",
                 (long long)B, (long long)H, (long long)Sq, (long long)Skv);
@@ -349,13 +352,35 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
        (uintptr_t)dk | (uintptr_t)dv) & 15)
     return fail(ATTN_ERR_MISALIGNED, "q, k, v, o, dO, dq, dk and dv must be 16-byte aligned");
   if (((uintptr_t)lse | (uintptr_t)delta) & 3) return fail(ATTN_ERR_MISALIGNED, "lse and delta must be 4-byte aligned");
-  const int64_t nq = B * H * Sq * D * 2, nk = B * H * Skv * D * 2, nr = B * H * Sq * 4;
+  auto view = [&](const void* ptr, const int64_t* sts, int64_t rows, const char* name) {
+    View t = {ptr, H * rows * D, rows * D, D, rows, name};
+    if (sts) t.sb = sts[0], t.sh = sts[1], t.ss = sts[2];
+    normalise(t, B, H, D);
+    return t;
+  };
+  View vs[8] = {view(q, q_strides, Sq, "q"),    view(k, k_strides, Skv, "k"),   view(v, v_strides, Skv, "v"),
+                view(o, o_strides, Sq, "o"),    view(dO, do_strides, Sq, "dO"), view(dq, dq_strides, Sq, "dq"),
+                view(dk, dk_strides, Skv, "dk"), view(dv, dv_strides, Skv, "dv")};
+  for (const View& t : vs) {
+    if (t.rows == 0) continue;
+    st = check_view(t, B, H, D);
+    if (st != ATTN_OK) return st;
+  }
+  for (int i = 5; i < 8; ++i)
+    if (vs[i].rows > 0 && !self_disjoint(vs[i], B, H, D))
+      return fail(ATTN_ERR_ALIASING, "%s strides make rows overlap", vs[i].name);
+  const int64_t nr = B * H * Sq * 4;
   struct Buf {
     const void* p;
     int64_t n;
   };
-  const Buf outs[4] = {{dq, nq}, {dk, nk}, {dv, nk}, {delta, nr}};
-  const Buf ins[6] = {{q, nq}, {k, nk}, {v, nk}, {o, nq}, {dO, nq}, {lse, nr}};
+  const Buf outs[4] = {{dq, extent_bytes(vs[5], B, H, D)},
+                       {dk, extent_bytes(vs[6], B, H, D)},
+                       {dv, extent_bytes(vs[7], B, H, D)},
+                       {delta, nr}};
+  const Buf ins[6] = {{q, extent_bytes(vs[0], B, H, D)}, {k, extent_bytes(vs[1], B, H, D)},
+                      {v, extent_bytes(vs[2], B, H, D)}, {o, extent_bytes(vs[3], B, H, D)},
+                      {dO, extent_bytes(vs[4], B, H, D)}, {lse, nr}};
   for (int i = 0; i < 4; ++i) {
     for (int j = i + 1; j < 4; ++j)
       if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n))
@@ -377,6 +402,9 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   p.q = (const uint16_t*)q, p.k = (const uint16_t*)k, p.v = (const uint16_t*)v, p.o = (const uint16_t*)o;
   p.dO = (const uint16_t*)dO, p.lse = lse, p.delta = delta;
   p.dq = (uint16_t*)dq, p.dk = (uint16_t*)dk, p.dv = (uint16_t*)dv;
+  attn::Strides* ps[8] = {&p.s_q, &p.s_k, &p.s_v, &p.s_o, &p.s_do, &p.s_dq, &p.s_dk, &p.s_dv};
+  for (int i = 0; i < 8; ++i) *ps[i] = attn::Strides{vs[i].sb, vs[i].sh, (int)vs[i].ss};
+  p.H = (int)H;
   p.Sq = (int)Sq, p.Skv = (int)Skv, p.nq = 0, p.nk = 0, p.BH = B * H;
   float c = (float)((double)scale * 1.4426950408889634074);
   p.c = c < FLT_MIN ? FLT_MIN : c;
@@ -384,6 +412,14 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   const hipError_t e = attn::bwd_launch(p, (int)D, causal != 0, dtype, (hipStream_t)stream);
   if (e != hipSuccess) return fail(ATTN_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+             void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
+             int64_t D, float scale, int causal, int dtype, void* stream) {
+  // contiguous tensors: the strided entry with every stride array NULL
+  return attn_bwd_strided(q, k, v, o, lse, dO, dq, dk, dv, delta, B, H, Sq, Skv, D, nullptr, nullptr, nullptr,
+                          nullptr, nullptr, nullptr, nullptr, nullptr, scale, causal, dtype, stream);
 }
 
 int64_t attn_fwd_unfused_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t D) {

@@ -7,9 +7,16 @@
 
 namespace attn {
 
-// Contiguous Q, O, dO, dQ [B,H,Sq,D] and K, V, dK, dV [B,H,Skv,D] of 16-bit
-// elements; LSE and delta [B,H,Sq] fp32.  Causal keeps key j for query i iff
-// j <= i + (Skv - Sq), as in the forward.
+// Batch, head and row strides (elements) of one [B,H,rows,D] tensor whose
+// rows are contiguous.
+struct Strides {
+  int64_t sb, sh;
+  int ss;
+};
+
+// Q, O, dO, dQ [B,H,Sq,D] and K, V, dK, dV [B,H,Skv,D] of 16-bit elements,
+// each with its own strides; LSE and delta [B,H,Sq] fp32, contiguous.  Causal
+// keeps key j for query i iff j <= i + (Skv - Sq), as in the forward.
 struct BwdProblem {
   const uint16_t* q;
   const uint16_t* k;
@@ -21,6 +28,8 @@ struct BwdProblem {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
+  Strides s_q, s_k, s_v, s_o, s_do, s_dq, s_dk, s_dv;
+  int H;
   int Sq, Skv;
   int nq, nk;  // query tiles per head (dQ kernel), key tiles per head (dK/dV kernel)
   int64_t BH;  // B * H

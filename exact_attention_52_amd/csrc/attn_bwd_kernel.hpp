@@ -83,28 +83,35 @@ constexpr bool offsets_split() {
   return true;
 }
 
-// HBM -> LDS copies of XTile tiles of one head (contiguous rows of D).  Lane i
-// of a copy instruction carries row slot i / (D/8) of the line and 16-byte
-// chunk i % (D/8).  Rows at or past `rows` read as 0.
+// The first row of head bh (= b*H + h) of a tensor with strides s.
+template <class T>
+__device__ __forceinline__ T* head_ptr(T* base, const Strides& s, int64_t bh, int H) {
+  return base + (bh / H) * s.sb + (bh % H) * s.sh;
+}
+
+// HBM -> LDS copies of XTile tiles of one head (rows of D elements, ss
+// apart).  Lane i of a copy instruction carries row slot i / (D/8) of the
+// line and 16-byte chunk i % (D/8).  Rows at or past `rows` read as 0.
 template <class X>
 struct XCopier {
   static constexpr int D = X::D;
   const uint16_t* src;
-  int rows;
+  int rows, ss;
   uint32_t lane_off;
-  __device__ __forceinline__ void init(const uint16_t* src_, int rows_, int lane) {
+  __device__ __forceinline__ void init(const uint16_t* src_, int ss_, int rows_, int lane) {
     src = src_;
+    ss = ss_;
     rows = rows_;
-    lane_off = (uint32_t)(16 * (lane / (D / 8)) * D + (lane % (D / 8)) * 8) * 2u;
+    lane_off = (uint32_t)(16 * (lane / (D / 8)) * ss + (lane % (D / 8)) * 8) * 2u;
   }
   // (the byte count is wave-uniform; readfirstlane keeps it in an SGPR, where
   // a buffer descriptor must be, instead of a loop over distinct lane values)
   __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile(int r0) const {
-    const uint32_t bytes = r0 < rows ? rows_bytes(rows - r0, D, D) : 0u;
-    return make_rsrc(src + (int64_t)r0 * D, (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes));
+    const uint32_t bytes = r0 < rows ? rows_bytes(rows - r0, ss, D) : 0u;
+    return make_rsrc(src + (int64_t)r0 * ss, (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes));
   }
   __device__ __forceinline__ void line(__amdgpu_buffer_rsrc_t r, uint8_t* dst, int n) const {
-    load16_lds(r, dst + n * X::LINE, lane_off, (uint32_t)(X::line_row(n) * D) * 2u);
+    load16_lds(r, dst + n * X::LINE, lane_off, (uint32_t)(X::line_row(n) * ss) * 2u);
   }
 };
 
@@ -148,8 +155,11 @@ __global__ __launch_bounds__(256) void attn_bwd_delta(const BwdProblem p) {
   const int part = threadIdx.x % LPR;
   float acc = 0.f;
   if (row < p.BH * p.Sq) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(p.o + row * D + part * 8);
-    const u32x4 b = *reinterpret_cast<const u32x4*>(p.dO + row * D + part * 8);
+    const int64_t bh = row / p.Sq, i = row % p.Sq;
+    const uint16_t* orow = head_ptr(p.o, p.s_o, bh, p.H) + i * p.s_o.ss;
+    const uint16_t* dorow = head_ptr(p.dO, p.s_do, bh, p.H) + i * p.s_do.ss;
+    const u32x4 a = *reinterpret_cast<const u32x4*>(orow + part * 8);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(dorow + part * 8);
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc = dot2<DT>(a[e], b[e], acc);
   }
@@ -236,10 +246,10 @@ void attn_bwd_dkdv(const BwdProblem p) {
   }
   const int Sq = p.Sq, Skv = p.Skv, koff = Skv - Sq;
   const int k0 = (int)kt64 * BN, kbase = k0 + 32 * wave, my_k = kbase + col;
-  const uint16_t* qh = p.q + bh * Sq * D;
-  const uint16_t* doh = p.dO + bh * Sq * D;
-  const uint16_t* kh = p.k + bh * Skv * D;
-  const uint16_t* vh = p.v + bh * Skv * D;
+  const uint16_t* qh = head_ptr(p.q, p.s_q, bh, p.H);
+  const uint16_t* doh = head_ptr(p.dO, p.s_do, bh, p.H);
+  const uint16_t* kh = head_ptr(p.k, p.s_k, bh, p.H);
+  const uint16_t* vh = head_ptr(p.v, p.s_v, bh, p.H);
   const float* lseh = p.lse + bh * Sq;
   const float* delh = p.delta + bh * Sq;
   const __amdgpu_buffer_rsrc_t lse_r = make_rsrc(lseh, (uint32_t)Sq * 4u);
@@ -248,13 +258,14 @@ void attn_bwd_dkdv(const BwdProblem p) {
   // this wave's keys: B operands of S = Q K^T and dP = dO V^T (rows past Skv read 0)
   u32x4 kf[DK], vf[DK];
   {
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kh, rows_bytes(Skv, D, D));
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vh, rows_bytes(Skv, D, D));
-    const uint32_t off = (uint32_t)(my_k * D + 8 * half) * 2u;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kh, rows_bytes(Skv, p.s_k.ss, D));
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vh, rows_bytes(Skv, p.s_v.ss, D));
+    const uint32_t koff = (uint32_t)(my_k * p.s_k.ss + 8 * half) * 2u;
+    const uint32_t voff = (uint32_t)(my_k * p.s_v.ss + 8 * half) * 2u;
 #pragma unroll
     for (int kc = 0; kc < DK; ++kc) {
-      kf[kc] = load16(kr, off + 32 * kc);
-      vf[kc] = load16(vr, off + 32 * kc);
+      kf[kc] = load16(kr, koff + 32 * kc);
+      vf[kc] = load16(vr, voff + 32 * kc);
     }
   }
   f32x16 dka[DB], dva[DB];
@@ -267,8 +278,8 @@ void attn_bwd_dkdv(const BwdProblem p) {
   const int n = qs < Sq ? (Sq - qs + BQ - 1) / BQ : 0;
 
   XCopier<X> qc, oc;
-  qc.init(qh, Sq, lane);
-  oc.init(doh, Sq, lane);
+  qc.init(qh, p.s_q.ss, Sq, lane);
+  oc.init(doh, p.s_do.ss, Sq, lane);
   auto fetch = [&](int s, uint8_t* dq_, uint8_t* do_, float* ls_, float* dl_) __attribute__((always_inline)) {
     const int r0 = qs + s * BQ;
     const __amdgpu_buffer_rsrc_t rq = qc.tile(r0), ro = oc.tile(r0);
@@ -394,8 +405,8 @@ void attn_bwd_dkdv(const BwdProblem p) {
   }
 
   if (my_k < Skv) {
-    uint16_t* dkr = p.dk + (bh * Skv + my_k) * D;
-    uint16_t* dvr = p.dv + (bh * Skv + my_k) * D;
+    uint16_t* dkr = head_ptr(p.dk, p.s_dk, bh, p.H) + (int64_t)my_k * p.s_dk.ss;
+    uint16_t* dvr = head_ptr(p.dv, p.s_dv, bh, p.H) + (int64_t)my_k * p.s_dv.ss;
     const float sc = p.scale;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -439,19 +450,20 @@ void attn_bwd_dq(const BwdProblem p) {
   workgroup_tile(blockIdx.x, p.BH * p.nq, p.nq, CAUSAL, &tile64, &bh);
   const int Sq = p.Sq, Skv = p.Skv, koff = Skv - Sq;
   const int q0 = (int)tile64 * BM, wq_first = q0 + 32 * wave, my_q = wq_first + col;
-  const uint16_t* kh = p.k + bh * Skv * D;
-  const uint16_t* vh = p.v + bh * Skv * D;
+  const uint16_t* kh = head_ptr(p.k, p.s_k, bh, p.H);
+  const uint16_t* vh = head_ptr(p.v, p.s_v, bh, p.H);
 
   // this wave's queries: B operands of S^T = K Q^T and dP^T = V dO^T
   u32x4 qf[DK], of[DK];
   {
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(p.q + bh * Sq * D, rows_bytes(Sq, D, D));
-    const __amdgpu_buffer_rsrc_t orr = make_rsrc(p.dO + bh * Sq * D, rows_bytes(Sq, D, D));
-    const uint32_t off = (uint32_t)(my_q * D + 8 * half) * 2u;
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(head_ptr(p.q, p.s_q, bh, p.H), rows_bytes(Sq, p.s_q.ss, D));
+    const __amdgpu_buffer_rsrc_t orr = make_rsrc(head_ptr(p.dO, p.s_do, bh, p.H), rows_bytes(Sq, p.s_do.ss, D));
+    const uint32_t qoff = (uint32_t)(my_q * p.s_q.ss + 8 * half) * 2u;
+    const uint32_t ooff = (uint32_t)(my_q * p.s_do.ss + 8 * half) * 2u;
 #pragma unroll
     for (int kc = 0; kc < DK; ++kc) {
-      qf[kc] = load16(qr, off + 32 * kc);
-      of[kc] = load16(orr, off + 32 * kc);
+      qf[kc] = load16(qr, qoff + 32 * kc);
+      of[kc] = load16(orr, ooff + 32 * kc);
     }
   }
   const bool q_ok = my_q < Sq;
@@ -467,8 +479,8 @@ void attn_bwd_dq(const BwdProblem p) {
   const int n = kv_end > 0 ? (kv_end + BNK - 1) / BNK : 0;
 
   XCopier<X> kc_, vc_;
-  kc_.init(kh, Skv, lane);
-  vc_.init(vh, Skv, lane);
+  kc_.init(kh, p.s_k.ss, Skv, lane);
+  vc_.init(vh, p.s_v.ss, Skv, lane);
   auto fetch = [&](int j, uint8_t* k_, uint8_t* v_) __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t rk = kc_.tile(j * BNK), rv = vc_.tile(j * BNK);
 #pragma unroll
@@ -564,7 +576,7 @@ void attn_bwd_dq(const BwdProblem p) {
   }
 
   if (q_ok) {
-    uint16_t* dqr = p.dq + (bh * Sq + my_q) * D;
+    uint16_t* dqr = head_ptr(p.dq, p.s_dq, bh, p.H) + (int64_t)my_q * p.s_dq.ss;
     const float sc = p.scale;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {

@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 4
+#define ATTN_ABI_VERSION 5
 
 /* Element type of Q, K, V and O.  The page restricts the float type to F16 or
  * BF16 (validate_config, "float_type must be F16 or BF16"). */
@@ -154,6 +154,25 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
              const float* lse, const void* dO, void* dq, void* dk, void* dv,
              float* delta, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
              int64_t D, float scale, int causal, int dtype, void* stream);
+
+/*
+ * attn_bwd_strided -- attn_bwd for strided tensors.
+ *
+ * Same operation, results and errors as attn_bwd; every 16-bit tensor takes
+ * a host array of 3 int64 (batch, head, row) strides in elements, or NULL
+ * for contiguous [B,H,rows,D], under the rules of attn_fwd_strided (strides
+ * of dimensions longer than 1 >= 0 and multiples of 8, row strides >= D, one
+ * head < 2 GiB; dq, dk and dv must not address one element twice).  lse and
+ * delta stay contiguous [B,H,Sq].  Aliasing is judged on byte extents.
+ */
+int attn_bwd_strided(const void* q, const void* k, const void* v, const void* o,
+                     const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                     float* delta, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
+                     int64_t D, const int64_t* q_strides, const int64_t* k_strides,
+                     const int64_t* v_strides, const int64_t* o_strides,
+                     const int64_t* do_strides, const int64_t* dq_strides,
+                     const int64_t* dk_strides, const int64_t* dv_strides, float scale,
+                     int causal, int dtype, void* stream);
 
 /*
  * attn_fwd_variant -- attn_fwd with another copy schedule, for A/B

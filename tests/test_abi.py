@@ -376,3 +376,46 @@ def test_variants_reach_the_device_check():
             assert vcall(v, D) == 8, _lib.last_error()
     assert vcall(0, 256) == 8
     assert vcall(3, 64, B=0) == 0  # empty
+
+
+def bscall(strides, **kw):
+    args = dict(q=FAKE, k=FAKE + MB_, v=FAKE + 2 * MB_, o=FAKE + 3 * MB_, lse=FAKE + 4 * MB_, do=FAKE + 5 * MB_,
+                dq=FAKE + 6 * MB_, dk=FAKE + 7 * MB_, dv=FAKE + 8 * MB_, delta=FAKE + 9 * MB_, B=1, H=2, Sq=16,
+                Skv=24, D=64)
+    args.update(kw)
+    st = [strides.get(n) for n in ("q", "k", "v", "o", "do", "dq", "dk", "dv")]
+    return _lib.attn_bwd_strided(args["q"], args["k"], args["v"], args["o"], args["lse"], args["do"], args["dq"],
+                                 args["dk"], args["dv"], args["delta"], args["B"], args["H"], args["Sq"],
+                                 args["Skv"], args["D"], st, 0.125, 0, 0, 0)
+
+
+@pytest.mark.parametrize("strides,status,word", [
+    ({"k": (3072, -1536, 64)}, 10, ">= 0"),
+    ({"do": (2048, 1024, 60)}, 10, "shorter than a row"),
+    ({"dv": (3072, 1536, 68)}, 5, "multiples of 8"),
+    ({"dq": (2048, 512, 64)}, 7, "dq strides"),        # head 1 inside head 0's 16 rows
+    ({"dk": (3072, 32, 128)}, 7, "dk strides"),
+])
+def test_bwd_strided_invalid_arguments(strides, status, word):
+    st = bscall(strides)
+    assert st == status, (st, _lib.last_error())
+    assert word.lower() in _lib.last_error().lower()
+
+
+def test_bwd_strided_extent_aliasing():
+    # dq starts past lse, but its second head (16 MiB on) lies inside dO's region
+    st = bscall({"dq": (1 << 24, 1 << 23, 64)}, dq=FAKE + 4 * MB_ + 4096)
+    assert st == 7 and "overlap" in _lib.last_error()
+
+
+def test_bwd_strided_valid_layouts_reach_the_device_check():
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("would launch on a real GPU with fake pointers")
+    H, Sq, Skv, D = 2, 16, 24, 64
+    bshd_q = (Sq * H * D, D, H * D)
+    bshd_k = (Skv * H * D, D, H * D)
+    layouts = {"q": bshd_q, "o": bshd_q, "do": bshd_q, "dq": bshd_q, "k": bshd_k, "v": bshd_k, "dk": bshd_k,
+               "dv": bshd_k}
+    assert bscall(layouts) == 8, _lib.last_error()
+    assert bscall({}) == 8, _lib.last_error()

@@ -140,3 +140,49 @@ def test_bwd_deterministic(ea):
 def test_bwd_full_size(ea, oracle_mod, wl, heads):
     B, H, S, D, dtype, causal, mult = inputs.WORKLOADS[wl]
     run_case(ea, oracle_mod, B, H, S, S, D, dtype, causal, seed=0, mult=mult, heads=heads)
+
+
+def as_layout(t, layout):
+    import torch
+    B, H, S, D = t.shape
+    if layout == "bshd":
+        return t.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    if layout == "padded":
+        buf = torch.zeros((B, H, S, D + 8), dtype=t.dtype, device=t.device)
+        buf[..., :D] = t
+        return buf[..., :D]
+    return t
+
+
+@pytest.mark.parametrize("D,dtype,causal", [(64, "fp16", True), (128, "bf16", False), (128, "fp16", True),
+                                            (256, "bf16", True)])
+@pytest.mark.parametrize("layout", ["bshd", "padded"])
+def test_bwd_strided_equals_contiguous_bitwise(ea, D, dtype, causal, layout):
+    # the layout changes the addresses, not the arithmetic
+    import torch
+    q, k, v, do = gen(2, 3, 300, 300, D, dtype, seed=D + 1)
+    dev = [to_dev(x, dtype) for x in (q, k, v, do)]
+    o, lse = ea.fwd(*dev[:3], causal=causal)
+    ref = ea.bwd(*dev[:3], o, lse, dev[3], causal=causal)
+    ins = [as_layout(t, layout) for t in (*dev[:3], o, dev[3])]
+    outs = [as_layout(torch.full_like(t, float("nan")), layout) for t in dev[:3]]
+    got = ea.bwd(*ins[:4], lse, ins[4], causal=causal, dq=outs[0], dk=outs[1], dv=outs[2])
+    torch.cuda.synchronize()
+    for a, b in zip(got, ref):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_strided_unequal_lengths_vs_oracle(ea, oracle_mod, causal):
+    import torch
+    D, dtype = 128, "fp16"
+    q, k, v, do = gen(1, 2, 150, 333, D, dtype, seed=4)
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    dev = [as_layout(to_dev(x, dtype), "bshd") for x in (q, k, v, do)]
+    o, lse = ea.fwd(*dev[:3], scale=scale, causal=causal)
+    got = ea.bwd(*dev[:3], o, lse, dev[3], scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    ref = oracle_mod.attn_bwd(q, k, v, do, dtype, scale, causal)
+    for name, a, r in zip(("dq", "dk", "dv", "delta"), got, ref):
+        e = rel_err(a.float().cpu().numpy().astype(np.float64), r)
+        assert e <= TOL_G[dtype], f"{name}: {e:.3e}"
