@@ -4,7 +4,8 @@
 CUDA tensors q [B,H,Sq,D] and k, v [B,H,Skv,D] (any strides with the last
 dimension contiguous): O = softmax(scale * Q K^T [causal]) V and the
 natural-log LSE per row (fp32).  ``bwd(q, k, v, o, lse, do, ...)`` returns
-``(dq, dk, dv, delta)``, the gradients for a given dO (any such strides).
+``(dq, dk, dv, delta)``, the gradients for a given dO (any such strides);
+``attention(q, k, v, scale, causal)`` wraps both as a torch.autograd function.
 PyTorch only provides device memory and the
 stream; the computation is the libattn.so gfx950 kernel behind the C ABI of
 include/attn.h.  ``inputs`` holds the seeded synthetic-input generator.
@@ -16,7 +17,7 @@ import math
 from . import _lib
 from ._lib import ATTN_BF16, ATTN_F16, AttnError  # noqa: F401
 
-__all__ = ["fwd", "bwd", "fwd_unfused", "fwd_variant", "attn_fwd", "attn_fwd_strided", "attn_fwd_variant",
+__all__ = ["attention", "fwd", "bwd", "fwd_unfused", "fwd_variant", "attn_fwd", "attn_fwd_strided", "attn_fwd_variant",
            "attn_bwd", "attn_bwd_strided", "attn_fwd_unfused",
            "attn_fwd_unfused_workspace_bytes", "attn_fwd_plan", "attn_fwd_workgroup_tile", "AttnError"]
 
@@ -207,3 +208,43 @@ def fwd_variant(q, k, v, variant, scale=None, causal=False, out=None, lse=None, 
                                    B, H, S, D, scale, causal, dt, int(variant), stream.cuda_stream)
     _lib.check(st)
     return out, lse
+
+
+def _autograd_function():
+    import torch
+
+    class _Attention(torch.autograd.Function):
+        """O = attention(q, k, v) with the library's forward and backward kernels;
+        O and LSE are saved for the backward (the page's recomputation from the
+        saved log-sum-exp)."""
+
+        @staticmethod
+        def forward(ctx, q, k, v, scale, causal):
+            o, lse = fwd(q, k, v, scale=scale, causal=causal)
+            ctx.save_for_backward(q, k, v, o, lse)
+            ctx.scale, ctx.causal = scale, causal
+            return o
+
+        @staticmethod
+        def backward(ctx, do):
+            q, k, v, o, lse = ctx.saved_tensors
+            dq, dk, dv, _ = bwd(q, k, v, o, lse, do.contiguous() if do.stride(-1) != 1 else do,
+                                scale=ctx.scale, causal=ctx.causal)
+            return dq, dk, dv, None, None
+
+    return _Attention
+
+
+_ATTENTION = None
+
+
+def attention(q, k, v, scale=None, causal=False):
+    """Differentiable exact attention: ``fwd`` forward, ``bwd`` backward
+    (torch.autograd).  q [B,H,Sq,D], k, v [B,H,Skv,D], fp16 or bf16 CUDA
+    tensors with the last dimension contiguous.  Returns O."""
+    global _ATTENTION
+    if _ATTENTION is None:
+        _ATTENTION = _autograd_function()
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    return _ATTENTION.apply(q, k, v, float(scale), bool(causal))

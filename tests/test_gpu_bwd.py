@@ -186,3 +186,19 @@ def test_bwd_strided_unequal_lengths_vs_oracle(ea, oracle_mod, causal):
     for name, a, r in zip(("dq", "dk", "dv", "delta"), got, ref):
         e = rel_err(a.float().cpu().numpy().astype(np.float64), r)
         assert e <= TOL_G[dtype], f"{name}: {e:.3e}"
+
+
+@pytest.mark.parametrize("D,dtype,causal", [(64, "bf16", True), (128, "fp16", False), (256, "fp16", True)])
+def test_autograd_wrapper(ea, oracle_mod, D, dtype, causal):
+    # attention() through torch.autograd gives the oracle's gradients
+    import torch
+    q, k, v, do = gen(1, 2, 130, 200, D, dtype, seed=D + 9)
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    dev = [to_dev(x, dtype).requires_grad_(True) for x in (q, k, v)]
+    out = ea.attention(*dev, scale=scale, causal=causal)
+    out.backward(to_dev(do, dtype))
+    torch.cuda.synchronize()
+    dq_ref, dk_ref, dv_ref, _ = oracle_mod.attn_bwd(q, k, v, do, dtype, scale, causal)
+    for name, t, r in zip(("dq", "dk", "dv"), dev, (dq_ref, dk_ref, dv_ref)):
+        e = rel_err(t.grad.float().cpu().numpy().astype(np.float64), r)
+        assert e <= TOL_G[dtype], f"{name}: {e:.3e}"
