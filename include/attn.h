@@ -1,27 +1,37 @@
 /*
- * attn.h -- C ABI of the MI355X (gfx950) exact attention forward library.
+ * attn.h -- C ABI of the MI355X (gfx950) exact attention library.
  *
- * The operation is the fused, tiled, exact scaled-dot-product attention
- * forward described on the docs.rs page "oxicuda-dnn 0.1.8,
- * src/attn/flash_attn/hopper.rs" (doc comment of
- * FlashAttention3Plan::generate_forward): scores S = Q K^T scaled by the
- * softmax scale, future positions removed when causal, an online softmax with
- * a running max m and running sum l, O = (P V) / l, and the per-row
- * log-sum-exp m + log(l).  The S x S score matrix never reaches memory.
+ * The operation is the fused, tiled, exact scaled-dot-product attention of
+ * the docs.rs page "oxicuda-dnn 0.1.8, src/attn/flash_attn/hopper.rs":
+ *   forward (doc comment of FlashAttention3Plan::generate_forward): scores
+ *   S = Q K^T scaled by the softmax scale, future positions removed when
+ *   causal, an online softmax with a running max m and running sum l,
+ *   O = (P V) / l, and the per-row log-sum-exp m + log(l); the S x S score
+ *   matrix never reaches memory;
+ *   backward (doc comment of generate_backward): dQ, dK, dV recomputing P
+ *   from the saved log-sum-exp.
+ *
+ * Entry points: attn_fwd (contiguous), attn_fwd_strided (strides, Sq != Skv),
+ * attn_bwd / attn_bwd_strided (backward), attn_fwd_variant (other copy
+ * schedules, for A/B measurements), attn_fwd_unfused (an unfused comparator
+ * that sends S through memory), and host-only planning helpers.
  *
  * Conventions shared by every entry point:
- *   - Tensors are dense and contiguous, C order: Q, K, V, O are [B, H, S, D]
- *     of 16-bit elements (fp16 or bf16, chosen by `dtype`); LSE is [B, H, S]
- *     of fp32.  The caller owns every buffer; the library allocates no device
- *     memory and keeps no pointer after a call returns.
- *   - Causal keeps key j for query i iff j <= i (attn_fwd: Sq == Skv == S;
- *     attn_fwd_strided aligns the last query with the last key).
+ *   - Q, K, V, O (and dQ, dK, dV, dO) are [B, H, rows, D] of 16-bit elements
+ *     (fp16 or bf16, chosen by `dtype`), contiguous C order unless an entry
+ *     point takes strides; LSE (and D_i) are [B, H, Sq] fp32, contiguous.
+ *   - The caller owns every buffer and keeps no pointer from a call.  The
+ *     kernels use no memory beyond the caller's buffers (and the workspace
+ *     attn_fwd_unfused takes); the one allocation the library makes is the
+ *     vendor BLAS handle attn_fwd_unfused creates per device on first use.
+ *   - Causal keeps key j for query i iff j <= i + (Skv - Sq): j <= i when
+ *     Sq == Skv, and in general the last query sees the last key.
  *   - LSE is the natural logarithm of sum_j exp(scale * q_i . k_j) over the
  *     kept keys.
  *   - Status codes are returned, never thrown; attn_last_error() gives a
  *     thread-local text for the most recent failure on the calling thread.
  *   - All argument checks happen before any HIP call.  A failed check
- *     launches nothing and leaves o and lse untouched.
+ *     launches nothing and leaves every output untouched.
  */
 #ifndef EXACT_ATTENTION_52_AMD_ATTN_H
 #define EXACT_ATTENTION_52_AMD_ATTN_H
