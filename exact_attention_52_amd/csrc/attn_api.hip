@@ -42,11 +42,15 @@ int ok() {
   return ATTN_OK;
 }
 
-// Per-head-dim tile shapes.  All use two K/V LDS stages.
-//   D=64 : 4 query waves x 32 rows = 128 rows, 128-key tiles, 70 KiB LDS
-//   D=128: 8 query waves = 256 rows, 128-key tiles, 136 KiB LDS
-//   D=256: 2 query waves = 64 rows (the page's 64-row Q tile for D=256), each
-//          64-key tile split over 2 key waves, 138 KiB LDS
+// Per-head-dim tile shapes (TileCfg arguments: D, query waves, key waves,
+// keys per tile, ping-pong kernel, staggered copies).  All use two K/V LDS
+// stages.
+//   D=64 : kernel 1, 8 query waves x 32 rows = 256 rows, 128-key tiles,
+//          67 KiB LDS
+//   D=128: ping-pong kernel, 8 waves = 256 rows, 128-key tiles, 134 KiB LDS
+//   D=256: kernel 1 with staggered copies, 2 query waves = 64 rows (the
+//          page's 64-row Q tile for D=256), each 64-key tile split over 2
+//          key waves, 134 KiB LDS
 #ifndef ATTN_CFG64
 #define ATTN_CFG64 64, 8, 1, 128, false
 #endif

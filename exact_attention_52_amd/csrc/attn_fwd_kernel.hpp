@@ -917,6 +917,7 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(const Problem p) {
 // read through an empty buffer descriptor: they fetch nothing and fill a
 // stage no later phase reads.
 // ---------------------------------------------------------------------------
+// MFMAs between two copy instructions in group 0's MFMA block
 #ifndef ATTN_LSTRIDE
 #define ATTN_LSTRIDE 3
 #endif
