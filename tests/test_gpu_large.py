@@ -1,6 +1,6 @@
 """Largest sizes: long sequences (one head near the 32-bit per-head offset
-range the kernels use), a grid of 2^18 heads, and the backward at S = 2^17,
-checked on outputs the oracle computes one by one (sampled query rows,
+range the kernels use), a grid of 2^18 heads, the backward at S = 2^17
+(2^16 for D = 256) and over 2^16 short heads, checked on outputs the oracle computes one by one (sampled query rows,
 sampled keys few queries see) and on identities that hold at any size.
 
 Inputs here are seeded standard normals from numpy's PCG64 (not the Philox
@@ -62,10 +62,9 @@ def test_forward_largest_sizes(ea, oracle_mod, B, H, S, D, dtype, causal):
     assert el <= TOL_LSE, f"max dLSE {el:.3e}"
 
 
-@pytest.mark.parametrize("D,dtype", [(128, "fp16"), (64, "bf16")])
-def test_backward_long_causal_sequence(ea, oracle_mod, D, dtype):
+@pytest.mark.parametrize("D,dtype,S", [(128, "fp16", 1 << 17), (64, "bf16", 1 << 17), (256, "bf16", 1 << 16)])
+def test_backward_long_causal_sequence(ea, oracle_mod, D, dtype, S):
     import torch
-    S = 1 << 17
     print(f"large bwd S={S} D={D} {dtype} causal", flush=True)
     q, k, v, do = (words((1, 1, S, D), dtype, seed=11 + i) for i in range(4))
     scale = float(np.float32(1.0 / math.sqrt(D)))
@@ -105,3 +104,20 @@ def test_backward_long_causal_sequence(ea, oracle_mod, D, dtype):
     dv_mag = dv.double().abs().sum(dim=2)[0, 0].cpu().numpy()
     assert np.all(np.abs(dv_sum - do_sum) <= 2 * U[dtype] * dv_mag + 1e-6), \
         (np.abs(dv_sum - do_sum) / dv_mag).max()
+
+
+def test_backward_many_heads(ea, oracle_mod):
+    # 2^16 heads of 7 rows: the grid and head arithmetic at scale, checked in full
+    import torch
+    B, H, S, D, dtype = 64, 1024, 7, 64, "fp16"
+    q, k, v, do = (words((B, H, S, D), dtype, seed=21 + i) for i in range(4))
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    dev = [to_dev(x, dtype) for x in (q, k, v, do)]
+    o, lse = ea.fwd(*dev[:3], scale=scale, causal=False)
+    got = ea.bwd(*dev[:3], o, lse, dev[3], scale=scale, causal=False)
+    torch.cuda.synchronize()
+    ref = oracle_mod.attn_bwd(q, k, v, do, dtype, scale, False)
+    tol = 4 * U[dtype]
+    for name, g, r in zip(("dq", "dk", "dv", "delta"), got, ref):
+        g = g.float().cpu().numpy().astype(np.float64)
+        assert np.abs(g - r).max() <= tol * max(1.0, np.abs(r).max()), name
