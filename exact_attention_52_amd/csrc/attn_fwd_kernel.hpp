@@ -586,6 +586,8 @@ struct Wave {
 
   // O = O_acc / l (RNE to 16 bits), LSE = (m + log2 l) ln 2.
   // A row with no key (causal, Sq > Skv) has l = 0: O = 0 and LSE = -inf.
+  // The accumulator layout gives each lane 8-byte pieces of its one row, so
+  // a store instruction writes 16 bytes into each of 32 rows.
   __device__ __forceinline__ void epilogue(const HeadView& hv) {
     const float l_tot = sum_halves(l_run);
     const float lr_tot = sum_halves(lr_sum());
@@ -606,6 +608,62 @@ struct Wave {
       if (half == 0)
         hv.lse[my_q] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f;
     }
+  }
+
+  // The same through LDS: the wave writes its 32 rows of O into `stage`
+  // (EPI_BYTES of LDS that no other wave and no copy touches), reads them
+  // back as whole rows and stores 16 contiguous bytes per lane, so one store
+  // instruction covers 1024 / (2D) complete rows: 8x fewer memory requests
+  // than the direct form.
+  static constexpr int EPI_RS = 2 * D + 16;      // staged row stride (bytes)
+  static constexpr int EPI_BYTES = 32 * EPI_RS;  // one wave's staging area
+  __device__ __forceinline__ void epilogue_staged(const HeadView& hv, uint8_t* stage) {
+    const float l_tot = sum_halves(l_run);
+    const float lr_tot = sum_halves(lr_sum());
+    const float inv = lr_tot > 0.f ? 1.0f / lr_tot : 0.f;
+    uint8_t* mine = stage + (lane & 31) * EPI_RS;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = db * 32 + 8 * g + 4 * half;
+        u32x2 w;
+        w[0] = E::pack2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv);
+        w[1] = E::pack2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+        *reinterpret_cast<u32x2*>(mine + 2 * d) = w;
+      }
+    }
+    // a wave's LDS accesses execute in order; keep the compiler from moving
+    // the reads above the writes
+    __asm__ volatile("" ::: "memory");
+    constexpr int LPR = D / 8;     // lanes per row, 16 bytes each
+    constexpr int RPI = 64 / LPR;  // rows per store instruction
+    const int rl = lane / LPR, cl = lane % LPR;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = i * RPI + rl;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * EPI_RS + 16 * cl);
+      if (wq_first + r < Sq) *reinterpret_cast<u32x4*>(hv.o + (int64_t)(wq_first + r) * hv.o_ss + 8 * cl) = v;
+    }
+    if (my_q < Sq && half == 0)
+      hv.lse[my_q] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f;
+  }
+};
+
+// Staging areas of the staged epilogue: the K/V stage arrays, which no step
+// reads once the key loop is over, cut into AREA-byte pieces in the order
+// k0, k1, v0, v1 (array sizes NK0 .. NV1 bytes).  Piece w goes to wave w.
+template <int AREA, int NK0, int NK1, int NV0, int NV1>
+struct EpiAreas {
+  static constexpr int P0 = NK0 / AREA, P1 = NK1 / AREA, P2 = NV0 / AREA, P3 = NV1 / AREA;
+  static constexpr int TOTAL = P0 + P1 + P2 + P3;
+  static __device__ __forceinline__ uint8_t* pick(int w, uint8_t* k0, uint8_t* k1, uint8_t* v0, uint8_t* v1) {
+    if (w < P0) return k0 + w * AREA;
+    w -= P0;
+    if (w < P1) return k1 + w * AREA;
+    w -= P1;
+    if (w < P2) return v0 + w * AREA;
+    return v1 + (w - P2) * AREA;
   }
 };
 
@@ -844,10 +902,17 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(const Problem p) {
     wait_loads();
     return;
   }
+  // Staged epilogue where the stage arrays hold a piece for every writing
+  // wave (with a key split, only the kw = 0 waves write, and their pieces
+  // must lie in the K arrays: the merge below reads partials from V stages).
+  using Areas = EpiAreas<Wave<C, CAUSAL, DT>::EPI_BYTES, C::K_TILE, C::STAGES >= 2 ? C::K_TILE : 16, C::V_TILE,
+                         C::STAGES >= 2 ? C::V_TILE : 16>;
+  constexpr bool STAGED = C::KW == 1 ? Areas::TOTAL >= C::NW
+                                     : ((C::KW - 1) * C::QW <= 2 && Areas::P0 + Areas::P1 >= C::QW);
   wait_loads();  // the (empty) copies issued past the last tile
-  // the key-split merge below reuses the V stages: every wave's copies must
-  // have landed before any wave writes there
-  if constexpr (C::KW > 1) __syncthreads();
+  // the key-split merge and the staged epilogue reuse the stage arrays: every
+  // wave's copies must have landed before any wave writes there
+  if constexpr (C::KW > 1 || STAGED) __syncthreads();
 
   // merge the key-split waves (KW > 1): partials of wave (kw, qw), kw > 0,
   // go to slot (kw - 1) * QW + qw: the V stages, then the K stages
@@ -893,7 +958,10 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(const Problem p) {
     }
   }
 
-  w.epilogue(hv);
+  if constexpr (STAGED)
+    w.epilogue_staged(hv, Areas::pick(qw, kt0, kt1, vt0, vt1));
+  else
+    w.epilogue(hv);
 }
 
 // ---------------------------------------------------------------------------
@@ -1042,7 +1110,10 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_pingpong_kernel(const Problem 
     loop(std::false_type{});
   }
 
-  w.epilogue(hv);
+  // the loop's last barrier has passed: every wave is done with LDS
+  using Areas = EpiAreas<Wave<C, CAUSAL, DT>::EPI_BYTES, C::K_TILE, C::K_TILE, C::V_TILE, C::V_TILE>;
+  static_assert(Areas::TOTAL >= 8, "the staged epilogue needs a piece per wave");
+  w.epilogue_staged(hv, Areas::pick(wave, kt0, kt1, vt0, vt1));
 }
 
 }  // namespace attn
