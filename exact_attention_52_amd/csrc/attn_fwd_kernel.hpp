@@ -264,7 +264,10 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_
 }
 
 // 16 bytes per lane from global memory straight into LDS at lds + 16*lane;
-// the source is byte_off (per lane) + wave_off (wave-uniform, an SGPR).
+// the source is byte_off (per lane) + wave_off (wave-uniform, an SGPR).  On
+// gfx950 the buffer range check covers the sum of both: a lane whose 16 bytes
+// lie past the descriptor's end writes zeros (measured with a NaN-filled tail
+// past the tensor), so the wave-uniform row offset can stay in a scalar.
 __device__ __forceinline__ void load16_lds(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t byte_off,
                                            uint32_t wave_off = 0) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, (int)byte_off, (int)wave_off, 0, 0);
