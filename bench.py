@@ -6,6 +6,10 @@ stream, score MFMA, mask, online softmax, PV MFMA, epilogue) over one batch of
 seeded synthetic input of the headline workload, by default
 B=2, H=16, S=4096, D=128, fp16, non-causal, Q,K ~ 2 N(0,1), V ~ N(0,1).
 
+Defaults: 100 untimed warm-up launches, then 100 timed ones (about 25 ms
+each at c4): the clock settles only after a few dozen back-to-back launches
+of a fresh process, and a shorter warm-up would average over that ramp.
+
 Prints ONE JSON line.  `value` is TFLOP/s with FLOPs = 4*B*H*S^2*D (halved when
 causal) and the inputs already resident in HBM.  The roofline object uses the
 average kernel duration from HIP events recorded around every launch of the
@@ -276,8 +280,11 @@ def cpu_baseline(shape, words, target_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    # the card's clock ramps over a process's first few dozen launches
+    # (c4: ~340 us per launch for the first 20, ~265 for the next 20, a
+    # steady ~241 from about the 60th on), so the default warm-up covers it
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true", help="skip timing the other workloads")
