@@ -384,6 +384,8 @@ struct Wave {
   int lane, half, wq_first, wq_last, my_q, kbase, Sq, Skv, koff, k_lane, v_lane;
   float c;
 
+  // LOAD_Q = false leaves qf to copy_q / read_q below
+  template <bool LOAD_Q = true>
   __device__ __forceinline__ void init(const HeadView& hv, int q_first, int kbase_, float c_) {
     lane = threadIdx.x & 63;
     const int col = lane & 31;
@@ -399,10 +401,12 @@ struct Wave {
     // lane parts of the operand read addresses (the rest are immediates)
     k_lane = C::k_off(kbase + col) + half * 16;
     v_lane = C::v_off(kbase + 4 * half + ((lane & 15) >> 2)) + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(hv.q, rows_bytes(Sq, hv.q_ss, D));
-    const uint32_t off = (uint32_t)(my_q * hv.q_ss + half * 8) * 2;  // rows >= Sq read 0
+    if constexpr (LOAD_Q) {
+      const __amdgpu_buffer_rsrc_t qr = make_rsrc(hv.q, rows_bytes(Sq, hv.q_ss, D));
+      const uint32_t off = (uint32_t)(my_q * hv.q_ss + half * 8) * 2;  // rows >= Sq read 0
 #pragma unroll
-    for (int kc = 0; kc < DK; ++kc) qf[kc] = load16(qr, off + kc * 32);
+      for (int kc = 0; kc < DK; ++kc) qf[kc] = load16(qr, off + kc * 32);
+    }
 #pragma unroll
     for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
     m_run = -__builtin_inff();
@@ -411,6 +415,31 @@ struct Wave {
     l_run = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) lr4[e] = 0.f;
+  }
+
+  // Q through LDS.  Loaded straight into the fragment, a load instruction
+  // reads 32 bytes from each of 32 rows; instead the wave copies its 32 rows
+  // HBM -> LDS as whole rows (one copy instruction moves 1 KiB, Q_RPL
+  // complete rows) and reads the fragment from there.  Line L of the area
+  // (Q_LINES lines of 1 KiB + 16 bytes of padding) holds rows L, L + Q_LINES,
+  // ..., so the 16-byte fragment reads of 8 consecutive rows hit distinct
+  // banks.  Rows >= Sq read as 0.
+  static constexpr int Q_RPL = 1024 / (2 * D);  // rows per line
+  static constexpr int Q_LINES = 32 / Q_RPL;
+  static constexpr int Q_LINE = 1024 + 16;
+  static constexpr int Q_BYTES = Q_LINES * Q_LINE;
+  __device__ __forceinline__ void copy_q(const HeadView& hv, uint8_t* area) const {
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(hv.q, rows_bytes(Sq, hv.q_ss, D));
+    const int m = lane / (D / 8), chunk = lane % (D / 8);
+#pragma unroll
+    for (int L = 0; L < Q_LINES; ++L)
+      load16_lds(qr, area + L * Q_LINE, (uint32_t)((wq_first + L + Q_LINES * m) * hv.q_ss) * 2u + 16u * chunk);
+  }
+  __device__ __forceinline__ void read_q(const uint8_t* area) {
+    const int col = lane & 31;
+    const uint8_t* src = area + (col % Q_LINES) * Q_LINE + (col / Q_LINES) * (2 * D) + 16 * half;
+#pragma unroll
+    for (int kc = 0; kc < DK; ++kc) qf[kc] = *reinterpret_cast<const u32x4*>(src + 32 * kc);
   }
 
   // P of a tile this wave skips: the next pv then adds exact zeros
@@ -1017,8 +1046,11 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_pingpong_kernel(const Problem 
   const int q0 = (int)tile64 * BM;
   const HeadView hv = head_view(p, bh64);
 
+  // with two stages the V stage arrays are free until the first iteration
+  // copies V_0: the waves stage their Q rows there
+  constexpr bool STAGE_Q = ST == 2 && 4 * Wave<C, CAUSAL, DT>::Q_BYTES <= C::V_TILE;
   Wave<C, CAUSAL, DT> w;
-  w.init(hv, q0 + wave * 32, 0, p.c);
+  w.template init<!STAGE_Q>(hv, q0 + wave * 32, 0, p.c);
 
   // key tiles this workgroup needs (none when causal leaves its rows no key)
   const int q_end = (q0 + BM < hv.Sq) ? q0 + BM : hv.Sq;
@@ -1093,6 +1125,8 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_pingpong_kernel(const Problem 
     }
   };
 
+  uint8_t* const q_area = (wave < 4 ? vt0 : vt1) + (wave & 3) * Wave<C, CAUSAL, DT>::Q_BYTES;
+  if constexpr (STAGE_Q) w.copy_q(hv, q_area);
   if (group == 0) {
     const __amdgpu_buffer_rsrc_t rk0 = kcp.tile(0, true);
 #pragma unroll
@@ -1106,6 +1140,10 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_pingpong_kernel(const Problem 
   }
   wait_loads();
   __syncthreads();
+  if constexpr (STAGE_Q) {
+    w.read_q(q_area);
+    __syncthreads();  // every wave holds its Q before V_0 is copied over the areas
+  }
   if (group == 0) {
     loop(std::true_type{});
   } else {
