@@ -138,7 +138,9 @@ struct TileCfg {
   static constexpr int V_TILE = LINES * V_LINE;
   static constexpr int KV_LDS_BYTES = STAGES * (K_TILE + V_TILE);
   static constexpr int LOADS_PER_WAVE = LINES / NW;      // K lines (and V lines) per wave
-  static constexpr int LDS_BYTES = KV_LDS_BYTES;
+  // plus, with a key split, the per-row l, m and rounded-P sums of the
+  // merged partials
+  static constexpr int LDS_BYTES = KV_LDS_BYTES + (KW > 1 ? (KW - 1) * QW * 3 * 64 * 4 : 0);
 
   // byte offset of tile row `row` inside a K / V tile
   static constexpr __host__ __device__ int k_off(int row) {
@@ -936,44 +938,52 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(const Problem p) {
   }
   // Staged epilogue where the stage arrays hold a piece for every writing
   // wave (with a key split, only the kw = 0 waves write, and their pieces
-  // must lie in the K arrays: the merge below reads partials from V stages).
+  // must lie in the K arrays: with two or more stages the merge below reads
+  // partials from V stages only; with one it uses kt0 too).
   using Areas = EpiAreas<Wave<C, CAUSAL, DT>::EPI_BYTES, C::K_TILE, C::STAGES >= 2 ? C::K_TILE : 16, C::V_TILE,
                          C::STAGES >= 2 ? C::V_TILE : 16>;
   constexpr bool STAGED = C::KW == 1 ? Areas::TOTAL >= C::NW
-                                     : ((C::KW - 1) * C::QW <= 2 && Areas::P0 + Areas::P1 >= C::QW);
+                                     : (C::STAGES >= 2 && (C::KW - 1) * C::QW <= 2 && Areas::P0 + Areas::P1 >= C::QW);
   wait_loads();  // the (empty) copies issued past the last tile
   // the key-split merge and the staged epilogue reuse the stage arrays: every
   // wave's copies must have landed before any wave writes there
   if constexpr (C::KW > 1 || STAGED) __syncthreads();
 
-  // merge the key-split waves (KW > 1): partials of wave (kw, qw), kw > 0,
-  // go to slot (kw - 1) * QW + qw: the V stages, then the K stages
+  // merge the key-split waves (KW > 1): the O partial of wave (kw, qw),
+  // kw > 0, goes to slot (kw - 1) * QW + qw of the stage arrays (vt0, vt1,
+  // kt0, kt1 with two or more stages; vt0, kt0 with one), its l, m and
+  // rounded-P sum to a small array of their own
   if constexpr (C::KW > 1) {
-    constexpr int FIELDS = D / 2 + 3;
-    static_assert((C::KW - 1) * C::QW <= 4 && FIELDS * 64 * 4 <= C::V_TILE &&
-                      ((C::KW - 1) * C::QW <= 2 || FIELDS * 64 * 4 <= C::K_TILE),
+    constexpr int NSLOT = (C::KW - 1) * C::QW;
+    constexpr int SLOTS = C::STAGES >= 2 ? 4 : 2;
+    constexpr int OBYTES = D / 2 * 64 * 4;  // one wave's O partial
+    static_assert(NSLOT <= SLOTS && OBYTES <= C::V_TILE && (NSLOT <= SLOTS / 2 || OBYTES <= C::K_TILE),
                   "merge area too small");
+    __shared__ float mscal[NSLOT][3][64];
     auto slot = [&](int i) __attribute__((always_inline)) -> uint8_t* {
+      if constexpr (SLOTS == 2) return i == 0 ? vt0 : kt0;
       return i == 0 ? vt0 : i == 1 ? vt1 : i == 2 ? kt0 : kt1;
     };
     if (kw > 0) {
-      float* dst = reinterpret_cast<float*>(slot((kw - 1) * C::QW + qw));
+      const int sl = (kw - 1) * C::QW + qw;
+      float* dst = reinterpret_cast<float*>(slot(sl));
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) dst[(db * 16 + i) * 64 + lane] = w.oacc[db][i];
-      dst[(D / 2) * 64 + lane] = w.l_run;
-      dst[(D / 2 + 1) * 64 + lane] = w.m_run;
-      dst[(D / 2 + 2) * 64 + lane] = w.lr_sum();
+      mscal[sl][0][lane] = w.l_run;
+      mscal[sl][1][lane] = w.m_run;
+      mscal[sl][2][lane] = w.lr_sum();
     }
     __syncthreads();
     if (kw > 0) return;
 #pragma unroll
     for (int ww = 1; ww < C::KW; ++ww) {
-      const float* src = reinterpret_cast<const float*>(slot((ww - 1) * C::QW + qw));
-      const float lb = src[(D / 2) * 64 + lane];
-      const float mb = src[(D / 2 + 1) * 64 + lane];
-      const float lrb = src[(D / 2 + 2) * 64 + lane];
+      const int sl = (ww - 1) * C::QW + qw;
+      const float* src = reinterpret_cast<const float*>(slot(sl));
+      const float lb = mscal[sl][0][lane];
+      const float mb = mscal[sl][1][lane];
+      const float lrb = mscal[sl][2][lane];
       const float mm = fmaxf(w.m_run, mb);
       const float mref = (mm == -__builtin_inff()) ? 0.f : mm;
       const float fa = __builtin_amdgcn_exp2f(w.m_run - mref);
