@@ -798,8 +798,25 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(const Problem p) {
   const int q0 = (int)tile64 * BM;
   const HeadView hv = head_view(p, bh64);
 
-  Wave<C, CAUSAL, DT> w;
-  if (!producer) w.init(hv, q0 + qw * 32, kw * C::KSUB, p.c);
+  // Q through LDS where a second K/V stage exists: the loop's first iteration
+  // writes it (the staggered schedule: vt1 only), so the waves stage their Q
+  // rows there first, one slice per query wave shared by its key waves
+  using W = Wave<C, CAUSAL, DT>;
+  constexpr int QPK = C::K_TILE / W::Q_BYTES, QPV = C::V_TILE / W::Q_BYTES;  // slices per array
+  constexpr bool STAGE_Q = !C::PRODUCER && C::STAGES == 2 && (C::STAGGER ? QPV >= C::QW : QPK + QPV >= C::QW);
+  W w;
+  if (!producer) w.template init<!STAGE_Q>(hv, q0 + qw * 32, kw * C::KSUB, p.c);
+  uint8_t* const q_area =
+      C::STAGGER ? vt1 + qw * W::Q_BYTES : (qw < QPK ? kt1 + qw * W::Q_BYTES : vt1 + (qw - QPK) * W::Q_BYTES);
+  // after the copies of the first tiles (and the barrier that ends them):
+  // every wave reads its fragment, and a second barrier keeps the loop's
+  // copies into those arrays behind all the reads
+  auto read_staged_q = [&]() __attribute__((always_inline)) {
+    if constexpr (STAGE_Q) {
+      w.read_q(q_area);
+      __syncthreads();
+    }
+  };
 
   // key tiles this workgroup needs (none when causal leaves its rows no key)
   const int q_end = (q0 + BM < hv.Sq) ? q0 + BM : hv.Sq;
@@ -857,8 +874,10 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(const Problem p) {
 #pragma unroll
       for (int i = 0; i < LPW; ++i) k0(i), v0(i), k1(i);
     }
+    if (STAGE_Q && kw == 0) w.copy_q(hv, q_area);
     wait_loads();
     __syncthreads();
+    read_staged_q();
     for (int j = 0; j < n; j += 2) {
       iter(j, kt0, vt0, vt1);
       if (j + 1 < n) iter(j + 1, kt1, vt1, vt0);
@@ -899,7 +918,9 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(const Problem p) {
     } else if constexpr (C::STAGES == 2) {
       // tile j+1 is copied while tile j is computed; one barrier per tile
       fetch(0, kt0, vt0);
+      if (STAGE_Q && kw == 0) w.copy_q(hv, q_area);
       __syncthreads();
+      read_staged_q();
       for (int j = 0; j < n; j += 2) {
         if (j + 1 < n) fetch(j + 1, kt1, vt1);
         compute(j, kt0, vt0);
