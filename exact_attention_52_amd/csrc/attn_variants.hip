@@ -8,8 +8,9 @@
 //   3: 3 LDS stages  (copy tile j+2 while computing tile j; counted waits)
 //   4: 2 LDS stages, plus one producer wave that issues every HBM -> LDS copy
 //      while the other waves only compute
-// D=64: 8 computing waves x 32 query rows, 128-key tiles (the shipped D=64
-// shape); D=128: 4 computing waves, 64-key tiles (so that 3 stages fit).
+// D=64: 8 computing waves x 32 query rows, 128-key tiles (one workgroup per
+// CU; attn_fwd itself runs 4-wave, 128-row workgroups at D=64, two per CU);
+// D=128: 4 computing waves, 64-key tiles (so that 3 stages fit).
 #include "attn_variants.hpp"
 
 namespace attn {
