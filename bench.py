@@ -9,6 +9,9 @@ B=2, H=16, S=4096, D=128, fp16, non-causal, Q,K ~ 2 N(0,1), V ~ N(0,1).
 Defaults: 100 untimed warm-up launches, then 100 timed ones (about 25 ms
 each at c4): the clock settles only after a few dozen back-to-back launches
 of a fresh process, and a shorter warm-up would average over that ramp.
+Every forward warm-up (the headline's and each other workload's) also lasts
+at least 30 ms of wall time, however short the launches; the JSON line
+reports the warm-up launches actually run.
 
 Prints ONE JSON line.  `value` is TFLOP/s with FLOPs = 4*B*H*S^2*D (halved when
 causal) and the inputs already resident in HBM.  The roofline object uses the
@@ -101,8 +104,31 @@ def make_inputs(name, seed=0):
     return (B, H, S, D, dtype, causal), (q, k, v), dev
 
 
+# The card's clock settles only after some tens of milliseconds of
+# back-to-back work, whatever the number of launches that takes, so every
+# forward warm-up runs at least `warmup` launches and at least this long.
+MIN_WARM_MS = 30.0
+
+
+def warm_up(launch, warmup, min_ms=MIN_WARM_MS):
+    """Runs launch() at least `warmup` times and for at least min_ms of wall
+    time (in batches of up to 10, synchronised); returns the launch count."""
+    import torch
+    done = 0
+    t_start = time.perf_counter()
+    while True:
+        n = min(10, warmup - done) if done < warmup else 10
+        for _ in range(n):
+            launch()
+        done += n
+        torch.cuda.synchronize()
+        if done >= warmup and (time.perf_counter() - t_start) * 1e3 >= min_ms:
+            return done
+
+
 def time_workload(ea, shape, dev, steps, warmup):
-    """Returns (ms_per_step over the timed region, mean per-launch ms)."""
+    """Returns (ms_per_step over the timed region, mean per-launch ms, o, lse,
+    warm-up launches run)."""
     import torch
     B, H, S, D, dtype, causal = shape
     scale = float(np.float32(1.0 / math.sqrt(D)))
@@ -110,8 +136,7 @@ def time_workload(ea, shape, dev, steps, warmup):
     o = torch.empty_like(q)
     lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
     stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        ea.fwd(q, k, v, scale=scale, causal=causal, out=o, lse=lse, stream=stream)
+    warmed = warm_up(lambda: ea.fwd(q, k, v, scale=scale, causal=causal, out=o, lse=lse, stream=stream), warmup)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -125,7 +150,7 @@ def time_workload(ea, shape, dev, steps, warmup):
     torch.cuda.synchronize()
     total = t0.elapsed_time(t1)
     per = [a.elapsed_time(b) for a, b in ev]
-    return total / steps, float(np.mean(per)), o, lse
+    return total / steps, float(np.mean(per)), o, lse, warmed
 
 
 def bwd_flops(B, H, S, D, causal, gemms=5):
@@ -313,7 +338,7 @@ def main():
 
     shape, words, dev = make_inputs(args.workload)
     B, H, S, D, dtype, causal = shape
-    ms_step, ms_kernel, o, lse = time_workload(ea, shape, dev, args.steps, args.warmup)
+    ms_step, ms_kernel, o, lse, warmed = time_workload(ea, shape, dev, args.steps, args.warmup)
     f = flops(B, H, S, D, causal)
     value = f / (ms_step * 1e-3) / 1e12
     achieved = f / (ms_kernel * 1e-3) / 1e12
@@ -366,7 +391,7 @@ def main():
             if name == args.workload:
                 continue
             shp, _, dv = make_inputs(name)
-            ms_s, ms_k, _, _ = time_workload(ea, shp, dv, max(5, args.steps // 2), max(2, args.warmup // 2))
+            ms_s, ms_k, _, _, _ = time_workload(ea, shp, dv, max(5, args.steps // 2), max(2, args.warmup // 2))
             fl = flops(shp[0], shp[1], shp[2], shp[3], shp[5])
             others[name] = {"us_per_call": round(ms_k * 1e3, 2),
                             "tflops": round(fl / (ms_k * 1e-3) / 1e12, 1),
@@ -397,6 +422,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_launches_run": warmed,
+        "warmup_min_ms": MIN_WARM_MS,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
