@@ -43,19 +43,21 @@ int ok() {
 }
 
 // Per-head-dim tile shapes (TileCfg arguments: D, query waves, key waves,
-// keys per tile, ping-pong kernel, staggered copies).  All use two K/V LDS
-// stages.
-//   D=64 : kernel 1, 4 query waves x 32 rows = 128 rows, 128-key tiles,
-//          66.5 KiB LDS: two workgroups share a CU, so one's transitions
-//          (prologue, output, launch) overlap the other's loop, and the two
-//          waves on a SIMD belong to different workgroups and do not meet at
-//          the same barriers (8 waves of 256 rows: one workgroup per CU)
-//   D=128: ping-pong kernel, 8 waves = 256 rows, 128-key tiles, 133 KiB LDS
-//   D=256: kernel 1 with staggered copies, 2 query waves = 64 rows (the
-//          page's 64-row Q tile for D=256), each 64-key tile split over 2
-//          key waves, 134.5 KiB LDS (with the key-split merge's row sums)
+// keys per tile, ping-pong kernel, staggered copies, K/V LDS stages).
+//   D=64 : kernel 1, 4 query waves x 32 rows = 128 rows, 128-key tiles, one
+//          K/V stage: 34 KiB of LDS and 164 VGPRs, so three workgroups share
+//          a CU (three waves per SIMD).  Each one's copy waits, prologue and
+//          output overlap the others' loops, and the waves on a SIMD belong
+//          to different workgroups, so they do not meet at the same barriers
+//          and fill each other's MFMA and VALU gaps.
+//   D=128: ping-pong kernel, 8 waves = 256 rows, 128-key tiles, two stages,
+//          133 KiB LDS
+//   D=256: kernel 1 with staggered copies over two stages, 2 query waves =
+//          64 rows (the page's 64-row Q tile for D=256), each 64-key tile
+//          split over 2 key waves, 134.5 KiB LDS (with the key-split merge's
+//          row sums)
 #ifndef ATTN_CFG64
-#define ATTN_CFG64 64, 4, 1, 128, false
+#define ATTN_CFG64 64, 4, 1, 128, false, false, 1
 #endif
 #ifndef ATTN_CFG128
 #define ATTN_CFG128 128, 8, 1, 128, true
