@@ -44,9 +44,9 @@ int ok() {
 
 // Per-head-dim tile shapes (TileCfg arguments: D, query waves, key waves,
 // keys per tile, ping-pong kernel, staggered copies, K/V LDS stages).
-//   D=64 : kernel 1, 4 query waves x 32 rows = 128 rows, 128-key tiles, one
-//          K/V stage: 34 KiB of LDS and 164 VGPRs, so three workgroups share
-//          a CU (three waves per SIMD).  Each one's copy waits, prologue and
+//   D=64 : kernel 1, 4 query waves x 32 rows = 128 rows, 64-key tiles, two
+//          K/V stages: 35 KiB of LDS and 114 VGPRs, so four workgroups share
+//          a CU (four waves per SIMD).  Each one's copy waits, prologue and
 //          output overlap the others' loops, and the waves on a SIMD belong
 //          to different workgroups, so they do not meet at the same barriers
 //          and fill each other's MFMA and VALU gaps.
@@ -57,7 +57,7 @@ int ok() {
 //          split over 2 key waves, 134.5 KiB LDS (with the key-split merge's
 //          row sums)
 #ifndef ATTN_CFG64
-#define ATTN_CFG64 64, 4, 1, 128, false, false, 1
+#define ATTN_CFG64 64, 4, 1, 64, false, false, 2
 #endif
 #ifndef ATTN_CFG128
 #define ATTN_CFG128 128, 8, 1, 128, true

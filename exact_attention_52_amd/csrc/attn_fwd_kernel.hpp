@@ -105,7 +105,10 @@ struct Elem<DT_BF16> {
 // LDS (256 bytes per bank sweep):
 //   K: line L of a 16-line block holds rows L, L+16, L+32, ... (pad 16 B), so
 //      the 16 consecutive rows read by one 16-lane quarter of a 16-byte
-//      operand read sit 16 bytes apart modulo 256;
+//      operand read sit 16 bytes apart modulo 256; a tile of fewer lines
+//      (8 at D=64 with 64 keys) forms one block of all its lines, rows L,
+//      L+8, ..., and the 8 rows that one 128-byte read cycle serves still
+//      fall in distinct 16-byte slots;
 //   V: line L of a 4-line block holds rows L, L+4, ... (pad 64 B), so the 4
 //      consecutive rows of a transposing read, 64 bytes wide across two
 //      16-lane groups, sit 64 bytes apart modulo 256.
@@ -142,20 +145,23 @@ struct TileCfg {
   // merged partials
   static constexpr int LDS_BYTES = KV_LDS_BYTES + (KW > 1 ? (KW - 1) * QW * 3 * 64 * 4 : 0);
 
+  // K lines form blocks of KB lines (16, or all the lines of a smaller
+  // tile); line L of a block holds rows L, L + KB, ...
+  static constexpr int KB = LINES < 16 ? LINES : 16;
   // byte offset of tile row `row` inside a K / V tile
   static constexpr __host__ __device__ int k_off(int row) {
-    return (row / (16 * RPL)) * 16 * K_LINE + (row % 16) * K_LINE + ((row % (16 * RPL)) / 16) * ROW_BYTES;
+    return (row / (KB * RPL)) * KB * K_LINE + (row % KB) * K_LINE + ((row % (KB * RPL)) / KB) * ROW_BYTES;
   }
   static constexpr __host__ __device__ int v_off(int row) {
     return (row / (4 * RPL)) * 4 * V_LINE + (row % 4) * V_LINE + ((row % (4 * RPL)) / 4) * ROW_BYTES;
   }
   // first tile row of load line n (the line's rows step by 16 for K, 4 for V)
-  static constexpr __host__ __device__ int k_line_row(int n) { return (n / 16) * 16 * RPL + n % 16; }
+  static constexpr __host__ __device__ int k_line_row(int n) { return (n / KB) * KB * RPL + n % KB; }
   static constexpr __host__ __device__ int v_line_row(int n) { return (n / 4) * 4 * RPL + n % 4; }
 
   static_assert(D % 32 == 0 && RPL >= 1, "head dim must be a multiple of 32, at most 512");
   static_assert(KSUB % 32 == 0 && NB >= 1, "each wave needs whole 32-key blocks");
-  static_assert(BN % (16 * RPL) == 0, "tile must hold whole K line blocks");
+  static_assert(BN % (KB * RPL) == 0 && KB >= 8, "tile must hold whole K line blocks of >= 8 lines");
   static_assert(LINES % NW == 0, "load lines must split evenly over the waves");
   static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per CU");
   static_assert(STAGES >= 1 && STAGES <= 3, "1 to 3 K/V stages");
@@ -702,13 +708,13 @@ struct EpiAreas {
 };
 
 // HBM -> LDS copies of K or V tiles of one head.  Line n of a tile holds rows
-// (first row of line n) + STEP*m (STEP 16 for K, 4 for V); lane i of a copy
+// (first row of line n) + STEP*m (STEP = KB for K, 4 for V); lane i of a copy
 // instruction carries row STEP*(i / (D/8)) of the line and 16-byte chunk
 // i % (D/8).  Rows at or past `rows` (the key length) fall outside the buffer
 // descriptor and read as 0, as does a whole tile the caller marks invalid.
 template <class C, bool IS_K>
 struct TileCopier {
-  static constexpr int D = C::D, STEP = IS_K ? 16 : 4, LINE = IS_K ? C::K_LINE : C::V_LINE;
+  static constexpr int D = C::D, STEP = IS_K ? C::KB : 4, LINE = IS_K ? C::K_LINE : C::V_LINE;
   const uint16_t* src;  // the head's first row
   int ss;               // row stride (elements)
   int rows;             // key length

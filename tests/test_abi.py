@@ -75,8 +75,7 @@ def test_plan_rules(D, S):
     assert p["threads_per_workgroup"] == 64 * p["waves_q"] * p["waves_k"]
     assert bm == 32 * p["waves_q"]
     assert p["lds_bytes"] <= 160 * 1024
-    # one K/V stage at D=64 (three workgroups share a CU), two otherwise
-    assert p["kv_stages"] == (1 if D == 64 else 2)
+    assert p["kv_stages"] == 2
     if D == 256:
         assert bm == 64  # the 64-row query tile of the D=256 workload
 
