@@ -16,8 +16,14 @@ reports the warm-up launches actually run.
 Prints ONE JSON line.  `value` is TFLOP/s with FLOPs = 4*B*H*S^2*D (halved when
 causal) and the inputs already resident in HBM.  The roofline object uses the
 average kernel duration from HIP events recorded around every launch of the
-timed region on the stream the kernel runs on.  The CPU baseline times the
-fp64 oracle on a bounded sample of rows of the same workload.
+timed region on the stream the kernel runs on; `launch_stats` gives their
+mean, median, min and max.  `shader_clock` is the GFX clock sampled while the
+headline kernel runs back to back right after the timed region.
+
+The CPU leg runs after all GPU timing: the fp64 oracle, as it stands, over
+every row of every timed workload (`cpu_baseline` is its rate on the headline
+workload, with the thread count), and every O and LSE element of each GPU run
+compared against it (`parity`, and `parity` of each other workload).
 
 The `backward` object times attn_bwd (dQ, dK, dV and D_i for a seeded dO)
 on the same inputs, with the forward's O and LSE: TFLOP/s at the usual
@@ -127,7 +133,7 @@ def warm_up(launch, warmup, min_ms=MIN_WARM_MS):
 
 
 def time_workload(ea, shape, dev, steps, warmup):
-    """Returns (ms_per_step over the timed region, mean per-launch ms, o, lse,
+    """Returns (ms_per_step over the timed region, per-launch ms list, o, lse,
     warm-up launches run)."""
     import torch
     B, H, S, D, dtype, causal = shape
@@ -150,7 +156,90 @@ def time_workload(ea, shape, dev, steps, warmup):
     torch.cuda.synchronize()
     total = t0.elapsed_time(t1)
     per = [a.elapsed_time(b) for a, b in ev]
-    return total / steps, float(np.mean(per)), o, lse, warmed
+    return total / steps, per, o, lse, warmed
+
+
+def launch_stats(per_ms):
+    """Per-launch durations (HIP events around each launch) in microseconds."""
+    a = np.asarray(per_ms, dtype=np.float64) * 1e3
+    return {"launches": int(a.size), "mean_us": round(float(a.mean()), 2),
+            "median_us": round(float(np.median(a)), 2), "min_us": round(float(a.min()), 2),
+            "max_us": round(float(a.max()), 2)}
+
+
+class ClockSampler:
+    """The shader (GFX) clock of cuda:0 read through amdsmi (the library behind
+    amd-smi) from a sampling thread while kernels run back to back.  Reporting
+    only: any failure leaves the reading None with the reason."""
+
+    def __init__(self):
+        self.handle, self.error, self.api = None, None, None
+        try:
+            import amdsmi
+            import torch
+            amdsmi.amdsmi_init(amdsmi.AmdSmiInitFlags.INIT_AMD_GPUS)
+            prop = torch.cuda.get_device_properties(0)
+            want = (prop.pci_domain_id, prop.pci_bus_id, prop.pci_device_id)
+            for h in amdsmi.amdsmi_get_processor_handles():
+                dom, bus, rest = amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")
+                if (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
+                    self.handle = h
+            if self.handle is None:
+                self.error = "no amdsmi device has cuda:0's PCI address"
+            self.api = amdsmi
+        except Exception as e:  # noqa: BLE001 -- reporting only
+            self.error = f"amdsmi unavailable: {e}"
+
+    def read_mhz(self):
+        """Mean of the per-XCD current GFX clocks (MHz), or the GFX clock."""
+        m = self.api.amdsmi_get_gpu_metrics_info(self.handle)
+        clks = m.get("current_gfxclks")
+        if isinstance(clks, (list, tuple)):
+            vals = [float(c) for c in clks if isinstance(c, (int, float)) and 0 < c < 10000]
+            if vals:
+                return sum(vals) / len(vals)
+        c = m.get("current_gfxclk")
+        if isinstance(c, (int, float)) and 0 < c < 10000:
+            return float(c)
+        return float(self.api.amdsmi_get_clock_info(self.handle, self.api.AmdSmiClkType.GFX)["clk"])
+
+    def during(self, launch, ms=200.0, period_s=0.002):
+        """Runs launch() back to back for about `ms` of wall time (synchronised
+        every 20 launches) while a thread samples the clock; returns a dict."""
+        import threading
+
+        import torch
+        if self.handle is None:
+            return {"mhz_median": None, "error": self.error}
+        samples, errs, stop = [], [], threading.Event()
+
+        def loop():
+            while not stop.is_set():
+                try:
+                    samples.append(self.read_mhz())
+                except Exception as e:  # noqa: BLE001
+                    errs.append(str(e))
+                    return
+                time.sleep(period_s)
+
+        th = threading.Thread(target=loop, daemon=True)
+        n, t0 = 0, time.perf_counter()
+        th.start()
+        while (time.perf_counter() - t0) * 1e3 < ms:
+            for _ in range(20):
+                launch()
+            n += 20
+            torch.cuda.synchronize()
+        stop.set()
+        th.join()
+        if not samples:
+            return {"mhz_median": None, "error": errs[0] if errs else "no samples"}
+        a = np.asarray(samples)
+        return {"mhz_median": round(float(np.median(a)), 1), "mhz_min": round(float(a.min()), 1),
+                "mhz_max": round(float(a.max()), 1), "samples": int(a.size), "launches": n,
+                "window_ms": round((time.perf_counter() - t0) * 1e3, 1),
+                "source": "amdsmi gpu_metrics current_gfxclks (mean over XCDs), sampled every 2 ms "
+                          "while the kernel ran back to back after the timed region"}
 
 
 def bwd_flops(B, H, S, D, causal, gemms=5):
@@ -258,48 +347,41 @@ def reference_gemm(n, steps=50):
             "us_per_call": round(ms * 1e3, 1), "tflops": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)}
 
 
-def parity_spot_check(shape, words, o, lse, n_rows=128):
+def full_oracle(shape, words):
+    """The fp64 oracle, as it stands, over every row of the workload; returns
+    (O, LSE, wall seconds)."""
     import oracle
-    from exact_attention_52_amd import inputs
     B, H, S, D, dtype, causal = shape
     scale = float(np.float32(1.0 / math.sqrt(D)))
-    rng = np.random.default_rng(123)
-    rows = np.unique(np.concatenate([[0, B * H * S - 1], rng.integers(0, B * H * S, n_rows)]))
-    o_ref, l_ref = oracle.attn_fwd(*words, dtype, scale, causal, rows=rows)
-    og = o.float().cpu().numpy().reshape(-1, D)[rows].astype(np.float64)
-    lg = lse.cpu().numpy().reshape(-1)[rows].astype(np.float64)
-    eo = float(np.abs(og - o_ref).max())
-    el = float((np.abs(lg - l_ref) / np.maximum(1.0, np.abs(l_ref))).max())
+    t = time.perf_counter()
+    o_ref, l_ref = oracle.attn_fwd(*words, dtype, scale, causal)
+    return o_ref, l_ref, time.perf_counter() - t
+
+
+def parity_all(shape, o_host, lse_host, o_ref, l_ref):
+    """Every O and LSE element of the GPU output against the oracle's."""
+    B, H, S, D, dtype, causal = shape
+    eo = float(np.abs(o_host.astype(np.float64) - o_ref).max())
+    el = float((np.abs(lse_host.astype(np.float64) - l_ref) / np.maximum(1.0, np.abs(l_ref))).max())
     tol = 2e-3 if dtype == "fp16" else 1.6e-2
-    return {"rows": int(rows.size), "max_abs_err_o": eo, "max_err_lse": el,
+    return {"rows": int(B * H * S), "elements_o": int(o_ref.size), "max_abs_err_o": eo, "max_err_lse": el,
             "tol_o": tol, "tol_lse": 1e-4, "ok": bool(eo <= tol and el <= 1e-4)}
 
 
-def cpu_baseline(shape, words, target_s=12.0):
-    """The fp64 oracle, as it stands, on a bounded sample of rows."""
+def oracle_rate(shape, seconds):
+    """The oracle's rate in the GPU figure's FLOP convention (4*D per query-key
+    pair, exactly halved for causal)."""
     import oracle
     B, H, S, D, dtype, causal = shape
-    scale = float(np.float32(1.0 / math.sqrt(D)))
-    total_rows = B * H * S
-    rng = np.random.default_rng(7)
-    probe = rng.choice(total_rows, size=min(256, total_rows), replace=False)
-    t = time.perf_counter()
-    oracle.attn_fwd(*words, dtype, scale, causal, rows=probe)
-    dt = max(time.perf_counter() - t, 1e-6)
-    n = int(min(total_rows, max(probe.size, probe.size * target_s / dt)))
-    rows = rng.choice(total_rows, size=n, replace=False)
-    t = time.perf_counter()
-    oracle.attn_fwd(*words, dtype, scale, causal, rows=rows)
-    dt = time.perf_counter() - t
-    i = rows % S
-    keys = (i + 1) if causal else np.full(rows.size, S)
-    # same FLOP convention as the GPU figure: 4*D per (query, kept key) pair,
-    # counted as the exact-half convention for causal
-    fl = float(4.0 * D * (keys.sum() if not causal else rows.size * S / 2))
-    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"{rows.size} random query rows of {total_rows} ({rows.size / total_rows:.2%}) "
-                      f"of the same workload, fp64 two-pass oracle, {dt:.1f} s wall"}
+    fl = flops(B, H, S, D, causal)
+    return {"value": fl / seconds / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(seconds, 2),
+            "sample": f"all {B * H * S} query rows of the workload (100%), fp64 two-pass oracle, "
+                      f"{seconds:.1f} s wall on {oracle.num_threads()} threads"}
+
+
+def host(o, lse):
+    return o.float().cpu().numpy(), lse.cpu().numpy()
 
 
 def main():
@@ -311,7 +393,12 @@ def main():
     # steady ~241 from about the 60th on), so the default warm-up covers it
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=HEADLINE)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU leg: the timed fp64 oracle over every workload and the "
+                         "comparison of every output element against it")
+    ap.add_argument("--clock-ms", type=float, default=200.0,
+                    help="after the timed region, run the headline kernel back to back this long "
+                         "while sampling the shader clock (0: skip)")
     ap.add_argument("--no-others", action="store_true", help="skip timing the other workloads")
     ap.add_argument("--ref-gemm", type=int, default=8192,
                     help="also time an fp16 N^3 torch.matmul as context for the MFMA roofline (0: skip)")
@@ -338,12 +425,24 @@ def main():
 
     shape, words, dev = make_inputs(args.workload)
     B, H, S, D, dtype, causal = shape
-    ms_step, ms_kernel, o, lse, warmed = time_workload(ea, shape, dev, args.steps, args.warmup)
+    ms_step, per, o, lse, warmed = time_workload(ea, shape, dev, args.steps, args.warmup)
+    stats = launch_stats(per)
+    ms_kernel = stats["mean_us"] * 1e-3
     f = flops(B, H, S, D, causal)
     value = f / (ms_step * 1e-3) / 1e12
     achieved = f / (ms_kernel * 1e-3) / 1e12
-    print(f"# {args.workload}: {ms_step * 1e3:.1f} us/step, kernel {ms_kernel * 1e3:.1f} us, "
+    print(f"# {args.workload}: {ms_step * 1e3:.1f} us/step, kernel {stats}, "
           f"{achieved:.1f} TFLOP/s ({achieved / PEAK_TFLOPS:.1%} of peak)", file=sys.stderr, flush=True)
+    outputs = {args.workload: (shape, words, *host(o, lse))}
+
+    clock = None
+    if args.clock_ms > 0:
+        scale = float(np.float32(1.0 / math.sqrt(D)))
+        stream = torch.cuda.current_stream()
+        clock = ClockSampler().during(
+            lambda: ea.fwd(*dev, scale=scale, causal=causal, out=o, lse=lse, stream=stream), ms=args.clock_ms)
+        print(f"# shader clock: {clock}", file=sys.stderr, flush=True)
+    del o, lse
 
     if args.calib_copy_mib:
         # a plain streaming kernel of known traffic for HBM-counter calibration:
@@ -355,9 +454,6 @@ def main():
         torch.add(src, 1.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
-
-    parity = parity_spot_check(shape, words, o, lse)
-    print(f"# parity spot check: {parity}", file=sys.stderr, flush=True)
 
     backward = None
     if not args.no_backward:
@@ -372,7 +468,7 @@ def main():
         print(f"# backward: {backward}", file=sys.stderr, flush=True)
         del outs, ddo
 
-    unfused = None
+    unfused, unfused_out = None, None
     if not args.no_unfused:
         ms_u, o_u, lse_u = time_unfused(ea, shape, dev, max(5, args.steps // 5), 2)
         nb = unfused_bytes(B, H, S, D)
@@ -380,22 +476,28 @@ def main():
                    "tflops": round(f / (ms_u * 1e-3) / 1e12, 1),
                    "hbm_bytes_min": nb, "hbm_bound_us": round(nb / 8e12 * 1e6, 1),
                    "achieved_gbps_of_min": round(nb / (ms_u * 1e-3) / 1e9, 1),
-                   "fused_speedup": round(ms_u / ms_kernel, 2),
-                   "parity_spot_check": parity_spot_check(shape, words, o_u, lse_u)}
+                   "fused_speedup": round(ms_u / ms_kernel, 2)}
+        unfused_out = host(o_u, lse_u)
         print(f"# unfused comparator: {unfused}", file=sys.stderr, flush=True)
         del o_u, lse_u
+    del dev
+    torch.cuda.empty_cache()
 
     others = {}
     if not args.no_others:
         for name in inputs.WORKLOADS:
             if name == args.workload:
                 continue
-            shp, _, dv = make_inputs(name)
-            ms_s, ms_k, _, _, _ = time_workload(ea, shp, dv, max(5, args.steps // 2), max(2, args.warmup // 2))
+            shp, wds, dv = make_inputs(name)
+            _, per_o, o_o, l_o, _ = time_workload(ea, shp, dv, max(5, args.steps // 2), max(2, args.warmup // 2))
+            st = launch_stats(per_o)
             fl = flops(shp[0], shp[1], shp[2], shp[3], shp[5])
-            others[name] = {"us_per_call": round(ms_k * 1e3, 2),
-                            "tflops": round(fl / (ms_k * 1e-3) / 1e12, 1),
-                            "frac_of_peak": round(fl / (ms_k * 1e-3) / 1e12 / PEAK_TFLOPS, 4)}
+            t_us = st["mean_us"]
+            others[name] = {"us_per_call": t_us, "launch_stats": st,
+                            "tflops": round(fl / (t_us * 1e-6) / 1e12, 1),
+                            "frac_of_peak": round(fl / (t_us * 1e-6) / 1e12 / PEAK_TFLOPS, 4)}
+            outputs[name] = (shp, wds, *host(o_o, l_o))
+            del o_o, l_o
             if not args.no_backward:
                 _, ddo = make_do(shp)
                 ms_b, _ = time_backward(ea, shp, dv, ddo, max(5, args.steps // 5), 2)
@@ -411,9 +513,26 @@ def main():
     if gemm:
         print(f"# reference gemm: {gemm}", file=sys.stderr, flush=True)
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(shape, words)
-    if cpu:
-        print(f"# cpu baseline: {cpu}", file=sys.stderr, flush=True)
+    # The CPU leg, after all GPU timing: the fp64 oracle over every row of
+    # each timed workload, timed, and every output element of the GPU run
+    # compared against it.
+    cpu, parity = None, None
+    if not args.no_cpu_baseline:
+        for name, (shp, wds, o_h, l_h) in outputs.items():
+            o_ref, l_ref, secs = full_oracle(shp, wds)
+            par = parity_all(shp, o_h, l_h, o_ref, l_ref)
+            rate = oracle_rate(shp, secs)
+            print(f"# {name}: oracle {secs:.2f} s on {rate['cores']} threads; parity {par}",
+                  file=sys.stderr, flush=True)
+            if name == args.workload:
+                cpu, parity = rate, par
+                if unfused_out is not None:
+                    unfused["parity"] = parity_all(shp, *unfused_out, o_ref, l_ref)
+            else:
+                others[name]["parity"] = par
+                others[name]["cpu_oracle"] = {k: rate[k] for k in ("value", "unit", "cores", "seconds")}
+            del o_ref, l_ref
+    del outputs
 
     line = {
         "metric": METRIC,
@@ -437,8 +556,10 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
                      "traffic": read_traffic(),
                      "algorithmic_min_hbm_bytes": min_bytes(B, H, S, D)},
+        "launch_stats": stats,
+        "shader_clock": clock,
         "cpu_baseline": cpu,
-        "parity_spot_check": parity,
+        "parity": parity,
         "backward": backward,
         "unfused": unfused,
         "other_workloads": others,

@@ -8,7 +8,8 @@ natural-log LSE per row (fp32).  ``bwd(q, k, v, o, lse, do, ...)`` returns
 ``attention(q, k, v, scale, causal)`` wraps both as a torch.autograd function.
 PyTorch only provides device memory and the
 stream; the computation is the libattn.so gfx950 kernel behind the C ABI of
-include/attn.h.  ``inputs`` holds the seeded synthetic-input generator.
+include/attn.h (the unfused comparator ``fwd_unfused``: libattn_unfused.so,
+include/attn_unfused.h).  ``inputs`` holds the seeded synthetic-input generator.
 """
 from __future__ import annotations
 
@@ -179,13 +180,14 @@ def fwd_unfused(q, k, v, scale=None, causal=False, out=None, lse=None, workspace
         st = _lib.attn_fwd_unfused(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                    workspace.data_ptr(), workspace.numel() * workspace.element_size(), B, H, S,
                                    D, scale, causal, dt, stream.cuda_stream)
-    _lib.check(st)
+    _lib.check_unfused(st)
     return out, lse
 
 
 def fwd_variant(q, k, v, variant, scale=None, causal=False, out=None, lse=None, stream=None):
     """``fwd`` on contiguous [B,H,S,D] tensors with copy schedule ``variant``
-    (0: shipped; 1/2/3: K/V LDS stages; 4: 2 stages plus a producer wave).
+    (0: shipped; 1/2/3: K/V LDS stages; 4: 2 stages plus a producer wave;
+    5/6: the shipped tile shape with 1 or 2 stages and no ping-pong).
     Returns (o, lse)."""
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):

@@ -1,5 +1,6 @@
-"""ctypes binding of libattn.so: the C ABI of include/attn.h, one Python name
-per exported symbol.  Argument marshalling only; every step of the attention
+"""ctypes binding of libattn.so (the C ABI of include/attn.h) and of
+libattn_unfused.so (include/attn_unfused.h), one Python name per exported
+symbol.  Argument marshalling only; every step of the attention
 runs in the library's gfx950 kernels."""
 from __future__ import annotations
 
@@ -7,7 +8,7 @@ import ctypes
 import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 ATTN_F16, ATTN_BF16 = 0, 1
 STATUS = {
@@ -16,9 +17,10 @@ STATUS = {
     5: "ATTN_ERR_MISALIGNED", 6: "ATTN_ERR_BAD_SCALE", 7: "ATTN_ERR_ALIASING",
     8: "ATTN_ERR_UNSUPPORTED_DEVICE", 9: "ATTN_ERR_LAUNCH", 10: "ATTN_ERR_BAD_ARGUMENT",
 }
-EXPORTS = ("attn_fwd", "attn_fwd_strided", "attn_fwd_variant", "attn_bwd", "attn_bwd_strided", "attn_fwd_unfused",
-           "attn_fwd_unfused_workspace_bytes", "attn_fwd_plan", "attn_fwd_workgroup_tile",
-           "attn_status_string", "attn_last_error", "attn_abi_version")
+UNFUSED_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn_unfused.so")
+EXPORTS = ("attn_fwd", "attn_fwd_strided", "attn_fwd_variant", "attn_bwd", "attn_bwd_strided",
+           "attn_fwd_plan", "attn_fwd_workgroup_tile", "attn_status_string", "attn_last_error", "attn_abi_version")
+UNFUSED_EXPORTS = ("attn_fwd_unfused", "attn_fwd_unfused_workspace_bytes", "attn_unfused_last_error")
 
 
 class AttnError(RuntimeError):
@@ -64,10 +66,6 @@ def load():
     lib.attn_bwd_strided.restype = ci
     lib.attn_fwd_variant.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, cf, ci, ci, ci, vp]
     lib.attn_fwd_variant.restype = ci
-    lib.attn_fwd_unfused.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, cf, ci, ci, vp]
-    lib.attn_fwd_unfused.restype = ci
-    lib.attn_fwd_unfused_workspace_bytes.argtypes = [i64, i64, i64, i64]
-    lib.attn_fwd_unfused_workspace_bytes.restype = i64
     lib.attn_fwd_plan.argtypes = [i64, i64, i64, i64, ci, ci, ctypes.POINTER(Plan)]
     lib.attn_fwd_plan.restype = ci
     lib.attn_fwd_workgroup_tile.argtypes = [i64, i64, i64, i64, ci, ci, i64,
@@ -83,6 +81,41 @@ def load():
         raise ImportError(f"libattn.so ABI {lib.attn_abi_version()} != expected {ABI_VERSION}")
     _lib = lib
     return lib
+
+
+_unfused = None
+
+
+def load_unfused():
+    """Load libattn_unfused.so, the unfused comparator (its own library: the
+    fused libattn.so links no vendor BLAS); raise loudly if it is missing."""
+    global _unfused
+    if _unfused is not None:
+        return _unfused
+    load()  # the comparator shares libattn.so's status codes; both are built together
+    if not os.path.exists(UNFUSED_LIB_PATH):
+        raise ImportError(
+            f"{UNFUSED_LIB_PATH} is missing: build it with `python -m exact_attention_52_amd.build` "
+            "(or __graft_entry__.build()); there is no CPU or fallback path")
+    lib = ctypes.CDLL(UNFUSED_LIB_PATH)
+    i64, vp, ci, cf = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.attn_fwd_unfused.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, cf, ci, ci, vp]
+    lib.attn_fwd_unfused.restype = ci
+    lib.attn_fwd_unfused_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    lib.attn_fwd_unfused_workspace_bytes.restype = i64
+    lib.attn_unfused_last_error.argtypes = []
+    lib.attn_unfused_last_error.restype = ctypes.c_char_p
+    _unfused = lib
+    return lib
+
+
+def unfused_last_error() -> str:
+    return load_unfused().attn_unfused_last_error().decode()
+
+
+def check_unfused(status: int) -> None:
+    if status != 0:
+        raise AttnError(status, unfused_last_error())
 
 
 def last_error() -> str:
@@ -146,7 +179,7 @@ def attn_bwd_strided(q: int, k: int, v: int, o: int, lse: int, do: int, dq: int,
 
 def attn_fwd_variant(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, S: int, D: int,
                      scale: float, causal: bool, dtype: int, variant: int, stream: int) -> int:
-    """Raw call: attn_fwd with copy schedule `variant` (0..4); returns the status code."""
+    """Raw call: attn_fwd with copy schedule `variant` (0..6); returns the status code."""
     return load().attn_fwd_variant(q, k, v, o, lse, B, H, S, D, float(scale), int(bool(causal)), int(dtype),
                                    int(variant), stream)
 
@@ -154,12 +187,12 @@ def attn_fwd_variant(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, S
 def attn_fwd_unfused(q: int, k: int, v: int, o: int, lse: int, workspace: int, workspace_bytes: int, B: int,
                      H: int, S: int, D: int, scale: float, causal: bool, dtype: int, stream: int) -> int:
     """Raw call: device pointers as ints; returns the status code."""
-    return load().attn_fwd_unfused(q, k, v, o, lse, workspace, workspace_bytes, B, H, S, D, float(scale),
-                                   int(bool(causal)), int(dtype), stream)
+    return load_unfused().attn_fwd_unfused(q, k, v, o, lse, workspace, workspace_bytes, B, H, S, D, float(scale),
+                                           int(bool(causal)), int(dtype), stream)
 
 
 def attn_fwd_unfused_workspace_bytes(B: int, H: int, S: int, D: int) -> int:
-    return int(load().attn_fwd_unfused_workspace_bytes(B, H, S, D))
+    return int(load_unfused().attn_fwd_unfused_workspace_bytes(B, H, S, D))
 
 
 def attn_fwd_plan(B: int, H: int, S: int, D: int, causal: bool, dtype: int) -> dict:

@@ -18,29 +18,11 @@
 
 #include "attn.h"
 #include "attn_bwd.hpp"
+#include "attn_common.hpp"
 #include "attn_fwd_kernel.hpp"
-#include "attn_unfused.hpp"
 #include "attn_variants.hpp"
 
 namespace {
-
-thread_local std::string g_last_error;
-
-int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
-int fail(int status, const char* fmt, ...) {
-  char buf[512];
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(buf, sizeof buf, fmt, ap);
-  va_end(ap);
-  g_last_error = buf;
-  return status;
-}
-
-int ok() {
-  g_last_error.clear();
-  return ATTN_OK;
-}
 
 // Per-head-dim tile shapes (TileCfg arguments: D, query waves, key waves,
 // keys per tile, ping-pong kernel, staggered copies, K/V LDS stages).
@@ -56,18 +38,9 @@ int ok() {
 //          64 rows (the page's 64-row Q tile for D=256), each 64-key tile
 //          split over 2 key waves, 134.5 KiB LDS (with the key-split merge's
 //          row sums)
-#ifndef ATTN_CFG64
-#define ATTN_CFG64 64, 4, 1, 64, false, false, 2
-#endif
-#ifndef ATTN_CFG128
-#define ATTN_CFG128 128, 8, 1, 128, true
-#endif
-#ifndef ATTN_CFG256
-#define ATTN_CFG256 256, 2, 2, 64, false, true
-#endif
-using Cfg64 = attn::TileCfg<ATTN_CFG64>;
-using Cfg128 = attn::TileCfg<ATTN_CFG128>;
-using Cfg256 = attn::TileCfg<ATTN_CFG256>;
+using Cfg64 = attn::TileCfg<64, 4, 1, 64, false, false, 2>;
+using Cfg128 = attn::TileCfg<128, 8, 1, 128, true>;
+using Cfg256 = attn::TileCfg<256, 2, 2, 64, false, true>;
 
 template <class C>
 void fill_plan(int64_t B, int64_t H, int64_t S, attn_fwd_plan_t* p) {
@@ -82,29 +55,6 @@ void fill_plan(int64_t B, int64_t H, int64_t S, attn_fwd_plan_t* p) {
   p->num_workgroups = p->num_q_tiles * B * H;
 }
 
-int check_sizes(int64_t B, int64_t H, int64_t S, int64_t D, int dtype) {
-  if (B < 0 || H < 0 || S < 0)
-    return fail(ATTN_ERR_BAD_SHAPE, "B, H and S must be >= 0 (got B=%lld H=%lld S=%lld)",
-                (long long)B, (long long)H, (long long)S);
-  if (D != 64 && D != 128 && D != 256)
-    return fail(ATTN_ERR_UNSUPPORTED_HEAD_DIM, "head_dim %lld not supported; must be one of 64, 128, 256",
-                (long long)D);
-  if (dtype != ATTN_F16 && dtype != ATTN_BF16)
-    return fail(ATTN_ERR_UNSUPPORTED_DTYPE, "dtype %d not supported; must be ATTN_F16 (0) or ATTN_BF16 (1)",
-                dtype);
-  // Per-head offsets are 32-bit byte offsets (buffer loads); keep one head's
-  // S*D elements, plus a tile of padding, far inside that range.
-  const int64_t lim = (int64_t)1 << 30;
-  if (S > lim / D)
-    return fail(ATTN_ERR_BAD_SHAPE, "S=%lld too large for head_dim %lld", (long long)S, (long long)D);
-  if (B > 0 && H > 0 && S > 0) {
-    const int64_t bh_lim = ((int64_t)1 << 62) / (S * D);
-    if (H > bh_lim / (B > 0 ? B : 1) || B * H > bh_lim)
-      return fail(ATTN_ERR_BAD_SHAPE, "B*H*S*D overflows");
-  }
-  return ATTN_OK;
-}
-
 int plan_for(int64_t B, int64_t H, int64_t S, int64_t D, attn_fwd_plan_t* p) {
   switch (D) {
     case 64: fill_plan<Cfg64>(B, H, S, p); break;
@@ -114,36 +64,6 @@ int plan_for(int64_t B, int64_t H, int64_t S, int64_t D, attn_fwd_plan_t* p) {
   if (p->num_workgroups > (int64_t)0x7FFFFFFF)
     return fail(ATTN_ERR_BAD_SHAPE, "grid of %lld workgroups exceeds the launch limit",
                 (long long)p->num_workgroups);
-  return ATTN_OK;
-}
-
-bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
-  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
-  return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
-}
-
-// gfx950 check, cached per device.
-constexpr int kMaxDevices = 64;
-std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 yes, 2 no
-
-int check_device() {
-  int dev = -1;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess || dev < 0)
-    return fail(ATTN_ERR_UNSUPPORTED_DEVICE, "no current HIP device (%s)", hipGetErrorString(e));
-  int state = dev < kMaxDevices ? g_arch_ok[dev].load(std::memory_order_relaxed) : 0;
-  if (state == 0) {
-    hipDeviceProp_t prop;
-    e = hipGetDeviceProperties(&prop, dev);
-    if (e != hipSuccess)
-      return fail(ATTN_ERR_UNSUPPORTED_DEVICE, "hipGetDeviceProperties failed (%s)", hipGetErrorString(e));
-    state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
-    if (dev < kMaxDevices) g_arch_ok[dev].store(state, std::memory_order_relaxed);
-    if (state == 2)
-      return fail(ATTN_ERR_UNSUPPORTED_DEVICE, "device %d is %s; this library is built for gfx950 only", dev,
-                  prop.gcnArchName);
-  }
-  if (state == 2) return fail(ATTN_ERR_UNSUPPORTED_DEVICE, "device %d is not gfx950", dev);
   return ATTN_OK;
 }
 
@@ -231,8 +151,7 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int64_
                 (long long)B, (long long)H, (long long)Sq, (long long)Skv);
   int st = check_sizes(B, H, Sq > Skv ? Sq : Skv, D, dtype);
   if (st != ATTN_OK) return st;
-  if (!(std::isfinite(scale) && scale >= 0.f))
-    return fail(ATTN_ERR_BAD_SCALE, "scale must be finite and >= 0 (got %g)", (double)scale);
+  if (!std::isfinite(scale)) return fail(ATTN_ERR_BAD_SCALE, "scale must be finite (got %g)", (double)scale);
   if (B == 0 || H == 0 || Sq == 0) return ok();  // empty: nothing to compute
   // with no keys nothing is read from k or v, which may then be NULL
   if (!q || !o || !lse || (Skv > 0 && (!k || !v)))
@@ -266,12 +185,14 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int64_
   pr.q_ss = (int)vq.ss, pr.k_ss = (int)vk.ss, pr.v_ss = (int)vv.ss, pr.o_ss = (int)vo.ss;
   pr.Sq = (int)Sq, pr.Skv = (int)Skv, pr.H = (int)H, pr.nq = (int)plan.num_q_tiles;
   pr.G = plan.num_workgroups;
-  // scale * log2(e), kept >= FLT_MIN: a masked score (-inf) times c must stay
-  // -inf, never NaN, and for scale == 0 every kept score times FLT_MIN is far
-  // below one ulp of the row max, so the softmax is exactly uniform.
-  float c = (float)((double)scale * 1.4426950408889634074);
+  // |scale| * log2(e), kept >= FLT_MIN: a masked score (-inf) times c must
+  // stay -inf, never NaN, and for scale == 0 every kept score times FLT_MIN
+  // is far below one ulp of the row max, so the softmax is exactly uniform.
+  // A negative scale multiplies -Q (sign flips in registers, exact) by |scale|.
+  float c = (float)(std::fabs((double)scale) * 1.4426950408889634074);
   if (c < FLT_MIN) c = FLT_MIN;
   pr.c = c;
+  pr.qsign = scale < 0.f ? 0x80008000u : 0u;
   hipStream_t hs = (hipStream_t)stream;
   const bool cz = causal != 0;
   if (variant != 0) {
@@ -308,7 +229,7 @@ int attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float
   const int st = check_sizes(B, H, S, D, dtype);
   if (st != ATTN_OK) return st;
   if (variant < 0 || variant >= attn::kNumVariants || (variant > 0 && attn::variant_block_m((int)D, variant) == 0))
-    return fail(ATTN_ERR_BAD_ARGUMENT, "variant %d not available for head_dim %lld (0..%d for D 64 and 128, 0 for 256)",
+    return fail(ATTN_ERR_BAD_ARGUMENT, "variant %d not available for head_dim %lld (0..%d for D 64 and 128; 0, 5, 6 for 256)",
                 variant, (long long)D, attn::kNumVariants - 1);
   if (variant > 0 && B * H * ((S + attn::variant_block_m((int)D, variant) - 1) / attn::variant_block_m((int)D, variant)) >
                          0x7FFFFFFF)
@@ -351,8 +272,7 @@ int attn_bwd_strided(const void* q, const void* k, const void* v, const void* o,
                 (long long)B, (long long)H, (long long)Sq, (long long)Skv);
   int st = check_sizes(B, H, Sq > Skv ? Sq : Skv, D, dtype);
   if (st != ATTN_OK) return st;
-  if (!(std::isfinite(scale) && scale >= 0.f))
-    return fail(ATTN_ERR_BAD_SCALE, "scale must be finite and >= 0 (got %g)", (double)scale);
+  if (!std::isfinite(scale)) return fail(ATTN_ERR_BAD_SCALE, "scale must be finite (got %g)", (double)scale);
   if (B == 0 || H == 0 || (Sq == 0 && Skv == 0)) return ok();
   const bool has_q = Sq > 0, has_k = Skv > 0;
   if ((has_q && (!q || !o || !dO || !lse || !dq || !delta)) || (has_k && (!k || !v || !dk || !dv)))
@@ -415,8 +335,10 @@ int attn_bwd_strided(const void* q, const void* k, const void* v, const void* o,
   for (int i = 0; i < 8; ++i) *ps[i] = attn::Strides{vs[i].sb, vs[i].sh, (int)vs[i].ss};
   p.H = (int)H;
   p.Sq = (int)Sq, p.Skv = (int)Skv, p.nq = 0, p.nk = 0, p.BH = B * H;
+  // the backward masks P itself (never a score), so c may take any sign;
+  // a tiny positive c is kept >= FLT_MIN as in the forward
   float c = (float)((double)scale * 1.4426950408889634074);
-  p.c = c < FLT_MIN ? FLT_MIN : c;
+  p.c = (c >= 0.f && c < FLT_MIN) ? FLT_MIN : c;
   p.scale = scale;
   const hipError_t e = attn::bwd_launch(p, (int)D, causal != 0, dtype, (hipStream_t)stream);
   if (e != hipSuccess) return fail(ATTN_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
@@ -429,51 +351,6 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   // contiguous tensors: the strided entry with every stride array NULL
   return attn_bwd_strided(q, k, v, o, lse, dO, dq, dk, dv, delta, B, H, Sq, Skv, D, nullptr, nullptr, nullptr,
                           nullptr, nullptr, nullptr, nullptr, nullptr, scale, causal, dtype, stream);
-}
-
-int64_t attn_fwd_unfused_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t D) {
-  if (B < 0 || H < 0 || S < 0 || (D != 64 && D != 128 && D != 256)) return -1;
-  if (B == 0 || H == 0 || S == 0) return 0;
-  // B*H*S*(S+8+D+1)*6 must fit in int64 with room for the rounding
-  const int64_t lim = (int64_t)1 << 58;
-  if (S > (1 << 28) || H > lim / B || B * H > lim / S / (S + D + 9) / 6) return -1;
-  return attn::unfused_layout(B, H, S, D).bytes;
-}
-
-int attn_fwd_unfused(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
-                     int64_t workspace_bytes, int64_t B, int64_t H, int64_t S, int64_t D, float scale, int causal,
-                     int dtype, void* stream) {
-  int st = check_sizes(B, H, S, D, dtype);
-  if (st != ATTN_OK) return st;
-  if (!(std::isfinite(scale) && scale >= 0.f))
-    return fail(ATTN_ERR_BAD_SCALE, "scale must be finite and >= 0 (got %g)", (double)scale);
-  if (B == 0 || H == 0 || S == 0) return ok();
-  if (!q || !k || !v || !o || !lse || !workspace)
-    return fail(ATTN_ERR_NULL_PTR, "q, k, v, o, lse and workspace must be non-NULL");
-  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)workspace) & 15)
-    return fail(ATTN_ERR_MISALIGNED, "q, k, v, o and workspace must be 16-byte aligned");
-  if ((uintptr_t)lse & 3) return fail(ATTN_ERR_MISALIGNED, "lse must be 4-byte aligned");
-  const int64_t need = attn_fwd_unfused_workspace_bytes(B, H, S, D);
-  if (need < 0 || B * H > 0x7FFFFFFF || B * H * S > 0x7FFFFFFF)
-    return fail(ATTN_ERR_BAD_SHAPE, "B=%lld H=%lld S=%lld too large for the unfused path", (long long)B,
-                (long long)H, (long long)S);
-  if (workspace_bytes < need)
-    return fail(ATTN_ERR_BAD_ARGUMENT, "workspace of %lld bytes; %lld needed", (long long)workspace_bytes,
-                (long long)need);
-  const int64_t nt = B * H * S * D * 2, nl = B * H * S * 4;
-  if (overlaps(o, nt, q, nt) || overlaps(o, nt, k, nt) || overlaps(o, nt, v, nt) || overlaps(o, nt, lse, nl))
-    return fail(ATTN_ERR_ALIASING, "o overlaps q, k, v or lse");
-  if (overlaps(lse, nl, q, nt) || overlaps(lse, nl, k, nt) || overlaps(lse, nl, v, nt))
-    return fail(ATTN_ERR_ALIASING, "lse overlaps q, k or v");
-  for (const void* t : {(const void*)q, (const void*)k, (const void*)v, (const void*)o})
-    if (overlaps(workspace, need, t, nt)) return fail(ATTN_ERR_ALIASING, "workspace overlaps q, k, v or o");
-  if (overlaps(workspace, need, lse, nl)) return fail(ATTN_ERR_ALIASING, "workspace overlaps lse");
-  st = check_device();
-  if (st != ATTN_OK) return st;
-  const char* err = attn::unfused_launch(q, k, v, o, lse, workspace, B, H, S, D, scale, causal != 0, dtype,
-                                         (hipStream_t)stream);
-  if (err) return fail(ATTN_ERR_LAUNCH, "unfused path: %s", err);
-  return ok();
 }
 
 int attn_fwd_plan(int64_t B, int64_t H, int64_t S, int64_t D, int causal, int dtype, attn_fwd_plan_t* out) {

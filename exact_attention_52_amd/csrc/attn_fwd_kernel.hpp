@@ -64,16 +64,14 @@ struct Elem<DT_F16> {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
+  // x rounded to the nearest-even 16-bit value, back in fp32
+  static __device__ __forceinline__ float round(float x) { return (float)(_Float16)x; }
   // Two fp32 values -> packed 16-bit pair, round to nearest even.
   static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     f16x2 v;
     v[0] = (_Float16)lo;
     v[1] = (_Float16)hi;
     return __builtin_bit_cast(uint32_t, v);
-  }
-  // acc + lo + hi of a packed pair, in fp32 (v_dot2c_f32_f16 against (1, 1))
-  static __device__ __forceinline__ float add_pair(uint32_t pair, float acc) {
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), __builtin_bit_cast(f16x2, 0x3C003C00u), acc, false);
   }
 };
 
@@ -83,15 +81,12 @@ struct Elem<DT_BF16> {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
+  static __device__ __forceinline__ float round(float x) { return (float)(__bf16)x; }
   static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     bf16x2 v;
     v[0] = (__bf16)lo;
     v[1] = (__bf16)hi;
     return __builtin_bit_cast(uint32_t, v);
-  }
-  static __device__ __forceinline__ float add_pair(uint32_t pair, float acc) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), __builtin_bit_cast(bf16x2, 0x3F803F80u),
-                                           acc, false);
   }
 };
 
@@ -121,6 +116,11 @@ struct TileCfg {
   // extra wave issues every HBM -> LDS copy while the others only compute
   static constexpr int STAGES = STAGES_;
   static constexpr bool PRODUCER = PRODUCER_;
+  // Running-max policy of the softmax: exact at D = 128, where the ping-pong
+  // kernel rescales O^T in the MFMA phase nearly for free; lagging by up to
+  // kRescaleSlack elsewhere, where the rescale sits on the wave's own
+  // critical path (see Wave::softmax)
+  static constexpr bool EXACT_MAX = D_ == 128;
   static constexpr int D = D_;
   static constexpr int QW = QW_;             // waves along query rows
   static constexpr int KW = KW_;             // waves along each key tile
@@ -141,9 +141,9 @@ struct TileCfg {
   static constexpr int V_TILE = LINES * V_LINE;
   static constexpr int KV_LDS_BYTES = STAGES * (K_TILE + V_TILE);
   static constexpr int LOADS_PER_WAVE = LINES / NW;      // K lines (and V lines) per wave
-  // plus, with a key split, the per-row l, m and rounded-P sums of the
-  // merged partials
-  static constexpr int LDS_BYTES = KV_LDS_BYTES + (KW > 1 ? (KW - 1) * QW * 3 * 64 * 4 : 0);
+  // plus, with a key split, the per-row l, m, p_top and e_top of the merged
+  // partials
+  static constexpr int LDS_BYTES = KV_LDS_BYTES + (KW > 1 ? (KW - 1) * QW * 4 * 64 * 4 : 0);
 
   // K lines form blocks of KB lines (16, or all the lines of a smaller
   // tile); line L of a block holds rows L, L + KB, ...
@@ -283,7 +283,8 @@ __device__ __forceinline__ void load16_lds(__amdgpu_buffer_rsrc_t r, uint8_t* ld
 
 // Running-max hysteresis (log2 units): O, l are only rescaled when some row's
 // max grows by more than this; otherwise P is taken against the old max and
-// may reach 2^8, which fp16/bf16 P and fp32 sums hold exactly as well.
+// may reach 2^8, which fp16/bf16 P and fp32 sums hold with unchanged
+// relative precision.
 constexpr float kRescaleSlack = 8.0f;
 
 // Workgroup id -> (query tile, b*H + h).  Workgroups are handed to the 8 XCDs
@@ -330,7 +331,8 @@ struct Problem {
   int q_ss, k_ss, v_ss, o_ss;                              // row strides (>= D)
   int Sq, Skv, H, nq;                                      // nq query tiles per head
   int64_t G;                                               // workgroups
-  float c;                                                 // scale * log2(e), > 0
+  float c;                                                 // |scale| * log2(e), > 0
+  uint32_t qsign;  // 0x80008000 when scale < 0: Q is negated in registers
 };
 
 // One (b, h) of the problem.
@@ -342,6 +344,7 @@ struct HeadView {
   float* lse;
   int q_ss, k_ss, v_ss, o_ss;
   int Sq, Skv, koff;  // koff = Skv - Sq
+  uint32_t qsign;     // XOR mask of every 32-bit word of the Q fragment
 };
 
 __device__ __forceinline__ HeadView head_view(const Problem& p, int64_t bh) {
@@ -354,6 +357,7 @@ __device__ __forceinline__ HeadView head_view(const Problem& p, int64_t bh) {
   hv.lse = p.lse + bh * p.Sq;
   hv.q_ss = p.q_ss, hv.k_ss = p.k_ss, hv.v_ss = p.v_ss, hv.o_ss = p.o_ss;
   hv.Sq = p.Sq, hv.Skv = p.Skv, hv.koff = p.Skv - p.Sq;
+  hv.qsign = p.qsign;
   return hv;
 }
 
@@ -369,8 +373,8 @@ __device__ __forceinline__ uint32_t rows_bytes(int n, int ss, int D) {
 // A wave owns 32 query rows (one per lane column) and the kw-th slice of
 // every key tile.  Per tile j it runs
 //   qk(j)      S^T = K_j Q^T into sacc (MFMA),
-//   softmax(j) mask, running max, P = exp2(c*s - m) packed into pf, row sums
-//              (VALU),
+//   softmax(j) mask, running max, rescale factor, P = exp2(c*s - m) packed
+//              into pf, row sums (VALU),
 //   pv(j)      O^T += V_j^T P^T (MFMA),
 // in that order; the kernels below only decide how these steps of different
 // waves and tiles are interleaved.
@@ -383,14 +387,24 @@ struct Wave {
   f32x16 oacc[DB];   // O^T accumulator
   f32x16 sacc[NB];   // scores of the tile between qk and softmax
   u32x4 pf[2 * NB];  // packed P of the tile between softmax and pv
-  float m_run;       // running max of c*s (log2 units)
+  float m_run;       // reference max of c*s (log2 units), lagging the true
+                     // running max by less than kRescaleSlack
   float nm_ref;      // -m_run, or 0 while m_run is -inf: the exp2 offset
   float m_thr;       // m_run + kRescaleSlack: scores above it force a rescale
   float l_run;       // partial running sum of the fp32 P over this lane's keys
-  float lr4[4];      // the same sum over the P as rounded to 16 bits, in
-                     // four chains (one per word of a packed P register)
+  float p_top;       // the row's largest P so far (fp32) ...
+  float e_top;       // ... and round16(P) - P for it.  O is normalised by
+                     // (sum of P) + e_top: the dominant key's weight is then
+                     // the same rounded P the MFMA used (to first order the
+                     // error is sum over the other keys j of w_j d_j V_j, d_j
+                     // their relative rounding), while the plain fp32 sum
+                     // would add w* d* V* of the dominant key: 2.03e-3 on a
+                     // peaky fp16 row with |O| ~ 4.5, over the 2e-3 bound
+  float alpha;       // exp2(old m_run - new m_run) of the last softmax: the
+                     // factor O^T still owes when the rescale is deferred
   int lane, half, wq_first, wq_last, my_q, kbase, Sq, Skv, koff, k_lane, v_lane;
   float c;
+  uint32_t qsign;  // a negative scale is applied as -Q (exact) times |scale|
 
   // LOAD_Q = false leaves qf to copy_q / read_q below
   template <bool LOAD_Q = true>
@@ -406,6 +420,7 @@ struct Wave {
     Skv = hv.Skv;
     koff = hv.koff;
     c = c_;
+    qsign = hv.qsign;
     // lane parts of the operand read addresses (the rest are immediates)
     k_lane = C::k_off(kbase + col) + half * 16;
     v_lane = C::v_off(kbase + 4 * half + ((lane & 15) >> 2)) + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
@@ -413,7 +428,7 @@ struct Wave {
       const __amdgpu_buffer_rsrc_t qr = make_rsrc(hv.q, rows_bytes(Sq, hv.q_ss, D));
       const uint32_t off = (uint32_t)(my_q * hv.q_ss + half * 8) * 2;  // rows >= Sq read 0
 #pragma unroll
-      for (int kc = 0; kc < DK; ++kc) qf[kc] = load16(qr, off + kc * 32);
+      for (int kc = 0; kc < DK; ++kc) qf[kc] = load16(qr, off + kc * 32) ^ qsign;
     }
 #pragma unroll
     for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
@@ -421,8 +436,9 @@ struct Wave {
     nm_ref = 0.f;
     m_thr = -__builtin_inff();
     l_run = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) lr4[e] = 0.f;
+    p_top = 0.f;
+    e_top = 0.f;
+    alpha = 1.f;
   }
 
   // Q through LDS.  Loaded straight into the fragment, a load instruction
@@ -447,13 +463,15 @@ struct Wave {
     const int col = lane & 31;
     const uint8_t* src = area + (col % Q_LINES) * Q_LINE + (col / Q_LINES) * (2 * D) + 16 * half;
 #pragma unroll
-    for (int kc = 0; kc < DK; ++kc) qf[kc] = *reinterpret_cast<const u32x4*>(src + 32 * kc);
+    for (int kc = 0; kc < DK; ++kc) qf[kc] = *reinterpret_cast<const u32x4*>(src + 32 * kc) ^ qsign;
   }
 
-  // P of a tile this wave skips: the next pv then adds exact zeros
+  // P of a tile this wave skips: the next pv then adds exact zeros (and
+  // owes O^T no rescale)
   __device__ __forceinline__ void zero_pf() {
 #pragma unroll
     for (int i = 0; i < 2 * NB; ++i) pf[i] = u32x4{0u, 0u, 0u, 0u};
+    alpha = 1.f;
   }
 
   // does this wave have any unmasked key in tile j?
@@ -475,6 +493,9 @@ struct Wave {
     }
   }
 
+  // DEFER_RESCALE leaves the rescale of O^T to the caller (rescale_o()
+  // before the next pv), so that it can run next to MFMA work
+  template <bool DEFER_RESCALE = false>
   __device__ __forceinline__ void softmax(int j) {
     const int kv0 = j * BN + kbase;
     // mask keys past the end or after the query (diagonal / ragged tiles)
@@ -505,28 +526,31 @@ struct Wave {
     const float mx = max_halves(max_tree<16 * NB>(sc));
 
     // Rescale only when some row's max outgrew the reference by the slack
-    // (always on the first tile with an unmasked key, m_run being -inf
-    // before); the branch is uniform across the wave.  c > 0, so a fully
-    // masked max stays -inf and never turns into NaN.
+    // (0 with EXACT_MAX; always on the first tile with an unmasked key,
+    // m_run being -inf before); the branch is uniform across the wave.
+    // c > 0, so a fully masked max stays -inf and never turns into NaN.
     const float mt = mx * c;
+    if constexpr (DEFER_RESCALE) alpha = 1.f;
     if (__builtin_amdgcn_ballot_w64(mt > m_thr) != 0) {
       const float m_new = __builtin_elementwise_maximum(m_run, mt);
       const bool none = m_new == -__builtin_inff();
-      const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      const float a = none ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       nm_ref = none ? 0.f : -m_new;
-      m_thr = m_new + kRescaleSlack;
-      l_run *= alpha;
+      m_thr = m_new + (C::EXACT_MAX ? 0.f : kRescaleSlack);
+      l_run *= a;
+      p_top *= a;
+      e_top *= a;
+      if constexpr (DEFER_RESCALE) {
+        alpha = a;
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) lr4[e] *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+        for (int db = 0; db < DB; ++db) oacc[db] *= a;
+      }
     }
-
-    // P = exp2(c*s - m), rounded to nearest-even as the MFMA operand.  The
-    // fp32 row sum feeds the LSE (a sum of rounded P would move it by up to
-    // 2^-9 relative in bf16); the fp32 sum of the rounded P normalises O, so
-    // that its weights are exactly the ones V was multiplied by.
+    // P = exp2(c*s - m), rounded to nearest-even as the MFMA operand; the
+    // fp32 row sum of the unrounded P feeds the LSE and, with e_top, O's
+    // normaliser
     float ls[2 * NB];
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb) {
@@ -546,16 +570,22 @@ struct Wave {
 #pragma unroll
       for (int i = 0; i < w / 2; ++i) ls[i] += ls[i + w / 2];
     l_run += ls[0];
-    // the sums of the rounded P (v_dot2 here: issued between the wave's
-    // own MFMAs instead, they stall the MFMA stream)
-#pragma unroll
-    for (int i = 0; i < 2 * NB; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) lr4[e] = E::add_pair(pf[i][e], lr4[e]);
+    if constexpr (!C::EXACT_MAX) {
+      // The largest P of this row in this tile, computed exactly as above,
+      // and the error of its 16-bit rounding: the one of the row's largest P
+      // so far joins O's normaliser (see e_top).  With the exact running max
+      // that P is exp2(0) = 1, exact in 16 bits, and e_top stays 0.
+      const float pm = __builtin_amdgcn_exp2f(__builtin_fmaf(mx, c, nm_ref));
+      const float em = E::round(pm) - pm;
+      if (pm > p_top) p_top = pm, e_top = em;
+    }
   }
 
-  // all four chains of the rounded-P sum
-  __device__ __forceinline__ float lr_sum() const { return (lr4[0] + lr4[1]) + (lr4[2] + lr4[3]); }
+  // O^T *= alpha: the rescale the last softmax asked for
+  __device__ __forceinline__ void rescale_o() {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+  }
 
   // O^T += V^T P^T.  MFMA k-slot t of this lane holds the key
   // 16*ks + 8*(t/4) + 4*half + t%4 (the score accumulator layout), so the
@@ -582,10 +612,7 @@ struct Wave {
   // HBM -> LDS copy instruction of the phase right after MFMA i*LSTRIDE, so
   // the copies queue up one at a time behind running MFMAs instead of
   // stalling the wave in a burst.
-#ifndef ATTN_PIPE
-#define ATTN_PIPE 4
-#endif
-  template <bool PV, bool QK, int NL = 0, int LSTRIDE = 1, class COPY = NoCopy, int PIPE = ATTN_PIPE>
+  template <bool PV, bool QK, int NL = 0, int LSTRIDE = 1, class COPY = NoCopy, int PIPE = 4>
   __device__ __forceinline__ void mfma_ops(const uint8_t* vt, const uint8_t* kt, const COPY& copy = COPY{}) {
     constexpr int NPV = PV ? 2 * NB * DB : 0;
     constexpr int NQK = QK ? DK * NB : 0;
@@ -630,9 +657,8 @@ struct Wave {
   // a store instruction writes 16 bytes into each of 32 rows.
   __device__ __forceinline__ void epilogue(const HeadView& hv) {
     const float l_tot = sum_halves(l_run);
-    const float lr_tot = sum_halves(lr_sum());
     if (my_q < Sq) {
-      const float inv = lr_tot > 0.f ? 1.0f / lr_tot : 0.f;
+      const float inv = l_tot > 0.f ? 1.0f / (l_tot + e_top) : 0.f;
       uint16_t* orow = hv.o + (int64_t)my_q * hv.o_ss;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
@@ -659,8 +685,7 @@ struct Wave {
   static constexpr int EPI_BYTES = 32 * EPI_RS;  // one wave's staging area
   __device__ __forceinline__ void epilogue_staged(const HeadView& hv, uint8_t* stage) {
     const float l_tot = sum_halves(l_run);
-    const float lr_tot = sum_halves(lr_sum());
-    const float inv = lr_tot > 0.f ? 1.0f / lr_tot : 0.f;
+    const float inv = l_tot > 0.f ? 1.0f / (l_tot + e_top) : 0.f;
     uint8_t* mine = stage + (lane & 31) * EPI_RS;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -760,19 +785,19 @@ __device__ __forceinline__ void wait_loads_but() {
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 1: every wave runs qk, softmax, pv per tile; K and V tiles use two LDS
-// stages each.  Two copy schedules:
-//   STAGGER: every copy gets about a tile and a half to land, for workgroups
-//   that are alone on their CU (D=256):
+// Kernel 1: every wave runs qk, softmax, pv per tile.  Copy schedules:
+//   STAGGER (two LDS stages of K and of V): every copy gets about a tile and
+//   a half to land, for workgroups that are alone on their CU (D=256):
 //     qk(j)      carries the copy of V_{j+1} (into the V stage pv(j-1) freed)
 //     softmax(j)
 //     wait V_j, barrier
 //     pv(j)      carries the copy of K_{j+2} (into the K stage qk(j) freed)
 //     wait K_{j+1}, barrier
 //   (the copy instructions ride in the MFMA blocks, one after every few MFMAs);
-//   otherwise K_{j+1} and V_{j+1} are copied while tile j is computed, with
-//   one barrier per tile, when two workgroups share a CU and cover each
-//   other's copy latency (D=64).
+//   otherwise STAGES = 2: K_{j+1} and V_{j+1} are copied while tile j is
+//   computed, with one barrier per tile, where several workgroups share a CU
+//   and cover each other's copy latency (D=64: four per CU); STAGES = 1 or 3
+//   (and a producer wave) serve the schedule variants.
 // Supports key-split waves (KW > 1), merged at the end through LDS.
 // ---------------------------------------------------------------------------
 template <class C, bool CAUSAL, int DT>
@@ -978,15 +1003,15 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(const Problem p) {
 
   // merge the key-split waves (KW > 1): the O partial of wave (kw, qw),
   // kw > 0, goes to slot (kw - 1) * QW + qw of the stage arrays (vt0, vt1,
-  // kt0, kt1 with two or more stages; vt0, kt0 with one), its l, m and
-  // rounded-P sum to a small array of their own
+  // kt0, kt1 with two or more stages; vt0, kt0 with one), its l, m, p_top
+  // and e_top to a small array of their own
   if constexpr (C::KW > 1) {
     constexpr int NSLOT = (C::KW - 1) * C::QW;
     constexpr int SLOTS = C::STAGES >= 2 ? 4 : 2;
     constexpr int OBYTES = D / 2 * 64 * 4;  // one wave's O partial
     static_assert(NSLOT <= SLOTS && OBYTES <= C::V_TILE && (NSLOT <= SLOTS / 2 || OBYTES <= C::K_TILE),
                   "merge area too small");
-    __shared__ float mscal[NSLOT][3][64];
+    __shared__ float mscal[NSLOT][4][64];
     auto slot = [&](int i) __attribute__((always_inline)) -> uint8_t* {
       if constexpr (SLOTS == 2) return i == 0 ? vt0 : kt0;
       return i == 0 ? vt0 : i == 1 ? vt1 : i == 2 ? kt0 : kt1;
@@ -1000,7 +1025,8 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(const Problem p) {
         for (int i = 0; i < 16; ++i) dst[(db * 16 + i) * 64 + lane] = w.oacc[db][i];
       mscal[sl][0][lane] = w.l_run;
       mscal[sl][1][lane] = w.m_run;
-      mscal[sl][2][lane] = w.lr_sum();
+      mscal[sl][2][lane] = w.p_top;
+      mscal[sl][3][lane] = w.e_top;
     }
     __syncthreads();
     if (kw > 0) return;
@@ -1010,7 +1036,8 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(const Problem p) {
       const float* src = reinterpret_cast<const float*>(slot(sl));
       const float lb = mscal[sl][0][lane];
       const float mb = mscal[sl][1][lane];
-      const float lrb = mscal[sl][2][lane];
+      const float pb = mscal[sl][2][lane];
+      const float eb = mscal[sl][3][lane];
       const float mm = fmaxf(w.m_run, mb);
       const float mref = (mm == -__builtin_inff()) ? 0.f : mm;
       const float fa = __builtin_amdgcn_exp2f(w.m_run - mref);
@@ -1021,8 +1048,10 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(const Problem p) {
         for (int i = 0; i < 16; ++i)
           w.oacc[db][i] = w.oacc[db][i] * fa + src[(db * 16 + i) * 64 + lane] * fb;
       w.l_run = w.l_run * fa + lb * fb;
-      w.lr4[0] = w.lr_sum() * fa + lrb * fb;
-      w.lr4[1] = w.lr4[2] = w.lr4[3] = 0.f;
+      // the larger of the two largest P, on the merged scale, with its error
+      const float pa = w.p_top * fa, pbs = pb * fb;
+      w.e_top = pa >= pbs ? w.e_top * fa : eb * fb;
+      w.p_top = pa >= pbs ? pa : pbs;
       w.m_run = mm;
     }
   }
@@ -1055,9 +1084,12 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(const Problem p) {
 // stage no later phase reads.
 // ---------------------------------------------------------------------------
 // MFMAs between two copy instructions in group 0's MFMA block
-#ifndef ATTN_LSTRIDE
-#define ATTN_LSTRIDE 3
-#endif
+constexpr int kPingPongCopyStride = 3;
+// Whether the ping-pong rescales O^T (when a row max moved) at the start of
+// the next MFMA phase instead of in the softmax phase.  Deferred is faster:
+// the softmax phase is the longer one, and with the multiplies there the
+// compiler spilled registers of the causal kernel.
+constexpr bool kPingPongDeferRescale = true;
 template <class C, bool CAUSAL, int DT>
 __global__ __launch_bounds__(C::NT) void attn_fwd_pingpong_kernel(const Problem p) {
   static_assert(C::NW == 8 && C::KW == 1, "ping-pong needs 8 query waves");
@@ -1123,14 +1155,16 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_pingpong_kernel(const Problem 
         else
           vcp.line(rv, vt_ld, wave * LPW + i - LPW);
       };
-      constexpr int LS = (PV && QK) ? ATTN_LSTRIDE : 2;
+      constexpr int LS = (PV && QK) ? kPingPongCopyStride : 2;
+      if constexpr (kPingPongDeferRescale && PV) w.rescale_o();
       w.template mfma_ops<PV, QK, 2 * LPW, LS>(vt_prev, kt_j, copy);
     } else {
+      if constexpr (kPingPongDeferRescale && PV) w.rescale_o();
       w.template mfma_ops<PV, QK>(vt_prev, kt_j);
     }
     barrier_keep_loads();
     if constexpr (!LAST) {
-      if (w.active(j)) w.softmax(j);
+      if (w.active(j)) w.template softmax<kPingPongDeferRescale>(j);
       else w.zero_pf();
     }
     if constexpr (COPIES) {

@@ -17,12 +17,18 @@
 // and [batch, heads, k, n]) is exactly the contraction of steps 1 and 3.  Per
 // head it moves S*S*(4 + 4 + 2 + 2) bytes through HBM (write S, read S,
 // write P, read P) that the fused kernels keep on chip.
+//
+// This file is all of libattn_unfused.so, a library of its own: the fused
+// library libattn.so links no vendor BLAS.
 #include <hip/hip_runtime.h>
 #include <rocblas/rocblas.h>
 
+#include <cmath>
 #include <mutex>
 #include <unordered_map>
 
+#include "attn_common.hpp"
+#include "attn_unfused.h"
 #include "attn_unfused.hpp"
 
 namespace attn {
@@ -250,3 +256,53 @@ const char* unfused_launch(const void* q, const void* k, const void* v, void* o,
 }
 
 }  // namespace attn
+
+extern "C" {
+
+int64_t attn_fwd_unfused_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t D) {
+  if (B < 0 || H < 0 || S < 0 || (D != 64 && D != 128 && D != 256)) return -1;
+  if (B == 0 || H == 0 || S == 0) return 0;
+  // B*H*S*(S+8+D+1)*6 must fit in int64 with room for the rounding
+  const int64_t lim = (int64_t)1 << 58;
+  if (S > (1 << 28) || H > lim / B || B * H > lim / S / (S + D + 9) / 6) return -1;
+  return attn::unfused_layout(B, H, S, D).bytes;
+}
+
+int attn_fwd_unfused(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                     int64_t workspace_bytes, int64_t B, int64_t H, int64_t S, int64_t D, float scale, int causal,
+                     int dtype, void* stream) {
+  int st = check_sizes(B, H, S, D, dtype);
+  if (st != ATTN_OK) return st;
+  if (!std::isfinite(scale)) return fail(ATTN_ERR_BAD_SCALE, "scale must be finite (got %g)", (double)scale);
+  if (B == 0 || H == 0 || S == 0) return ok();
+  if (!q || !k || !v || !o || !lse || !workspace)
+    return fail(ATTN_ERR_NULL_PTR, "q, k, v, o, lse and workspace must be non-NULL");
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)workspace) & 15)
+    return fail(ATTN_ERR_MISALIGNED, "q, k, v, o and workspace must be 16-byte aligned");
+  if ((uintptr_t)lse & 3) return fail(ATTN_ERR_MISALIGNED, "lse must be 4-byte aligned");
+  const int64_t need = attn_fwd_unfused_workspace_bytes(B, H, S, D);
+  if (need < 0 || B * H > 0x7FFFFFFF || B * H * S > 0x7FFFFFFF)
+    return fail(ATTN_ERR_BAD_SHAPE, "B=%lld H=%lld S=%lld too large for the unfused path", (long long)B,
+                (long long)H, (long long)S);
+  if (workspace_bytes < need)
+    return fail(ATTN_ERR_BAD_ARGUMENT, "workspace of %lld bytes; %lld needed", (long long)workspace_bytes,
+                (long long)need);
+  const int64_t nt = B * H * S * D * 2, nl = B * H * S * 4;
+  if (overlaps(o, nt, q, nt) || overlaps(o, nt, k, nt) || overlaps(o, nt, v, nt) || overlaps(o, nt, lse, nl))
+    return fail(ATTN_ERR_ALIASING, "o overlaps q, k, v or lse");
+  if (overlaps(lse, nl, q, nt) || overlaps(lse, nl, k, nt) || overlaps(lse, nl, v, nt))
+    return fail(ATTN_ERR_ALIASING, "lse overlaps q, k or v");
+  for (const void* t : {(const void*)q, (const void*)k, (const void*)v, (const void*)o})
+    if (overlaps(workspace, need, t, nt)) return fail(ATTN_ERR_ALIASING, "workspace overlaps q, k, v or o");
+  if (overlaps(workspace, need, lse, nl)) return fail(ATTN_ERR_ALIASING, "workspace overlaps lse");
+  st = check_device();
+  if (st != ATTN_OK) return st;
+  const char* err = attn::unfused_launch(q, k, v, o, lse, workspace, B, H, S, D, scale, causal != 0, dtype,
+                                         (hipStream_t)stream);
+  if (err) return fail(ATTN_ERR_LAUNCH, "unfused path: %s", err);
+  return ok();
+}
+
+const char* attn_unfused_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

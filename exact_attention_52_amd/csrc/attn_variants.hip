@@ -1,25 +1,49 @@
-// attn_variants.hip -- schedule variants of kernel 1 for A/B measurements of
-// the K/V pipeline depth and of a producer/consumer wave split (the page's
-// Hopper design makes both first-class knobs: pingpong_stages and
-// num_producer_warps of FlashAttention3Config).  Same computation and
-// results contract as attn_fwd; only the copy schedule differs:
+// attn_variants.hip -- schedule variants of the forward kernel, for A/B
+// measurements of the K/V pipeline depth and of a producer/consumer wave
+// split (the page's Hopper design makes both first-class knobs:
+// pingpong_stages and num_producer_warps of FlashAttention3Config), and as a
+// race canary for the shipped schedules.  Same computation and results
+// contract as attn_fwd; only the copy schedule differs:
 //   1: 1 LDS stage   (copy tile j, wait, compute tile j, wait)
 //   2: 2 LDS stages  (copy tile j+1 while computing tile j)
 //   3: 3 LDS stages  (copy tile j+2 while computing tile j; counted waits)
 //   4: 2 LDS stages, plus one producer wave that issues every HBM -> LDS copy
 //      while the other waves only compute
-// D=64: 8 computing waves x 32 query rows, 128-key tiles (one workgroup per
-// CU; attn_fwd itself runs 4-wave, 128-row workgroups at D=64, two per CU);
-// D=128: 4 computing waves, 64-key tiles (so that 3 stages fit).
+//   5: the shipped tile shape of the head dim in kernel 1 with one stage
+//   6: the shipped tile shape of the head dim in kernel 1 with two stages and
+//      one barrier per tile (no ping-pong, no staggered copies)
+// Variants 1-4: D=64 uses the shipped D=64 shape (4 waves x 32 query rows,
+// 64-key tiles), so variant 2 is the shipped kernel itself; D=128 uses 4
+// computing waves and 64-key tiles, the largest D=128 shape for which three
+// stages fit in LDS.  Variants 5 and 6 exist for every head dim.  Every wave
+// of every variant computes its rows with the same per-wave steps in the
+// same order as the shipped kernel of its tile shape, so results are
+// bit-identical to attn_fwd for the shipped shapes (variants 5, 6 and, at
+// D=64, 1-4) and among variants 1-4.
 #include "attn_variants.hpp"
 
 namespace attn {
 namespace {
 
-template <int D, int S, bool P>
-using V64 = TileCfg<64, 8, 1, 128, false, false, S, P>;
-template <int D, int S, bool P>
+template <int S, bool P>
+using V64 = TileCfg<64, 4, 1, 64, false, false, S, P>;
+template <int S, bool P>
 using V128 = TileCfg<128, 4, 1, 64, false, false, S, P>;
+// the shipped tile shapes (query waves, key waves, keys per tile) in kernel 1
+template <int D, int S>
+struct Shipped;
+template <int S>
+struct Shipped<64, S> {
+  using C = TileCfg<64, 4, 1, 64, false, false, S>;
+};
+template <int S>
+struct Shipped<128, S> {
+  using C = TileCfg<128, 8, 1, 128, false, false, S>;
+};
+template <int S>
+struct Shipped<256, S> {
+  using C = TileCfg<256, 2, 2, 64, false, false, S>;
+};
 
 template <class C, bool CAUSAL, int DT>
 hipError_t go(Problem p, hipStream_t st) {
@@ -37,29 +61,47 @@ hipError_t pick(const Problem& p, bool causal, int dtype, hipStream_t st) {
   return causal ? go<C, true, DT_BF16>(p, st) : go<C, false, DT_BF16>(p, st);
 }
 
-template <int D, template <int, int, bool> class V>
-hipError_t by_variant(const Problem& p, bool causal, int dtype, int v, hipStream_t st) {
+template <template <int, bool> class V>
+hipError_t schedule(const Problem& p, bool causal, int dtype, int v, hipStream_t st) {
   switch (v) {
-    case 1: return pick<V<D, 1, false>>(p, causal, dtype, st);
-    case 2: return pick<V<D, 2, false>>(p, causal, dtype, st);
-    case 3: return pick<V<D, 3, false>>(p, causal, dtype, st);
-    case 4: return pick<V<D, 2, true>>(p, causal, dtype, st);
+    case 1: return pick<V<1, false>>(p, causal, dtype, st);
+    case 2: return pick<V<2, false>>(p, causal, dtype, st);
+    case 3: return pick<V<3, false>>(p, causal, dtype, st);
+    case 4: return pick<V<2, true>>(p, causal, dtype, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <int D>
+hipError_t shipped_shape(const Problem& p, bool causal, int dtype, int v, hipStream_t st) {
+  if (v == 5) return pick<typename Shipped<D, 1>::C>(p, causal, dtype, st);
+  return pick<typename Shipped<D, 2>::C>(p, causal, dtype, st);
 }
 
 }  // namespace
 
 int variant_block_m(int D, int v) {
   if (v < 1 || v >= kNumVariants) return 0;
-  if (D == 64) return V64<64, 2, false>::BM;
-  if (D == 128) return V128<128, 2, false>::BM;
+  if (v >= 5) {
+    if (D == 64) return Shipped<64, 1>::C::BM;
+    if (D == 128) return Shipped<128, 1>::C::BM;
+    if (D == 256) return Shipped<256, 1>::C::BM;
+    return 0;
+  }
+  if (D == 64) return V64<2, false>::BM;
+  if (D == 128) return V128<2, false>::BM;
   return 0;
 }
 
 hipError_t variant_launch(Problem p, int D, bool causal, int dtype, int v, hipStream_t stream) {
-  if (D == 64) return by_variant<64, V64>(p, causal, dtype, v, stream);
-  if (D == 128) return by_variant<128, V128>(p, causal, dtype, v, stream);
+  if (v >= 5) {
+    if (D == 64) return shipped_shape<64>(p, causal, dtype, v, stream);
+    if (D == 128) return shipped_shape<128>(p, causal, dtype, v, stream);
+    if (D == 256) return shipped_shape<256>(p, causal, dtype, v, stream);
+    return hipErrorInvalidValue;
+  }
+  if (D == 64) return schedule<V64>(p, causal, dtype, v, stream);
+  if (D == 128) return schedule<V128>(p, causal, dtype, v, stream);
   return hipErrorInvalidValue;
 }
 

@@ -8,9 +8,9 @@
 
 namespace attn {
 
-constexpr int kNumVariants = 5;  // 0 is the shipped configuration
+constexpr int kNumVariants = 7;  // 0 is the shipped configuration
 
-// Launch variant v (1..kNumVariants-1) for head dim 64 or 128 on `p`, setting
+// Launch variant v (1..kNumVariants-1) for head dim D on `p`, setting
 // p.nq and p.G for the variant's query tile.  Returns hipErrorInvalidValue
 // for an unsupported (v, D) or a grid over the launch limit.
 hipError_t variant_launch(Problem p, int D, bool causal, int dtype, int v, hipStream_t stream);

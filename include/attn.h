@@ -13,17 +13,17 @@
  *
  * Entry points: attn_fwd (contiguous), attn_fwd_strided (strides, Sq != Skv),
  * attn_bwd / attn_bwd_strided (backward), attn_fwd_variant (other copy
- * schedules, for A/B measurements), attn_fwd_unfused (an unfused comparator
- * that sends S through memory), and host-only planning helpers.
+ * schedules, for A/B measurements), and host-only planning helpers.  The
+ * unfused comparator (attn_fwd_unfused) is in its own library, declared in
+ * attn_unfused.h.
  *
  * Conventions shared by every entry point:
  *   - Q, K, V, O (and dQ, dK, dV, dO) are [B, H, rows, D] of 16-bit elements
  *     (fp16 or bf16, chosen by `dtype`), contiguous C order unless an entry
  *     point takes strides; LSE (and D_i) are [B, H, Sq] fp32, contiguous.
- *   - The caller owns every buffer and keeps no pointer from a call.  The
- *     kernels use no memory beyond the caller's buffers (and the workspace
- *     attn_fwd_unfused takes); the one allocation the library makes is the
- *     vendor BLAS handle attn_fwd_unfused creates per device on first use.
+ *   - The caller owns every buffer and the library keeps no pointer from a
+ *     call.  The kernels use no memory beyond the caller's buffers, and the
+ *     library allocates nothing.
  *   - Causal keeps key j for query i iff j <= i + (Skv - Sq): j <= i when
  *     Sq == Skv, and in general the last query sees the last key.
  *   - LSE is the natural logarithm of sum_j exp(scale * q_i . k_j) over the
@@ -42,10 +42,11 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 5
+#define ATTN_ABI_VERSION 6
 
-/* Element type of Q, K, V and O.  The page restricts the float type to F16 or
- * BF16 (validate_config, "float_type must be F16 or BF16"). */
+/* Element type of Q, K, V and O.  The page's configuration check
+ * (validate_config of FlashAttention3Config) accepts only the two 16-bit
+ * float types. */
 typedef enum { ATTN_F16 = 0, ATTN_BF16 = 1 } attn_dtype_t;
 
 typedef enum {
@@ -55,7 +56,7 @@ typedef enum {
   ATTN_ERR_UNSUPPORTED_HEAD_DIM = 3,  /* D not in {64, 128, 256}             */
   ATTN_ERR_UNSUPPORTED_DTYPE = 4,     /* dtype not ATTN_F16 / ATTN_BF16      */
   ATTN_ERR_MISALIGNED = 5,            /* q/k/v/o not 16-B, lse not 4-B       */
-  ATTN_ERR_BAD_SCALE = 6,             /* scale NaN, infinite or negative     */
+  ATTN_ERR_BAD_SCALE = 6,             /* scale NaN or infinite               */
   ATTN_ERR_ALIASING = 7,              /* an output overlaps another buffer   */
   ATTN_ERR_UNSUPPORTED_DEVICE = 8,    /* current device is not gfx950        */
   ATTN_ERR_LAUNCH = 9,                /* the HIP runtime refused the launch  */
@@ -82,8 +83,9 @@ typedef enum {
  *   B, H, S  batch, heads, sequence length (>= 0; any S, no multiple needed).
  *            B*H*S == 0 is a valid empty call: nothing is launched.
  *   D        head dimension: 64, 128 or 256 (the page's supported set).
- *   scale    softmax scale applied to Q K^T; finite and >= 0 (0 gives a
- *            uniform softmax over the kept keys).
+ *   scale    softmax scale applied to Q K^T (the page's f32 sm_scale); any
+ *            finite value (0 gives a uniform softmax over the kept keys; a
+ *            negative scale is exact: it multiplies -Q by |scale|).
  *   causal   0 or 1 (any non-zero value means 1).
  *   dtype    ATTN_F16 or ATTN_BF16.
  *   stream   hipStream_t to enqueue on; NULL means the null stream.
@@ -196,47 +198,20 @@ int attn_bwd_strided(const void* q, const void* k, const void* v, const void* o,
  *   3  3 stages: tile j+2 copied while tile j is computed
  *   4  2 stages and one extra producer wave that issues every HBM -> LDS
  *      copy while the other waves only compute
- * Variants 1-4 exist for D = 64 (8 computing waves, 128-key tiles) and
- * D = 128 (4 computing waves, 64-key tiles); others return
- * ATTN_ERR_BAD_ARGUMENT.
+ *   5  the shipped tile shape of the head dim, 1 stage, one wave step after
+ *      another (no ping-pong of wave groups, no staggered copies)
+ *   6  the shipped tile shape of the head dim, 2 stages, one barrier per tile
+ * Variants 1-4 exist for D = 64 (the shipped 4-wave, 64-key tile shape, so
+ * variant 2 is attn_fwd itself) and D = 128 (4 computing waves, 64-key
+ * tiles, so that 3 stages fit); variants 5 and 6 for every head dim.  Others
+ * return ATTN_ERR_BAD_ARGUMENT.  Every variant's waves run the same per-wave
+ * arithmetic in the same order as the shipped kernel of their tile shape, so
+ * variants 5 and 6 (and 1-4 at D = 64) are bit-identical to attn_fwd, and
+ * 1-4 to one another: a race in any schedule shows up as a difference.
  */
 int attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse,
                      int64_t B, int64_t H, int64_t S, int64_t D, float scale,
                      int causal, int dtype, int variant, void* stream);
-
-/*
- * attn_fwd_unfused -- the same forward as attn_fwd, unfused: a comparator
- * that shows the HBM traffic the fused kernels avoid.
- *
- * Steps: S = scale Q K^T as fp32 into the workspace (vendor strided-batched
- * GEMM over the B*H heads, the batched 4-D GEMM of the docs.rs page
- * "aprender-train 0.36.0, entrenar/autograd/cuda_forward/matmul.rs",
- * batched_4d_gemm_forward); a row softmax kernel writing P in `dtype` and
- * unnormalised P rounded to `dtype`, LSE and 1 / (sum of the rounded P); O =
- * P V (vendor GEMM, fp32 accumulation), then scaled by that factor and
- * rounded (the fused kernels normalise the same way).  Per head S*S*12 bytes
- * go through HBM.
- *
- *   q, k, v, o, lse, B, H, S, D, scale, causal, dtype, stream: as attn_fwd.
- *   workspace        device memory of at least
- *                    attn_fwd_unfused_workspace_bytes(B, H, S, D) bytes,
- *                    16-byte aligned, owned by the caller, overwritten; must
- *                    not overlap q, k, v, o or lse.
- *   workspace_bytes  its size.
- * Returns as attn_fwd; ATTN_ERR_BAD_ARGUMENT if the workspace is too small.
- * Not reentrant per device (a vendor-library handle per device is shared and
- * created on first use, outside the caller's control of allocation).
- */
-int attn_fwd_unfused(const void* q, const void* k, const void* v, void* o,
-                     float* lse, void* workspace, int64_t workspace_bytes,
-                     int64_t B, int64_t H, int64_t S, int64_t D, float scale,
-                     int causal, int dtype, void* stream);
-
-/* Workspace bytes attn_fwd_unfused needs (per head S rows of fp32 scores
- * and of 16-bit probabilities, rows padded to 16 bytes, plus the fp32 output
- * before normalisation and one fp32 factor per row); -1 for negative or
- * overflowing sizes or an unsupported head dim. */
-int64_t attn_fwd_unfused_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t D);
 
 /*
  * attn_fwd_plan -- the launch geometry attn_fwd would use (host only, no HIP

@@ -31,8 +31,8 @@
  *   oracle_attn_fwd        two passes per row (max, then sums), the definition
  *   oracle_attn_fwd_online keys in blocks with a running max m and running
  *                          sum l, rescaling the partial output when m grows
- *                          (the page's "online softmax with running max (m)
- *                          and sum (l)"); used to show tiling is exact
+ *                          (the online softmax of the page's doc comment of
+ *                          generate_forward); used to show tiling is exact
  *   oracle_attn_probs      the softmax matrix P itself, for small S
  * and, on float64 inputs, the same forward (oracle_attn_fwd_f64) and the
  * backward of the page's doc comment of generate_backward

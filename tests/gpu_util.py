@@ -32,18 +32,3 @@ def errors(o_gpu, lse_gpu, o_ref, lse_ref):
     eo = float(np.abs(o_gpu - o_ref).max()) if o_ref.size else 0.0
     el = float((np.abs(lse_gpu - lse_ref) / np.maximum(1.0, np.abs(lse_ref))).max()) if lse_ref.size else 0.0
     return eo, el
-
-
-def sample_rows(B, H, S, bm, bn, n_random, seed=0):
-    """Row indices (b*H + h)*S + i: tile edges, ends, and random rows."""
-    rng = np.random.default_rng(seed)
-    special = {0, 1, S - 1, S - 2}
-    for step in (bm, bn):
-        for t in range(step, S, step):
-            special.update((t - 1, t, t + 1))
-    special = sorted(i for i in special if 0 <= i < S)
-    rows = set()
-    for bh in (0, B * H - 1):
-        rows.update(bh * S + i for i in special)
-    rows.update(int(r) for r in rng.integers(0, B * H * S, n_random))
-    return np.array(sorted(rows), dtype=np.int64)

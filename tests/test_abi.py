@@ -14,8 +14,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 GOLDEN = os.path.join(ROOT, "tests", "golden")
 
 
-def declared_functions():
-    text = open(os.path.join(ROOT, "include", "attn.h")).read()
+def declared_functions(header="attn.h"):
+    text = open(os.path.join(ROOT, "include", header)).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
 
@@ -29,17 +29,39 @@ def test_library_loads_and_exports_every_declared_symbol():
         assert hasattr(lib, n), n
     assert lib.attn_abi_version() == _lib.ABI_VERSION
     # no torch types cross the ABI: the header holds only C types
-    hdr = open(os.path.join(ROOT, "include", "attn.h")).read()
-    assert "torch" not in hdr.lower().replace("pytorch", "")
+    for hdr_name in ("attn.h", "attn_unfused.h"):
+        hdr = open(os.path.join(ROOT, "include", hdr_name)).read()
+        assert "torch" not in hdr.lower().replace("pytorch", "")
+
+
+def test_unfused_library_loads_and_exports_every_declared_symbol():
+    lib = _lib.load_unfused()
+    names = declared_functions("attn_unfused.h")
+    assert set(names) == set(_lib.UNFUSED_EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _dynamic_symbols(path):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True).stdout
+    return {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
 
 
 def test_exported_symbols_in_dynamic_table():
-    import subprocess
-    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH],
-                         capture_output=True, text=True, check=True).stdout
-    syms = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    syms = _dynamic_symbols(_lib.LIB_PATH)
     for n in declared_functions():
         assert n in syms
+    usyms = _dynamic_symbols(_lib.UNFUSED_LIB_PATH)
+    for n in declared_functions("attn_unfused.h"):
+        assert n in usyms
+
+
+def test_fused_library_links_no_vendor_blas():
+    import subprocess
+    out = subprocess.run(["readelf", "-d", _lib.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    needed = [ln for ln in out.splitlines() if "NEEDED" in ln]
+    assert needed and not any(x in ln for ln in needed for x in ("rocblas", "hipblas", "hipblaslt")), needed
 
 
 def test_status_strings():
@@ -168,7 +190,7 @@ def call(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, o=FAKE + 0x300000, lse=FA
     (dict(lse=FAKE + 0x400002), 5, "4-byte"),
     (dict(scale=float("nan")), 6, "scale"),
     (dict(scale=float("inf")), 6, "scale"),
-    (dict(scale=-0.5), 6, "scale"),
+    (dict(scale=float("-inf")), 6, "scale"),
     (dict(o=FAKE), 7, "overlaps"),
     (dict(o=FAKE + 0x100000 + 16), 7, "overlaps"),
     (dict(lse=FAKE + 0x300000 + 64), 7, "overlaps"),
@@ -204,6 +226,16 @@ def test_no_gpu_reports_unsupported_device():
     assert "device" in _lib.last_error()
 
 
+def test_any_finite_scale_passes_the_checks():
+    # the page's sm_scale is a plain f32: zero and negative scales are valid
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("would launch on a real GPU with fake pointers")
+    for sc in (-0.5, -0.0, 0.0, -1e30, 3.0e38):
+        assert call(scale=sc) == 8, (sc, _lib.last_error())
+        assert scall(scale=sc) == 8, (sc, _lib.last_error())
+
+
 # --------------------------------------------------------------------------
 # attn_fwd_strided: argument checks (all before any HIP call)
 # --------------------------------------------------------------------------
@@ -230,7 +262,7 @@ def scall(q=FAKE, k=FAKE + 0x1000000, v=FAKE + 0x2000000, o=FAKE + 0x3000000, ls
     (dict(os_=(2048, 32, 128)), 7, "o strides"),        # head 1 starts in the middle of a row of head 0
     (dict(o=FAKE + 64), 7, "overlaps"),
     (dict(lse=FAKE + 0x2000000 + 64), 7, "overlaps"),
-    (dict(scale=-1.0), 6, "scale"),
+    (dict(scale=float("nan")), 6, "scale"),
 ])
 def test_strided_invalid_arguments_rejected_before_launch(kwargs, status, word):
     st = scall(**kwargs)
@@ -342,16 +374,17 @@ def ucall(q=FAKE, k=FAKE + MB_, v=FAKE + 2 * MB_, o=FAKE + 3 * MB_, lse=FAKE + 4
 ])
 def test_unfused_invalid_arguments_rejected_before_launch(kwargs, status, word):
     st = ucall(**kwargs)
-    assert st == status, (st, _lib.last_error())
-    assert word.lower() in _lib.last_error().lower()
+    assert st == status, (st, _lib.unfused_last_error())
+    assert word.lower() in _lib.unfused_last_error().lower()
 
 
 def test_unfused_valid_call_reaches_the_device_check():
     import torch
     if torch.cuda.device_count() > 0:
         pytest.skip("would launch on a real GPU with fake pointers")
-    assert ucall() == 8, _lib.last_error()
+    assert ucall() == 8, _lib.unfused_last_error()
     assert ucall(B=0, q=0, k=0, v=0, o=0, lse=0, ws=0, wsb=0) == 0
+    assert ucall(scale=-0.25) == 8, _lib.unfused_last_error()
 
 
 # --------------------------------------------------------------------------
@@ -361,7 +394,7 @@ def vcall(variant, D=64, B=1, H=2, S=16, q=FAKE, o=FAKE + 3 * MB_, lse=FAKE + 4 
     return _lib.attn_fwd_variant(q, q, q, o, lse, B, H, S, D, 0.125, 0, 0, variant, 0)
 
 
-@pytest.mark.parametrize("variant,D", [(-1, 64), (5, 64), (1, 256), (4, 256)])
+@pytest.mark.parametrize("variant,D", [(-1, 64), (7, 64), (7, 256), (1, 256), (4, 256)])
 def test_variant_out_of_range(variant, D):
     assert vcall(variant, D) == 10
     assert "variant" in _lib.last_error()
@@ -371,10 +404,11 @@ def test_variants_reach_the_device_check():
     import torch
     if torch.cuda.device_count() > 0:
         pytest.skip("would launch on a real GPU with fake pointers")
-    for v in range(5):
+    for v in range(7):
         for D in (64, 128):
             assert vcall(v, D) == 8, _lib.last_error()
-    assert vcall(0, 256) == 8
+    for v in (0, 5, 6):
+        assert vcall(v, 256) == 8, _lib.last_error()
     assert vcall(3, 64, B=0) == 0  # empty
 
 

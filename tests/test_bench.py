@@ -51,3 +51,37 @@ def test_unfused_byte_convention():
     n = 2 * 16 * 4096
     assert bench.unfused_bytes(2, 16, 4096, 128) == (bench.min_bytes(2, 16, 4096, 128) + n * 4096 * 12
                                                      + n * 129 * 8)
+
+
+def test_launch_stats():
+    st = bench.launch_stats([0.25, 0.26, 0.24, 0.30])
+    assert st["launches"] == 4
+    assert st["mean_us"] == pytest.approx(262.5)
+    assert st["median_us"] == pytest.approx(255.0)
+    assert st["min_us"] == pytest.approx(240.0) and st["max_us"] == pytest.approx(300.0)
+
+
+def test_full_parity_checks_every_element():
+    # the CPU leg compares every element: one element off by more than the
+    # tolerance anywhere in the output fails the check
+    import numpy as np
+
+    from exact_attention_52_amd import inputs
+    B, H, S, D, dtype, causal, mult = inputs.WORKLOADS["c1_b1h2s128d64_fp16"]
+    shape = (B, H, S, D, dtype, causal)
+    words = inputs.gen_qkv(B, H, S, D, dtype, seed=0, qk_mult=mult)
+    o_ref, l_ref, secs = bench.full_oracle(shape, words)
+    assert secs >= 0 and o_ref.shape == (B, H, S, D)
+    o_h = o_ref.astype(np.float16).astype(np.float32)  # a correctly rounded output
+    l_h = l_ref.astype(np.float32)
+    par = bench.parity_all(shape, o_h, l_h, o_ref, l_ref)
+    assert par["ok"] and par["rows"] == B * H * S and par["elements_o"] == o_ref.size
+    o_bad = o_h.copy()
+    o_bad[B - 1, H - 1, S - 1, D - 1] += 3e-3
+    assert not bench.parity_all(shape, o_bad, l_h, o_ref, l_ref)["ok"]
+    l_bad = l_h.copy()
+    l_bad[0, 1, 77] += 5e-3 * max(1.0, abs(float(l_h[0, 1, 77])))
+    assert not bench.parity_all(shape, o_h, l_bad, o_ref, l_ref)["ok"]
+    rate = bench.oracle_rate(shape, 2.0)
+    assert rate["kind"] == "oracle" and rate["cores"] >= 1
+    assert rate["value"] == pytest.approx(bench.flops(B, H, S, D, causal) / 2.0 / 1e12)

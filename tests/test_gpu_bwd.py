@@ -52,11 +52,12 @@ def rel_err(x, ref):
     return float(np.abs(x - ref).max() / max(1.0, np.abs(ref).max()))
 
 
-def run_case(ea, oracle_mod, B, H, Sq, Skv, D, dtype, causal, seed, mult=1.0, heads=None):
+def run_case(ea, oracle_mod, B, H, Sq, Skv, D, dtype, causal, seed, mult=1.0, heads=None, scale=None):
     import torch
-    print(f"bwd case B={B} H={H} Sq={Sq} Skv={Skv} D={D} {dtype} causal={causal}", flush=True)
+    print(f"bwd case B={B} H={H} Sq={Sq} Skv={Skv} D={D} {dtype} causal={causal} scale={scale}", flush=True)
     q, k, v, do = gen(B, H, Sq, Skv, D, dtype, seed, mult)
-    scale = float(np.float32(1.0 / math.sqrt(D)))
+    if scale is None:
+        scale = float(np.float32(1.0 / math.sqrt(D)))
     dq_, dk_, dv_, ddo = (to_dev(x, dtype) for x in (q, k, v, do))
     o, lse = ea.fwd(dq_, dk_, dv_, scale=scale, causal=causal)
     dq, dk, dv, delta = ea.bwd(dq_, dk_, dv_, o, lse, ddo, scale=scale, causal=causal)
@@ -94,6 +95,14 @@ def test_bwd_unequal_lengths(ea, oracle_mod, D, causal, Sq, Skv):
     if causal and Sq > Skv:  # queries with no key
         cut = Sq - Skv
         assert np.all(got[0][:, :, :cut] == 0.0) and np.all(got[3][:, :, :cut] == 0.0)
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_negative_scale(ea, oracle_mod, D, causal):
+    # the page's sm_scale is a plain f32: a negative scale is valid
+    dtype = "bf16" if D == 128 else "fp16"
+    run_case(ea, oracle_mod, 1, 2, 211, 211, D, dtype, causal, seed=D + 17, scale=-0.09)
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])

@@ -45,8 +45,8 @@ def nan_tailed(words, dtype):
     return view, buf
 
 
-# (D, S): S leaves the last 128-key (D = 64, 128) or 64-key (D = 256) tile
-# with a few rows, and the last query tile ragged too
+# (D, S): S leaves the last key tile (64 keys at D = 64 and 256, 128 at
+# D = 128) with a few rows, and the last query tile ragged too
 CASES = [(64, 130), (128, 130), (128, 300), (256, 70), (256, 200)]
 
 

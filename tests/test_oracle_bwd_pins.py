@@ -43,9 +43,9 @@ def test_fwd_f64_is_the_pinned_16bit_forward():
             assert np.abs(l64 - l16).max() <= 1e-13
 
 
+@pytest.mark.parametrize("scale", [0.7, -0.45])
 @pytest.mark.parametrize("B,H,Sq,Skv,D,causal", CASES)
-def test_bwd_is_the_derivative_of_the_forward(B, H, Sq, Skv, D, causal):
-    scale = 0.7
+def test_bwd_is_the_derivative_of_the_forward(B, H, Sq, Skv, D, causal, scale):
     q, k, v, do = problem(B, H, Sq, Skv, D, seed=Sq * 10 + Skv)
 
     def loss(q_, k_, v_):

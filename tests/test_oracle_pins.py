@@ -36,7 +36,7 @@ TINY = [(1, 1, 1, 1), (1, 1, 2, 3), (1, 2, 3, 2), (2, 1, 5, 4), (2, 2, 8, 8),
 def test_p1_brute_force(oracle_mod, shape, causal, dtype):
     B, H, S, D = shape
     seed = zlib.crc32(repr((shape, causal, dtype)).encode()) & 0xFFFF
-    for mult, scale in ((1.0, 1 / math.sqrt(D)), (4.0, 1.7), (1.0, 0.0)):
+    for mult, scale in ((1.0, 1 / math.sqrt(D)), (4.0, 1.7), (1.0, 0.0), (2.0, -0.6)):
         q, k, v = inputs.gen_qkv(B, H, S, D, dtype, seed=seed, qk_mult=mult)
         o, lse = oracle_mod.attn_fwd(q, k, v, dtype, scale, causal)
         ob, lb = brute.attention(q.tolist(), k.tolist(), v.tolist(), dtype, scale, causal)
