@@ -19,13 +19,14 @@ from . import _lib
 from ._lib import ATTN_BF16, ATTN_F16, AttnError  # noqa: F401
 
 __all__ = ["attention", "fwd", "bwd", "fwd_unfused", "fwd_variant", "attn_fwd", "attn_fwd_strided", "attn_fwd_variant",
-           "attn_bwd", "attn_bwd_strided", "attn_fwd_unfused",
+           "attn_bwd", "attn_bwd_strided", "attn_bwd_noalloc", "attn_fwd_unfused",
            "attn_fwd_unfused_workspace_bytes", "attn_fwd_plan", "attn_fwd_workgroup_tile", "AttnError"]
 
 attn_fwd = _lib.attn_fwd
 attn_fwd_strided = _lib.attn_fwd_strided
 attn_bwd = _lib.attn_bwd
 attn_bwd_strided = _lib.attn_bwd_strided
+attn_bwd_noalloc = _lib.attn_bwd_noalloc
 attn_fwd_variant = _lib.attn_fwd_variant
 attn_fwd_unfused = _lib.attn_fwd_unfused
 attn_fwd_unfused_workspace_bytes = _lib.attn_fwd_unfused_workspace_bytes

@@ -18,7 +18,7 @@ STATUS = {
     8: "ATTN_ERR_UNSUPPORTED_DEVICE", 9: "ATTN_ERR_LAUNCH", 10: "ATTN_ERR_BAD_ARGUMENT",
 }
 UNFUSED_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn_unfused.so")
-EXPORTS = ("attn_fwd", "attn_fwd_strided", "attn_fwd_variant", "attn_bwd", "attn_bwd_strided",
+EXPORTS = ("attn_fwd", "attn_fwd_strided", "attn_fwd_variant", "attn_bwd", "attn_bwd_strided", "attn_bwd_noalloc",
            "attn_fwd_plan", "attn_fwd_workgroup_tile", "attn_status_string", "attn_last_error", "attn_abi_version")
 UNFUSED_EXPORTS = ("attn_fwd_unfused", "attn_fwd_unfused_workspace_bytes", "attn_unfused_last_error")
 
@@ -64,6 +64,8 @@ def load():
     lib.attn_bwd_strided.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                      p64, p64, p64, p64, p64, p64, p64, p64, cf, ci, ci, vp]
     lib.attn_bwd_strided.restype = ci
+    lib.attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, cf, ci, ci, vp]
+    lib.attn_bwd_noalloc.restype = ci
     lib.attn_fwd_variant.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, cf, ci, ci, ci, vp]
     lib.attn_fwd_variant.restype = ci
     lib.attn_fwd_plan.argtypes = [i64, i64, i64, i64, ci, ci, ctypes.POINTER(Plan)]
@@ -163,6 +165,16 @@ def attn_bwd(q: int, k: int, v: int, o: int, lse: int, do: int, dq: int, dk: int
     """Raw call: device pointers as ints; returns the status code."""
     return load().attn_bwd(q, k, v, o, lse, do, dq, dk, dv, delta, B, H, Sq, Skv, D, float(scale),
                            int(bool(causal)), int(dtype), stream)
+
+
+def attn_bwd_noalloc(q: int, k: int, v: int, o: int, lse: int, do: int, dq: int, dk: int, dv: int,
+                     B: int, H: int, Sq: int, Skv: int, D: int, scale: float, causal: bool, dtype: int,
+                     stream: int) -> int:
+    """Raw call: attn_bwd with D_i in the library's own device scratch (no
+    allocation, no delta argument); device pointers as ints; returns the
+    status code."""
+    return load().attn_bwd_noalloc(q, k, v, o, lse, do, dq, dk, dv, B, H, Sq, Skv, D, float(scale),
+                                   int(bool(causal)), int(dtype), stream)
 
 
 def attn_bwd_strided(q: int, k: int, v: int, o: int, lse: int, do: int, dq: int, dk: int, dv: int, delta: int,

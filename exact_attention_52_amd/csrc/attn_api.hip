@@ -14,6 +14,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "attn.h"
@@ -208,6 +209,135 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int64_
   }
 }
 
+// Scratch of attn_bwd_noalloc: the backward's per-row D_i, in a file-scope
+// device array so that the call allocates nothing.  Each GPU holds its own
+// copy (16 MiB) from the library's load until the process ends; host code
+// reaches it only through the address hipGetSymbolAddress returns for the
+// current device, never through the array's name.
+constexpr int64_t kNoAllocRows = (int64_t)1 << 22;
+static __device__ __align__(256) float scratch[kNoAllocRows];
+
+std::mutex g_scratch_mutex;
+float* g_scratch_ptr[kMaxDevices];  // guarded by g_scratch_mutex
+
+// This device's address of `scratch`, looked up once per device with the
+// device current.
+int scratch_address(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0)
+    return fail(ATTN_ERR_UNSUPPORTED_DEVICE, "no current HIP device (%s)", hipGetErrorString(e));
+  if (dev >= kMaxDevices)
+    return fail(ATTN_ERR_UNSUPPORTED_DEVICE, "device %d beyond the %d the scratch table covers", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(ATTN_ERR_LAUNCH, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = static_cast<float*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+
+// The backward of attn_bwd_strided; with use_scratch (attn_bwd_noalloc) D_i
+// goes to this device's copy of the file-scope scratch array instead of the
+// caller's delta.
+int bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,
+             void* dk, void* dv, float* delta, bool use_scratch, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
+             int64_t D,
+             const int64_t* q_strides, const int64_t* k_strides, const int64_t* v_strides, const int64_t* o_strides,
+             const int64_t* do_strides, const int64_t* dq_strides, const int64_t* dk_strides,
+             const int64_t* dv_strides, float scale, int causal, int dtype, void* stream) {
+  if (B < 0 || H < 0 || Sq < 0 || Skv < 0)
+    return fail(ATTN_ERR_BAD_SHAPE, "B, H, Sq and Skv must be >= 0 (got B=%lld H=%lld Sq=%lld Skv=%lld)",
+                (long long)B, (long long)H, (long long)Sq, (long long)Skv);
+  int st = check_sizes(B, H, Sq > Skv ? Sq : Skv, D, dtype);
+  if (st != ATTN_OK) return st;
+  if (!std::isfinite(scale)) return fail(ATTN_ERR_BAD_SCALE, "scale must be finite (got %g)", (double)scale);
+  if (use_scratch && B * H * Sq > kNoAllocRows)
+    return fail(ATTN_ERR_BAD_ARGUMENT,
+                "B*H*Sq = %lld rows exceed the %lld rows of D_i the no-allocation scratch holds",
+                (long long)(B * H * Sq), (long long)kNoAllocRows);
+  if (B == 0 || H == 0 || (Sq == 0 && Skv == 0)) return ok();
+  const bool has_q = Sq > 0, has_k = Skv > 0;
+  if ((has_q && (!q || !o || !dO || !lse || !dq || (!use_scratch && !delta))) || (has_k && (!k || !v || !dk || !dv)))
+    return fail(ATTN_ERR_NULL_PTR, use_scratch ? "q, k, v, o, lse, dO, dq, dk and dv must be non-NULL"
+                                               : "q, k, v, o, lse, dO, dq, dk, dv and delta must be non-NULL");
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dO | (uintptr_t)dq |
+       (uintptr_t)dk | (uintptr_t)dv) & 15)
+    return fail(ATTN_ERR_MISALIGNED, "q, k, v, o, dO, dq, dk and dv must be 16-byte aligned");
+  if (((uintptr_t)lse | (uintptr_t)delta) & 3) return fail(ATTN_ERR_MISALIGNED, "lse and delta must be 4-byte aligned");
+  auto view = [&](const void* ptr, const int64_t* sts, int64_t rows, const char* name) {
+    View t = {ptr, H * rows * D, rows * D, D, rows, name};
+    if (sts) t.sb = sts[0], t.sh = sts[1], t.ss = sts[2];
+    normalise(t, B, H, D);
+    return t;
+  };
+  View vs[8] = {view(q, q_strides, Sq, "q"),    view(k, k_strides, Skv, "k"),   view(v, v_strides, Skv, "v"),
+                view(o, o_strides, Sq, "o"),    view(dO, do_strides, Sq, "dO"), view(dq, dq_strides, Sq, "dq"),
+                view(dk, dk_strides, Skv, "dk"), view(dv, dv_strides, Skv, "dv")};
+  for (const View& t : vs) {
+    if (t.rows == 0) continue;
+    st = check_view(t, B, H, D);
+    if (st != ATTN_OK) return st;
+  }
+  for (int i = 5; i < 8; ++i)
+    if (vs[i].rows > 0 && !self_disjoint(vs[i], B, H, D))
+      return fail(ATTN_ERR_ALIASING, "%s strides make rows overlap", vs[i].name);
+  const int64_t nr = B * H * Sq * 4;
+  struct Buf {
+    const void* p;
+    int64_t n;
+  };
+  // the scratch is the library's own memory: no caller buffer can overlap it
+  const Buf outs[4] = {{dq, extent_bytes(vs[5], B, H, D)},
+                       {dk, extent_bytes(vs[6], B, H, D)},
+                       {dv, extent_bytes(vs[7], B, H, D)},
+                       {delta, use_scratch ? 0 : nr}};
+  const Buf ins[6] = {{q, extent_bytes(vs[0], B, H, D)}, {k, extent_bytes(vs[1], B, H, D)},
+                      {v, extent_bytes(vs[2], B, H, D)}, {o, extent_bytes(vs[3], B, H, D)},
+                      {dO, extent_bytes(vs[4], B, H, D)}, {lse, nr}};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n))
+        return fail(ATTN_ERR_ALIASING, "dq, dk, dv and delta must not overlap each other");
+    for (const Buf& b : ins)
+      if (overlaps(outs[i].p, outs[i].n, b.p, b.n))
+        return fail(ATTN_ERR_ALIASING, "dq, dk, dv and delta must not overlap q, k, v, o, dO or lse");
+  }
+  const attn::BwdPlan plan = attn::bwd_plan((int)D);
+  const int64_t gq = B * H * ((Sq + plan.dq_queries_per_workgroup - 1) / plan.dq_queries_per_workgroup);
+  const int64_t gk = B * H * ((Skv + plan.dkdv_keys_per_workgroup - 1) / plan.dkdv_keys_per_workgroup);
+  const int64_t gd = (B * H * Sq + plan.delta_rows_per_workgroup - 1) / plan.delta_rows_per_workgroup;
+  if (gq > 0x7FFFFFFF || gk > 0x7FFFFFFF || gd > 0x7FFFFFFF)
+    return fail(ATTN_ERR_BAD_SHAPE, "grid exceeds the launch limit");
+  st = check_device();
+  if (st != ATTN_OK) return st;
+  if (use_scratch && Sq > 0) {
+    st = scratch_address(&delta);
+    if (st != ATTN_OK) return st;
+  }
+
+  attn::BwdProblem p;
+  p.q = (const uint16_t*)q, p.k = (const uint16_t*)k, p.v = (const uint16_t*)v, p.o = (const uint16_t*)o;
+  p.dO = (const uint16_t*)dO, p.lse = lse, p.delta = delta;
+  p.dq = (uint16_t*)dq, p.dk = (uint16_t*)dk, p.dv = (uint16_t*)dv;
+  attn::Strides* ps[8] = {&p.s_q, &p.s_k, &p.s_v, &p.s_o, &p.s_do, &p.s_dq, &p.s_dk, &p.s_dv};
+  for (int i = 0; i < 8; ++i) *ps[i] = attn::Strides{vs[i].sb, vs[i].sh, (int)vs[i].ss};
+  p.H = (int)H;
+  p.Sq = (int)Sq, p.Skv = (int)Skv, p.nq = 0, p.nk = 0, p.BH = B * H;
+  // the backward masks P itself (never a score), so c may take any sign;
+  // a tiny positive c is kept >= FLT_MIN as in the forward
+  float c = (float)((double)scale * 1.4426950408889634074);
+  p.c = (c >= 0.f && c < FLT_MIN) ? FLT_MIN : c;
+  p.scale = scale;
+  const hipError_t e = attn::bwd_launch(p, (int)D, causal != 0, dtype, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(ATTN_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -267,82 +397,15 @@ int attn_bwd_strided(const void* q, const void* k, const void* v, const void* o,
                      const int64_t* o_strides, const int64_t* do_strides, const int64_t* dq_strides,
                      const int64_t* dk_strides, const int64_t* dv_strides, float scale, int causal, int dtype,
                      void* stream) {
-  if (B < 0 || H < 0 || Sq < 0 || Skv < 0)
-    return fail(ATTN_ERR_BAD_SHAPE, "B, H, Sq and Skv must be >= 0 (got B=%lld H=%lld Sq=%lld Skv=%lld)",
-                (long long)B, (long long)H, (long long)Sq, (long long)Skv);
-  int st = check_sizes(B, H, Sq > Skv ? Sq : Skv, D, dtype);
-  if (st != ATTN_OK) return st;
-  if (!std::isfinite(scale)) return fail(ATTN_ERR_BAD_SCALE, "scale must be finite (got %g)", (double)scale);
-  if (B == 0 || H == 0 || (Sq == 0 && Skv == 0)) return ok();
-  const bool has_q = Sq > 0, has_k = Skv > 0;
-  if ((has_q && (!q || !o || !dO || !lse || !dq || !delta)) || (has_k && (!k || !v || !dk || !dv)))
-    return fail(ATTN_ERR_NULL_PTR, "q, k, v, o, lse, dO, dq, dk, dv and delta must be non-NULL");
-  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dO | (uintptr_t)dq |
-       (uintptr_t)dk | (uintptr_t)dv) & 15)
-    return fail(ATTN_ERR_MISALIGNED, "q, k, v, o, dO, dq, dk and dv must be 16-byte aligned");
-  if (((uintptr_t)lse | (uintptr_t)delta) & 3) return fail(ATTN_ERR_MISALIGNED, "lse and delta must be 4-byte aligned");
-  auto view = [&](const void* ptr, const int64_t* sts, int64_t rows, const char* name) {
-    View t = {ptr, H * rows * D, rows * D, D, rows, name};
-    if (sts) t.sb = sts[0], t.sh = sts[1], t.ss = sts[2];
-    normalise(t, B, H, D);
-    return t;
-  };
-  View vs[8] = {view(q, q_strides, Sq, "q"),    view(k, k_strides, Skv, "k"),   view(v, v_strides, Skv, "v"),
-                view(o, o_strides, Sq, "o"),    view(dO, do_strides, Sq, "dO"), view(dq, dq_strides, Sq, "dq"),
-                view(dk, dk_strides, Skv, "dk"), view(dv, dv_strides, Skv, "dv")};
-  for (const View& t : vs) {
-    if (t.rows == 0) continue;
-    st = check_view(t, B, H, D);
-    if (st != ATTN_OK) return st;
-  }
-  for (int i = 5; i < 8; ++i)
-    if (vs[i].rows > 0 && !self_disjoint(vs[i], B, H, D))
-      return fail(ATTN_ERR_ALIASING, "%s strides make rows overlap", vs[i].name);
-  const int64_t nr = B * H * Sq * 4;
-  struct Buf {
-    const void* p;
-    int64_t n;
-  };
-  const Buf outs[4] = {{dq, extent_bytes(vs[5], B, H, D)},
-                       {dk, extent_bytes(vs[6], B, H, D)},
-                       {dv, extent_bytes(vs[7], B, H, D)},
-                       {delta, nr}};
-  const Buf ins[6] = {{q, extent_bytes(vs[0], B, H, D)}, {k, extent_bytes(vs[1], B, H, D)},
-                      {v, extent_bytes(vs[2], B, H, D)}, {o, extent_bytes(vs[3], B, H, D)},
-                      {dO, extent_bytes(vs[4], B, H, D)}, {lse, nr}};
-  for (int i = 0; i < 4; ++i) {
-    for (int j = i + 1; j < 4; ++j)
-      if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n))
-        return fail(ATTN_ERR_ALIASING, "dq, dk, dv and delta must not overlap each other");
-    for (const Buf& b : ins)
-      if (overlaps(outs[i].p, outs[i].n, b.p, b.n))
-        return fail(ATTN_ERR_ALIASING, "dq, dk, dv and delta must not overlap q, k, v, o, dO or lse");
-  }
-  const attn::BwdPlan plan = attn::bwd_plan((int)D);
-  const int64_t gq = B * H * ((Sq + plan.dq_queries_per_workgroup - 1) / plan.dq_queries_per_workgroup);
-  const int64_t gk = B * H * ((Skv + plan.dkdv_keys_per_workgroup - 1) / plan.dkdv_keys_per_workgroup);
-  const int64_t gd = (B * H * Sq + plan.delta_rows_per_workgroup - 1) / plan.delta_rows_per_workgroup;
-  if (gq > 0x7FFFFFFF || gk > 0x7FFFFFFF || gd > 0x7FFFFFFF)
-    return fail(ATTN_ERR_BAD_SHAPE, "grid exceeds the launch limit");
-  st = check_device();
-  if (st != ATTN_OK) return st;
+  return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, delta, false, B, H, Sq, Skv, D, q_strides, k_strides, v_strides,
+                  o_strides, do_strides, dq_strides, dk_strides, dv_strides, scale, causal, dtype, stream);
+}
 
-  attn::BwdProblem p;
-  p.q = (const uint16_t*)q, p.k = (const uint16_t*)k, p.v = (const uint16_t*)v, p.o = (const uint16_t*)o;
-  p.dO = (const uint16_t*)dO, p.lse = lse, p.delta = delta;
-  p.dq = (uint16_t*)dq, p.dk = (uint16_t*)dk, p.dv = (uint16_t*)dv;
-  attn::Strides* ps[8] = {&p.s_q, &p.s_k, &p.s_v, &p.s_o, &p.s_do, &p.s_dq, &p.s_dk, &p.s_dv};
-  for (int i = 0; i < 8; ++i) *ps[i] = attn::Strides{vs[i].sb, vs[i].sh, (int)vs[i].ss};
-  p.H = (int)H;
-  p.Sq = (int)Sq, p.Skv = (int)Skv, p.nq = 0, p.nk = 0, p.BH = B * H;
-  // the backward masks P itself (never a score), so c may take any sign;
-  // a tiny positive c is kept >= FLT_MIN as in the forward
-  float c = (float)((double)scale * 1.4426950408889634074);
-  p.c = (c >= 0.f && c < FLT_MIN) ? FLT_MIN : c;
-  p.scale = scale;
-  const hipError_t e = attn::bwd_launch(p, (int)D, causal != 0, dtype, (hipStream_t)stream);
-  if (e != hipSuccess) return fail(ATTN_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
-  return ok();
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+                     void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
+                     float scale, int causal, int dtype, void* stream) {
+  return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, nullptr, true, B, H, Sq, Skv, D, nullptr, nullptr, nullptr, nullptr,
+                  nullptr, nullptr, nullptr, nullptr, scale, causal, dtype, stream);
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,

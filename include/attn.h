@@ -12,7 +12,7 @@
  *   from the saved log-sum-exp.
  *
  * Entry points: attn_fwd (contiguous), attn_fwd_strided (strides, Sq != Skv),
- * attn_bwd / attn_bwd_strided (backward), attn_fwd_variant (other copy
+ * attn_bwd / attn_bwd_strided / attn_bwd_noalloc (backward), attn_fwd_variant (other copy
  * schedules, for A/B measurements), and host-only planning helpers.  The
  * unfused comparator (attn_fwd_unfused) is in its own library, declared in
  * attn_unfused.h.
@@ -185,6 +185,28 @@ int attn_bwd_strided(const void* q, const void* k, const void* v, const void* o,
                      const int64_t* do_strides, const int64_t* dq_strides,
                      const int64_t* dk_strides, const int64_t* dv_strides, float scale,
                      int causal, int dtype, void* stream);
+
+/*
+ * attn_bwd_noalloc -- attn_bwd that allocates nothing and takes no
+ * workspace, for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments, checks, results and errors as attn_bwd, except that D_i
+ * (attn_bwd's `delta`) is not returned: it lives in a file-scope device
+ * array of the library, 16 MiB per GPU (2^22 fp32 rows), held from the
+ * library's load until the process ends.  B*H*Sq above 2^22 returns
+ * ATTN_ERR_BAD_ARGUMENT before any HIP call.  The array's address on the
+ * current device is looked up once per device (hipGetSymbolAddress); after
+ * that no call makes a runtime allocation.  Every call on a GPU shares that
+ * GPU's array: calls that overlap in time on one GPU (different streams,
+ * threads or processes sharing a context) race on D_i and must be
+ * serialised by the caller.  Each call writes every D_i it reads before
+ * reading it, so nothing needs clearing between calls.
+ */
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                     const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                     int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
+                     float scale, int causal, int dtype, void* stream);
 
 /*
  * attn_fwd_variant -- attn_fwd with another copy schedule, for A/B

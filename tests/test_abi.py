@@ -453,3 +453,27 @@ def test_bwd_strided_valid_layouts_reach_the_device_check():
                "dv": bshd_k}
     assert bscall(layouts) == 8, _lib.last_error()
     assert bscall({}) == 8, _lib.last_error()
+
+
+# --------------------------------------------------------------------------
+# attn_bwd_noalloc: the scratch bound is checked before any HIP call
+# --------------------------------------------------------------------------
+def nacall(B=1, H=2, Sq=16, Skv=24, D=64, gap=MB_):
+    p = [FAKE + i * gap for i in range(9)]
+    return _lib.attn_bwd_noalloc(*p, B, H, Sq, Skv, D, 0.125, 0, 0, 0)
+
+
+def test_noalloc_rejects_more_rows_than_the_scratch_holds():
+    assert nacall(B=1, H=1, Sq=(1 << 22) + 1, Skv=8) == 10
+    assert "scratch" in _lib.last_error()
+    assert nacall(B=4, H=1 << 10, Sq=1 << 10 | 1, Skv=8) == 10
+    assert nacall(D=96) == 3  # the ordinary checks still apply
+
+
+def test_noalloc_valid_call_reaches_the_device_check():
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("would launch on a real GPU with fake pointers")
+    assert nacall() == 8, _lib.last_error()
+    assert nacall(B=1, H=1, Sq=1 << 22, Skv=8, gap=1 << 30) == 8, _lib.last_error()
+    assert nacall(B=0) == 0
