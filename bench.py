@@ -53,6 +53,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd TFLOPS + % of MI355X fp16/bf16 MFMA peak, hd128 causal/non-causal"
 PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
 HEADLINE = "c4_b2h16s4096d128_fp16_peaky"
+HEADLINE_SHAPE = (2, 16, 4096, 128, "fp16", False)  # the profiled HBM-traffic figure's workload
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_c4_hbm_traffic.txt")
 
 
@@ -159,6 +160,27 @@ def time_workload(ea, shape, dev, steps, warmup):
     return total / steps, per, o, lse, warmed
 
 
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+
+
+def roofline(shape, ms_kernel):
+    """The bound of the workload's kernel: MFMA when its FLOPs at the dense
+    fp16/bf16 peak take longer than its algorithmic bytes at the HBM peak,
+    else HBM; achieved = the algorithmic work per launch / the mean launch."""
+    B, H, S, D, dtype, causal = shape
+    f, nb = flops(B, H, S, D, causal), min_bytes(B, H, S, D)
+    t = ms_kernel * 1e-3
+    common = {"traffic": read_traffic() if shape == HEADLINE_SHAPE else None, "algorithmic_flop": f,
+              "algorithmic_min_hbm_bytes": nb}
+    if f / (PEAK_TFLOPS * 1e12) >= nb / (PEAK_HBM_GBS * 1e9):
+        a = f / t / 1e12
+        return {"bound": "mfma", "achieved": round(a, 2), "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(a / PEAK_TFLOPS, 4), **common}
+    a = nb / t / 1e9
+    return {"bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(a / PEAK_HBM_GBS, 4), **common}
+
+
 def launch_stats(per_ms):
     """Per-launch durations (HIP events around each launch) in microseconds."""
     a = np.asarray(per_ms, dtype=np.float64) * 1e3
@@ -203,9 +225,11 @@ class ClockSampler:
             return float(c)
         return float(self.api.amdsmi_get_clock_info(self.handle, self.api.AmdSmiClkType.GFX)["clk"])
 
-    def during(self, launch, ms=200.0, period_s=0.002):
+    def during(self, launch, ms=1500.0, skip_ms=500.0, period_s=0.005):
         """Runs launch() back to back for about `ms` of wall time (synchronised
-        every 20 launches) while a thread samples the clock; returns a dict."""
+        every 20 launches) while a thread samples the clock; the samples of the
+        first `skip_ms` are dropped (the metrics table amdsmi reads lags the
+        clock by a few hundred milliseconds).  Returns a dict."""
         import threading
 
         import torch
@@ -216,7 +240,9 @@ class ClockSampler:
         def loop():
             while not stop.is_set():
                 try:
-                    samples.append(self.read_mhz())
+                    mhz = self.read_mhz()
+                    if (time.perf_counter() - t0) * 1e3 >= skip_ms:
+                        samples.append(mhz)
                 except Exception as e:  # noqa: BLE001
                     errs.append(str(e))
                     return
@@ -238,8 +264,9 @@ class ClockSampler:
         return {"mhz_median": round(float(np.median(a)), 1), "mhz_min": round(float(a.min()), 1),
                 "mhz_max": round(float(a.max()), 1), "samples": int(a.size), "launches": n,
                 "window_ms": round((time.perf_counter() - t0) * 1e3, 1),
-                "source": "amdsmi gpu_metrics current_gfxclks (mean over XCDs), sampled every 2 ms "
-                          "while the kernel ran back to back after the timed region"}
+                "source": f"amdsmi gpu_metrics current_gfxclks (mean over the XCDs), sampled every "
+                          f"{period_s * 1e3:.0f} ms from {skip_ms:.0f} ms on while the kernel ran back to back "
+                          f"after the timed region"}
 
 
 def bwd_flops(B, H, S, D, causal, gemms=5):
@@ -396,7 +423,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU leg: the timed fp64 oracle over every workload and the "
                          "comparison of every output element against it")
-    ap.add_argument("--clock-ms", type=float, default=200.0,
+    ap.add_argument("--clock-ms", type=float, default=1500.0,
                     help="after the timed region, run the headline kernel back to back this long "
                          "while sampling the shader clock (0: skip)")
     ap.add_argument("--no-others", action="store_true", help="skip timing the other workloads")
@@ -552,10 +579,7 @@ def main():
         "config": {"workload": args.workload, "B": B, "H": H, "S": S, "D": D, "dtype": dtype,
                    "causal": causal, "scale": "1/sqrt(D)", "global_batch": B, "seq_len": S,
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
-                     "traffic": read_traffic(),
-                     "algorithmic_min_hbm_bytes": min_bytes(B, H, S, D)},
+        "roofline": roofline(shape, ms_kernel),
         "launch_stats": stats,
         "shader_clock": clock,
         "cpu_baseline": cpu,

@@ -186,6 +186,7 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int64_
   pr.q_ss = (int)vq.ss, pr.k_ss = (int)vk.ss, pr.v_ss = (int)vv.ss, pr.o_ss = (int)vo.ss;
   pr.Sq = (int)Sq, pr.Skv = (int)Skv, pr.H = (int)H, pr.nq = (int)plan.num_q_tiles;
   pr.G = plan.num_workgroups;
+  pr.hchunk = attn::causal_head_chunk(Skv, D);
   // |scale| * log2(e), kept >= FLT_MIN: a masked score (-inf) times c must
   // stay -inf, never NaN, and for scale == 0 every kept score times FLT_MIN
   // is far below one ulp of the row max, so the softmax is exactly uniform.
@@ -435,7 +436,7 @@ int attn_fwd_workgroup_tile(int64_t B, int64_t H, int64_t S, int64_t D, int caus
   if (wg < 0 || wg >= p.num_workgroups)
     return fail(ATTN_ERR_BAD_ARGUMENT, "workgroup %lld outside [0, %lld)", (long long)wg,
                 (long long)p.num_workgroups);
-  attn::workgroup_tile(wg, p.num_workgroups, p.num_q_tiles, causal != 0, q_tile, bh);
+  attn::workgroup_tile(wg, p.num_workgroups, p.num_q_tiles, causal != 0, attn::causal_head_chunk(S, D), q_tile, bh);
   return ok();
 }
 

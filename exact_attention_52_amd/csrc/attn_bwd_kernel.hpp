@@ -242,7 +242,7 @@ void attn_bwd_dkdv(const BwdProblem p) {
     bh = (int64_t)blockIdx.x % p.BH;
     kt64 = (int64_t)blockIdx.x / p.BH;
   } else {
-    workgroup_tile(blockIdx.x, p.BH * p.nk, p.nk, 0, &kt64, &bh);
+    workgroup_tile(blockIdx.x, p.BH * p.nk, p.nk, 0, 0, &kt64, &bh);
   }
   const int Sq = p.Sq, Skv = p.Skv, koff = Skv - Sq;
   const int k0 = (int)kt64 * BN, kbase = k0 + 32 * wave, my_k = kbase + col;
@@ -447,7 +447,7 @@ void attn_bwd_dq(const BwdProblem p) {
   const int col = lane & 31, half = lane >> 5;
 
   int64_t tile64, bh;
-  workgroup_tile(blockIdx.x, p.BH * p.nq, p.nq, CAUSAL, &tile64, &bh);
+  workgroup_tile(blockIdx.x, p.BH * p.nq, p.nq, CAUSAL, 0, &tile64, &bh);
   const int Sq = p.Sq, Skv = p.Skv, koff = Skv - Sq;
   const int q0 = (int)tile64 * BM, wq_first = q0 + 32 * wave, my_q = wq_first + col;
   const uint16_t* kh = head_ptr(p.k, p.s_k, bh, p.H);

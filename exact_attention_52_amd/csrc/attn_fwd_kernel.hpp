@@ -291,27 +291,52 @@ constexpr float kRescaleSlack = 8.0f;
 // round-robin in id order, so id g runs on XCD g % 8, and each XCD gives its
 // next workgroup to the first CU that frees up.
 //   Causal: tile costs differ (query tile t has t+1 tiles' worth of keys), so
-//   ids go in order of decreasing cost: id g takes the (g / heads)-th tile
-//   counted from the last and head g % heads.  Every XCD then runs its share
-//   longest first (list scheduling in longest-processing-time order, which
-//   pairs long and short tiles on each CU), and when heads is a multiple of 8
-//   all tiles of head h run on XCD h % 8 and share its L2.
+//   each XCD runs its tiles longest first (list scheduling in
+//   longest-processing-time order pairs long and short tiles on each CU).
+//   When heads is a multiple of 8, head h runs on XCD h % 8, and each XCD
+//   works through its heads `hchunk` at a time: all tiles of a chunk of heads
+//   in order of decreasing cost, then the next chunk.  The K/V rows the
+//   XCD's running workgroups read then belong to a few heads and stay in its
+//   4 MB L2 (with every head's last tile first, 64 heads' K/V at once went
+//   through HBM 3.15x over).  hchunk >= heads / 8 gives one chunk: plain
+//   longest-first over the XCD's heads.  Otherwise (heads not a multiple of
+//   8) id g takes the (g / heads)-th tile counted from the last and head
+//   g % heads.
 //   Non-causal: equal costs; each XCD gets a contiguous run of logical work
 //   (whole heads where the counts allow), in head order.
-__host__ __device__ inline void workgroup_tile(int64_t g, int64_t G, int64_t nq, int causal,
+__host__ __device__ inline void workgroup_tile(int64_t g, int64_t G, int64_t nq, int causal, int64_t hchunk,
                                                int64_t* tile, int64_t* bh) {
-  if (causal) {
-    const int64_t heads = G / nq;
-    *bh = g % heads;
-    *tile = nq - 1 - g / heads;
-    return;
-  }
   const int64_t X = 8;
   const int64_t xcd = g % X, slot = g / X;
+  if (causal) {
+    const int64_t heads = G / nq;
+    if (heads % X != 0 || hchunk <= 0) {
+      *bh = g % heads;
+      *tile = nq - 1 - g / heads;
+      return;
+    }
+    const int64_t hx = heads / X;                   // heads of this XCD
+    const int64_t c = hchunk < hx ? hchunk : hx;    // heads per chunk
+    const int64_t chunk = slot / (c * nq);
+    const int64_t r = slot - chunk * c * nq;
+    const int64_t cw = (hx - chunk * c) < c ? (hx - chunk * c) : c;  // heads in this chunk
+    *tile = nq - 1 - r / cw;
+    *bh = (chunk * c + r % cw) * X + xcd;
+    return;
+  }
   const int64_t base = G / X, rem = G % X;
   const int64_t logical = xcd * base + (xcd < rem ? xcd : rem) + slot;
   *bh = logical / nq;
   *tile = logical % nq;
+}
+
+// Heads per chunk of the causal order above: as many as keep the chunk's K
+// and V rows within kL2ChunkBytes of the XCD's L2.
+constexpr int64_t kL2ChunkBytes = (int64_t)4 << 20;
+__host__ __device__ inline int64_t causal_head_chunk(int64_t Skv, int64_t D) {
+  const int64_t kv = 4 * Skv * D;  // K and V rows of one head, 16-bit
+  const int64_t c = kv > 0 ? kL2ChunkBytes / kv : kL2ChunkBytes;
+  return c > 1 ? c : 1;
 }
 
 // ---------------------------------------------------------------------------
@@ -331,6 +356,7 @@ struct Problem {
   int q_ss, k_ss, v_ss, o_ss;                              // row strides (>= D)
   int Sq, Skv, H, nq;                                      // nq query tiles per head
   int64_t G;                                               // workgroups
+  int64_t hchunk;                                          // heads per chunk (causal order)
   float c;                                                 // |scale| * log2(e), > 0
   uint32_t qsign;  // 0x80008000 when scale < 0: Q is negated in registers
 };
@@ -825,7 +851,7 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(const Problem p) {
   const bool producer = C::PRODUCER && wave == C::NW;
 
   int64_t tile64, bh64;
-  workgroup_tile(blockIdx.x, p.G, p.nq, CAUSAL, &tile64, &bh64);
+  workgroup_tile(blockIdx.x, p.G, p.nq, CAUSAL, p.hchunk, &tile64, &bh64);
   const int q0 = (int)tile64 * BM;
   const HeadView hv = head_view(p, bh64);
 
@@ -1111,7 +1137,7 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_pingpong_kernel(const Problem 
   const int group = wave >> 2;
 
   int64_t tile64, bh64;
-  workgroup_tile(blockIdx.x, p.G, p.nq, CAUSAL, &tile64, &bh64);
+  workgroup_tile(blockIdx.x, p.G, p.nq, CAUSAL, p.hchunk, &tile64, &bh64);
   const int q0 = (int)tile64 * BM;
   const HeadView hv = head_view(p, bh64);
 

@@ -123,18 +123,30 @@ def test_workgroup_map_is_bijection_and_longest_first(B, H, S, D, causal):
     G, nq = p["num_workgroups"], p["num_q_tiles"]
     seen = set()
     last = {}
+    heads = B * H
+    chunk_heads = {}  # XCD -> heads of its current chunk
     for wg in range(G):
         t, bh = ea.attn_fwd_workgroup_tile(B, H, S, D, causal, 0, wg)
         assert 0 <= t < nq and 0 <= bh < B * H
         seen.add((t, bh))
         if causal:
-            # each XCD (wg % 8) is handed its tiles in order of non-increasing cost
-            # (tile t costs t + 1 key tiles)
             key = wg % 8
-            assert last.get(key, nq) >= t
-            last[key] = t
-            if (B * H) % 8 == 0:
+            if heads % 8 == 0:
                 assert bh % 8 == wg % 8  # a head's tiles share one XCD
+                # each XCD works through chunks of its heads; within a chunk
+                # its tiles come in order of non-increasing cost (tile t
+                # costs t + 1 key tiles), and a new chunk starts at the last
+                # tile of heads the XCD has not seen yet
+                cur = chunk_heads.setdefault(key, set())
+                if bh not in cur:
+                    if last.get(key, nq) < t:
+                        assert t == nq - 1 and all((tt, h) in seen for h in cur for tt in range(nq))
+                        cur.clear()
+                    cur.add(bh)
+                assert last.get(key, nq) >= t or t == nq - 1
+            else:
+                assert last.get(key, nq) >= t  # longest first over the whole grid
+            last[key] = t
     assert len(seen) == G
     if causal:
         t0, _ = ea.attn_fwd_workgroup_tile(B, H, S, D, causal, 0, 0)
@@ -143,10 +155,20 @@ def test_workgroup_map_is_bijection_and_longest_first(B, H, S, D, causal):
         ea.attn_fwd_workgroup_tile(B, H, S, D, causal, 0, G)
 
 
+def test_causal_map_chunks_heads_within_the_l2_budget():
+    # c2 (B16 H32 S1024 D64): K and V of a head are 256 KiB, so a chunk holds
+    # 16 heads (4 MiB); every XCD's first 16 * 8 workgroups cover 16 heads
+    B, H, S, D = 16, 32, 1024, 64
+    for x in range(8):
+        first = {ea.attn_fwd_workgroup_tile(B, H, S, D, True, 0, wg)[1] for wg in range(x, 8 * 128, 8)}
+        assert len(first) == 16 and all(h % 8 == x for h in first)
+
+
 def test_causal_map_balances_each_xcd():
     # c3 (B4 H16 S2048 D128 causal): 64 x 8 tiles, tile t costs t + 1. Greedy
     # list scheduling of each XCD's workgroups, in id order, onto 32 CUs that
-    # each hold one workgroup at a time gives every CU the same total.
+    # each hold one workgroup at a time gives every CU the same total (with
+    # 1 MiB of K and V per head, a chunk is 4 of the XCD's 8 heads).
     B, H, S, D = 4, 16, 2048, 128
     p = ea.attn_fwd_plan(B, H, S, D, True, 1)
     G = p["num_workgroups"]

@@ -85,3 +85,14 @@ def test_full_parity_checks_every_element():
     rate = bench.oracle_rate(shape, 2.0)
     assert rate["kind"] == "oracle" and rate["cores"] >= 1
     assert rate["value"] == pytest.approx(bench.flops(B, H, S, D, causal) / 2.0 / 1e12)
+
+
+def test_roofline_bound_follows_the_workload():
+    # c4: 2.75e11 FLOP at 2.5 PFLOP/s (110 us) against 134.7 MB at 8 TB/s (17 us): MFMA-bound
+    r = bench.roofline((2, 16, 4096, 128, "fp16", False), 0.25)
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s"
+    assert r["achieved"] == pytest.approx(bench.flops(2, 16, 4096, 128, False) / 0.25e-3 / 1e12, rel=1e-5)
+    # c2: 6.87e10 FLOP (27.5 us) against 270.5 MB (33.8 us): HBM-bound
+    r = bench.roofline((16, 32, 1024, 64, "fp16", True), 0.1)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["traffic"] is None
+    assert r["achieved"] == pytest.approx(bench.min_bytes(16, 32, 1024, 64) / 0.1e-3 / 1e9, rel=1e-3)
