@@ -329,6 +329,9 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   for (int i = 0; i < 8; ++i) *ps[i] = attn::Strides{vs[i].sb, vs[i].sh, (int)vs[i].ss};
   p.H = (int)H;
   p.Sq = (int)Sq, p.Skv = (int)Skv, p.nq = 0, p.nk = 0, p.BH = B * H;
+  // the dQ kernel streams K and V of its head, the dK/dV kernel Q and dO
+  p.hchunk_q = attn::causal_head_chunk(Skv, D);
+  p.hchunk_k = attn::causal_head_chunk(Sq, D);
   // the backward masks P itself (never a score), so c may take any sign;
   // a tiny positive c is kept >= FLT_MIN as in the forward
   float c = (float)((double)scale * 1.4426950408889634074);

@@ -33,6 +33,7 @@ struct BwdProblem {
   int Sq, Skv;
   int nq, nk;  // query tiles per head (dQ kernel), key tiles per head (dK/dV kernel)
   int64_t BH;  // B * H
+  int64_t hchunk_q, hchunk_k;  // heads per chunk of the causal orders (dQ, dK/dV kernels)
   float c;     // scale * log2(e), kept >= FLT_MIN
   float scale;
 };

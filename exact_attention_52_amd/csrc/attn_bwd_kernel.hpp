@@ -187,6 +187,60 @@ struct BwdCfg {
   static_assert(X::LINES % NW == 0, "copy lines must split evenly over the waves");
 };
 
+// Store a wave's 32 rows of a [rows, D] output held in the transposed MFMA
+// accumulator layout (lane l: row row0 + l%32, columns 32db + 8g + 4*half +
+// 0..3), each value times sc and rounded to 16 bits.  Stored directly, one
+// store instruction writes 8 bytes into each of 32 rows; STAGED, the wave
+// first writes the rows into its own LDS area (padded rows, so the 8-byte
+// pieces of 32 rows hit distinct banks), reads them back as whole rows and
+// stores 16 contiguous bytes per lane: 8x fewer memory requests at D=128.
+template <int D, int DT, bool STAGED>
+__device__ __forceinline__ void store_rows(uint8_t* area, const f32x16 (&acc)[D / 32], float sc, uint16_t* head,
+                                           int64_t ss, int row0, int rows, int lane) {
+  using E = Elem<DT>;
+  constexpr int DB = D / 32;
+  const int half = lane >> 5, my = row0 + (lane & 31);
+  if constexpr (!STAGED) {
+    if (my >= rows) return;
+    uint16_t* r = head + (int64_t)my * ss;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 w;
+        w[0] = E::pack2(acc[db][4 * g] * sc, acc[db][4 * g + 1] * sc);
+        w[1] = E::pack2(acc[db][4 * g + 2] * sc, acc[db][4 * g + 3] * sc);
+        *reinterpret_cast<u32x2*>(r + 32 * db + 8 * g + 4 * half) = w;
+      }
+    }
+  } else {
+    constexpr int RS = 2 * D + 16;  // staged row stride (bytes)
+    uint8_t* mine = area + (lane & 31) * RS;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 w;
+        w[0] = E::pack2(acc[db][4 * g] * sc, acc[db][4 * g + 1] * sc);
+        w[1] = E::pack2(acc[db][4 * g + 2] * sc, acc[db][4 * g + 3] * sc);
+        *reinterpret_cast<u32x2*>(mine + 2 * (32 * db + 8 * g + 4 * half)) = w;
+      }
+    }
+    // a wave's LDS accesses execute in order; keep the compiler from moving
+    // the reads above the writes (or a later reuse of the area above them)
+    __asm__ volatile("" ::: "memory");
+    constexpr int LPR = D / 8, RPI = 64 / LPR;  // lanes per row, rows per store instruction
+    const int rl = lane / LPR, cl = lane % LPR;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = i * RPI + rl;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(area + r * RS + 16 * cl);
+      if (row0 + r < rows) *reinterpret_cast<u32x4*>(head + (int64_t)(row0 + r) * ss + 8 * cl) = v;
+    }
+    __asm__ volatile("" ::: "memory");
+  }
+}
+
 // Lane part of a transposing read (ds_read_b64_tr_b16) of an XTile: in each
 // 16-lane group lane i reads row i/4 of 4 consecutive rows (4*half + i/4
 // after the k-slot order of the packed 16-bit operands) at columns
@@ -236,14 +290,11 @@ void attn_bwd_dkdv(const BwdProblem p) {
   const int col = lane & 31, half = lane >> 5;
 
   // key tiles in order of decreasing cost when causal (key tile 0 is seen by
-  // the most queries); otherwise contiguous runs per XCD as in the forward
+  // the most queries), in chunks of heads per XCD as the forward's query
+  // tiles; otherwise contiguous runs per XCD as in the forward
   int64_t kt64, bh;
-  if (CAUSAL) {
-    bh = (int64_t)blockIdx.x % p.BH;
-    kt64 = (int64_t)blockIdx.x / p.BH;
-  } else {
-    workgroup_tile(blockIdx.x, p.BH * p.nk, p.nk, 0, 0, &kt64, &bh);
-  }
+  workgroup_tile(blockIdx.x, p.BH * p.nk, p.nk, CAUSAL, p.hchunk_k, &kt64, &bh);
+  if (CAUSAL) kt64 = p.nk - 1 - kt64;
   const int Sq = p.Sq, Skv = p.Skv, koff = Skv - Sq;
   const int k0 = (int)kt64 * BN, kbase = k0 + 32 * wave, my_k = kbase + col;
   const uint16_t* qh = head_ptr(p.q, p.s_q, bh, p.H);
@@ -404,25 +455,15 @@ void attn_bwd_dkdv(const BwdProblem p) {
     step(s + 1, qt1, ot1, ls1, dl1);
   }
 
-  if (my_k < Skv) {
-    uint16_t* dkr = head_ptr(p.dk, p.s_dk, bh, p.H) + (int64_t)my_k * p.s_dk.ss;
-    uint16_t* dvr = head_ptr(p.dv, p.s_dv, bh, p.H) + (int64_t)my_k * p.s_dv.ss;
-    const float sc = p.scale;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = 32 * db + 8 * g + 4 * half;
-        u32x2 wk, wv;
-        wk[0] = E::pack2(dka[db][4 * g] * sc, dka[db][4 * g + 1] * sc);
-        wk[1] = E::pack2(dka[db][4 * g + 2] * sc, dka[db][4 * g + 3] * sc);
-        wv[0] = E::pack2(dva[db][4 * g], dva[db][4 * g + 1]);
-        wv[1] = E::pack2(dva[db][4 * g + 2], dva[db][4 * g + 3]);
-        *reinterpret_cast<u32x2*>(dkr + d) = wk;
-        *reinterpret_cast<u32x2*>(dvr + d) = wv;
-      }
-    }
-  }
+  // dK, dV: through LDS where a wave's 32 padded rows fit in one stage array
+  // (D <= 128; every wave is done with the stages after this barrier, and
+  // no copy is in flight), except in the causal D=128 kernel, whose loop
+  // takes all 256 registers: there the staging code made the compiler spill
+  constexpr bool STAGED = 32 * (2 * D + 16) <= X::BYTES && !(CAUSAL && D == 128);
+  if constexpr (STAGED) __syncthreads();
+  uint8_t* const area = wave == 0 ? qt0 : wave == 1 ? qt1 : wave == 2 ? ot0 : ot1;
+  store_rows<D, DT, STAGED>(area, dka, p.scale, head_ptr(p.dk, p.s_dk, bh, p.H), p.s_dk.ss, kbase, Skv, lane);
+  store_rows<D, DT, STAGED>(area, dva, 1.f, head_ptr(p.dv, p.s_dv, bh, p.H), p.s_dv.ss, kbase, Skv, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -447,7 +488,7 @@ void attn_bwd_dq(const BwdProblem p) {
   const int col = lane & 31, half = lane >> 5;
 
   int64_t tile64, bh;
-  workgroup_tile(blockIdx.x, p.BH * p.nq, p.nq, CAUSAL, 0, &tile64, &bh);
+  workgroup_tile(blockIdx.x, p.BH * p.nq, p.nq, CAUSAL, p.hchunk_q, &tile64, &bh);
   const int Sq = p.Sq, Skv = p.Skv, koff = Skv - Sq;
   const int q0 = (int)tile64 * BM, wq_first = q0 + 32 * wave, my_q = wq_first + col;
   const uint16_t* kh = head_ptr(p.k, p.s_k, bh, p.H);
@@ -575,21 +616,11 @@ void attn_bwd_dq(const BwdProblem p) {
     step(j + 1, kt1, vt1);
   }
 
-  if (q_ok) {
-    uint16_t* dqr = head_ptr(p.dq, p.s_dq, bh, p.H) + (int64_t)my_q * p.s_dq.ss;
-    const float sc = p.scale;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = 32 * db + 8 * g + 4 * half;
-        u32x2 w;
-        w[0] = E::pack2(dqa[db][4 * g] * sc, dqa[db][4 * g + 1] * sc);
-        w[1] = E::pack2(dqa[db][4 * g + 2] * sc, dqa[db][4 * g + 3] * sc);
-        *reinterpret_cast<u32x2*>(dqr + d) = w;
-      }
-    }
-  }
+  // dQ: through LDS where a wave's 32 padded rows fit in one stage array
+  constexpr bool STAGED = 32 * (2 * D + 16) <= X::BYTES;
+  if constexpr (STAGED) __syncthreads();
+  uint8_t* const area = wave == 0 ? kt0 : wave == 1 ? kt1 : wave == 2 ? vt0 : vt1;
+  store_rows<D, DT, STAGED>(area, dqa, p.scale, head_ptr(p.dq, p.s_dq, bh, p.H), p.s_dq.ss, wq_first, Sq, lane);
 }
 
 }  // namespace bwd

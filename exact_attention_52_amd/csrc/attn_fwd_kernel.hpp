@@ -304,28 +304,31 @@ constexpr float kRescaleSlack = 8.0f;
 //   g % heads.
 //   Non-causal: equal costs; each XCD gets a contiguous run of logical work
 //   (whole heads where the counts allow), in head order.
-__host__ __device__ inline void workgroup_tile(int64_t g, int64_t G, int64_t nq, int causal, int64_t hchunk,
+__host__ __device__ inline void workgroup_tile(int64_t g64, int64_t G64, int64_t nq64, int causal, int64_t hchunk64,
                                                int64_t* tile, int64_t* bh) {
-  const int64_t X = 8;
-  const int64_t xcd = g % X, slot = g / X;
+  // grids stay below 2^31 workgroups (checked at launch): 32-bit arithmetic
+  const uint32_t g = (uint32_t)g64, G = (uint32_t)G64, nq = (uint32_t)nq64;
+  const uint32_t X = 8;
+  const uint32_t xcd = g % X, slot = g / X;
   if (causal) {
-    const int64_t heads = G / nq;
-    if (heads % X != 0 || hchunk <= 0) {
+    const uint32_t heads = G / nq;
+    const uint32_t hchunk = hchunk64 > (int64_t)heads ? heads : (uint32_t)(hchunk64 > 0 ? hchunk64 : 0);
+    if (heads % X != 0 || hchunk == 0) {
       *bh = g % heads;
       *tile = nq - 1 - g / heads;
       return;
     }
-    const int64_t hx = heads / X;                   // heads of this XCD
-    const int64_t c = hchunk < hx ? hchunk : hx;    // heads per chunk
-    const int64_t chunk = slot / (c * nq);
-    const int64_t r = slot - chunk * c * nq;
-    const int64_t cw = (hx - chunk * c) < c ? (hx - chunk * c) : c;  // heads in this chunk
+    const uint32_t hx = heads / X;                 // heads of this XCD
+    const uint32_t c = hchunk < hx ? hchunk : hx;  // heads per chunk
+    const uint32_t chunk = slot / (c * nq);
+    const uint32_t r = slot - chunk * c * nq;
+    const uint32_t cw = (hx - chunk * c) < c ? (hx - chunk * c) : c;  // heads in this chunk
     *tile = nq - 1 - r / cw;
-    *bh = (chunk * c + r % cw) * X + xcd;
+    *bh = (int64_t)(chunk * c + r % cw) * X + xcd;
     return;
   }
-  const int64_t base = G / X, rem = G % X;
-  const int64_t logical = xcd * base + (xcd < rem ? xcd : rem) + slot;
+  const uint32_t base = G / X, rem = G % X;
+  const uint32_t logical = xcd * base + (xcd < rem ? xcd : rem) + slot;
   *bh = logical / nq;
   *tile = logical % nq;
 }
