@@ -133,7 +133,14 @@ def warm_up(launch, warmup, min_ms=MIN_WARM_MS):
             return done
 
 
-def time_workload(ea, shape, dev, steps, warmup):
+def fwd_launcher(ea, q, k, v, scale, causal, o, lse, stream, variant=0):
+    """One forward launch: attn_fwd, or attn_fwd_variant's copy schedule `variant`."""
+    if variant:
+        return lambda: ea.fwd_variant(q, k, v, variant, scale=scale, causal=causal, out=o, lse=lse, stream=stream)
+    return lambda: ea.fwd(q, k, v, scale=scale, causal=causal, out=o, lse=lse, stream=stream)
+
+
+def time_workload(ea, shape, dev, steps, warmup, variant=0):
     """Returns (ms_per_step over the timed region, per-launch ms list, o, lse,
     warm-up launches run)."""
     import torch
@@ -143,7 +150,8 @@ def time_workload(ea, shape, dev, steps, warmup):
     o = torch.empty_like(q)
     lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
     stream = torch.cuda.current_stream()
-    warmed = warm_up(lambda: ea.fwd(q, k, v, scale=scale, causal=causal, out=o, lse=lse, stream=stream), warmup)
+    launch = fwd_launcher(ea, q, k, v, scale, causal, o, lse, stream, variant)
+    warmed = warm_up(launch, warmup)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -151,7 +159,7 @@ def time_workload(ea, shape, dev, steps, warmup):
     t0.record(stream)
     for i in range(steps):
         ev[i][0].record(stream)
-        ea.fwd(q, k, v, scale=scale, causal=causal, out=o, lse=lse, stream=stream)
+        launch()
         ev[i][1].record(stream)
     t1.record(stream)
     torch.cuda.synchronize()
@@ -420,6 +428,9 @@ def main():
     # steady ~241 from about the 60th on), so the default warm-up covers it
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--variant", type=int, default=0,
+                    help="time attn_fwd_variant's copy schedule VARIANT instead of attn_fwd (A/B runs; "
+                         "0 is attn_fwd itself)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU leg: the timed fp64 oracle over every workload and the "
                          "comparison of every output element against it")
@@ -452,7 +463,7 @@ def main():
 
     shape, words, dev = make_inputs(args.workload)
     B, H, S, D, dtype, causal = shape
-    ms_step, per, o, lse, warmed = time_workload(ea, shape, dev, args.steps, args.warmup)
+    ms_step, per, o, lse, warmed = time_workload(ea, shape, dev, args.steps, args.warmup, args.variant)
     stats = launch_stats(per)
     ms_kernel = stats["mean_us"] * 1e-3
     f = flops(B, H, S, D, causal)
@@ -466,8 +477,8 @@ def main():
     if args.clock_ms > 0:
         scale = float(np.float32(1.0 / math.sqrt(D)))
         stream = torch.cuda.current_stream()
-        clock = ClockSampler().during(
-            lambda: ea.fwd(*dev, scale=scale, causal=causal, out=o, lse=lse, stream=stream), ms=args.clock_ms)
+        clock = ClockSampler().during(fwd_launcher(ea, *dev, scale, causal, o, lse, stream, args.variant),
+                                      ms=args.clock_ms)
         print(f"# shader clock: {clock}", file=sys.stderr, flush=True)
     del o, lse
 
@@ -576,7 +587,7 @@ def main():
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic (seeded Philox4x32-10 + Box-Muller)",
-        "config": {"workload": args.workload, "B": B, "H": H, "S": S, "D": D, "dtype": dtype,
+        "config": {"workload": args.workload, "variant": args.variant, "B": B, "H": H, "S": S, "D": D, "dtype": dtype,
                    "causal": causal, "scale": "1/sqrt(D)", "global_batch": B, "seq_len": S,
                    "parallelism": "single GPU"},
         "roofline": roofline(shape, ms_kernel),
