@@ -4,13 +4,16 @@
 //   1. S = scale * Q K^T for every (b, h), fp32, written to a workspace
 //      (rocBLAS strided-batched GEMM over the B*H heads);
 //   2. one workgroup per row: mask, row max, P = exp(s - m) rounded to the
-//      input dtype, LSE = m + log l, and 1 / (the sum of the rounded P);
+//      input dtype, LSE = m + log l, and 1 / l, l the fp32 sum of P;
 //   3. O = P V (rocBLAS strided-batched GEMM, fp32 accumulation and output);
 //   4. O times that factor per row, rounded to the input dtype.
-// Normalising by the sum of the rounded P, as the fused kernels do, makes O
-// an exact convex combination of V rows with the weights the GEMM used
-// (rounding the normalised P instead moves a peaky fp16 row by up to u/2 of
-// its largest V entries).
+// P is taken against the exact row max, so the row's largest P is exp(0) =
+// 1, exact in 16 bits, and O normalised by the fp32 sum then carries only the
+// other keys' 16-bit rounding, weighted by their (small) P.  Rounding the
+// normalised P instead moves a peaky fp16 row by up to u/2 of its largest V
+// entries; normalising by the sum of the rounded P multiplies the other keys'
+// rounding by V_j - O, which reached 2.03e-3 (over the 2e-3 fp16 bound) on a
+// peaky row with |O| ~ 4.5.
 // The batched 4-D GEMM of the docs.rs page "aprender-train 0.36.0,
 // entrenar/autograd/cuda_forward/matmul.rs" (doc comment of
 // batched_4d_gemm_forward: C[b,h] = A[b,h] B[b,h] over [batch, heads, m, k]
@@ -40,14 +43,6 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
-
-template <int DT>
-__device__ __forceinline__ float round16(float x) {
-  if constexpr (DT == 0)
-    return (float)(_Float16)x;
-  else
-    return (float)(__bf16)x;
-}
 
 template <int DT>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
@@ -88,7 +83,7 @@ __device__ __forceinline__ float block_reduce(float x, float* red) {
 // or after the query (causal) get P = 0; a row with no key gets LSE = -inf.
 template <int NC, int DT>
 __global__ __launch_bounds__(kThreads) void row_softmax(const float* __restrict__ s, uint16_t* __restrict__ p,
-                                                        float* __restrict__ lse, float* __restrict__ inv_lr, int S,
+                                                        float* __restrict__ lse, float* __restrict__ inv_l, int S,
                                                         int64_t ld_s, int64_t ld_p, int causal) {
   __shared__ float red[kThreads / 64];
   const int64_t row = blockIdx.x;
@@ -122,8 +117,8 @@ __global__ __launch_bounds__(kThreads) void row_softmax(const float* __restrict_
   m = block_reduce<true>(m, red);
   // exp2 offset: 0 for a row with no key (every value is -inf, P = 0)
   const float off = m == -__builtin_inff() ? 0.f : -m * kLog2e;
-  // l: fp32 sum of P (for the LSE); lr: sum of P as rounded to 16 bits
-  float l = 0.f, lr = 0.f;
+  // l: fp32 sum of P (the LSE and O's normaliser)
+  float l = 0.f;
   auto store = [&](const f32x4& pe, int c) __attribute__((always_inline)) {
     const u32x2 w = {pack2<DT>(pe[0], pe[1]), pack2<DT>(pe[2], pe[3])};
     *reinterpret_cast<u32x2*>(prow + 4 * c) = w;
@@ -133,7 +128,6 @@ __global__ __launch_bounds__(kThreads) void row_softmax(const float* __restrict_
     for (int e = 0; e < 4; ++e) {
       x[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(val(x, c, e), kLog2e, off));
       l += x[e];
-      lr += round16<DT>(x[e]);
     }
     return x;
   };
@@ -147,20 +141,19 @@ __global__ __launch_bounds__(kThreads) void row_softmax(const float* __restrict_
     for (int c = threadIdx.x; c < nchunk; c += kThreads) store(expo(*reinterpret_cast<const f32x4*>(srow + 4 * c), c), c);
   }
   l = block_reduce<false>(l, red);
-  lr = block_reduce<false>(lr, red);
   if (threadIdx.x == 0) {
     lse[row] = l > 0.f ? m + __builtin_amdgcn_logf(l) * 0.69314718055994530942f : -__builtin_inff();
-    inv_lr[row] = lr > 0.f ? 1.f / lr : 0.f;
+    inv_l[row] = l > 0.f ? 1.f / l : 0.f;
   }
 }
 
-// O = O32 * inv_lr per row, rounded to the input dtype; 8 elements a thread.
+// O = O32 * inv_l per row, rounded to the input dtype; 8 elements a thread.
 template <int DT>
-__global__ __launch_bounds__(kThreads) void scale_rows(const float* __restrict__ o32, const float* __restrict__ inv_lr,
+__global__ __launch_bounds__(kThreads) void scale_rows(const float* __restrict__ o32, const float* __restrict__ inv_l,
                                                        uint16_t* __restrict__ o, int64_t n8, int D) {
   const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (t >= n8) return;
-  const float f = inv_lr[t * 8 / D];
+  const float f = inv_l[t * 8 / D];
   const f32x4 a = *reinterpret_cast<const f32x4*>(o32 + 8 * t);
   const f32x4 b = *reinterpret_cast<const f32x4*>(o32 + 8 * t + 4);
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -195,7 +188,7 @@ const char* unfused_launch(const void* q, const void* k, const void* v, void* o,
   float* sbuf = static_cast<float*>(ws);
   uint16_t* pbuf = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + u.p_offset);
   float* o32 = reinterpret_cast<float*>(static_cast<char*>(ws) + u.o_offset);
-  float* inv_lr = reinterpret_cast<float*>(static_cast<char*>(ws) + u.r_offset);
+  float* inv_l = reinterpret_cast<float*>(static_cast<char*>(ws) + u.r_offset);
   const rocblas_datatype in_t = dtype == 0 ? rocblas_datatype_f16_r : rocblas_datatype_bf16_r;
   const int batch = (int)(B * H);
   {
@@ -220,7 +213,7 @@ const char* unfused_launch(const void* q, const void* k, const void* v, void* o,
     const int64_t rows = B * H * S;
     const int nc = (int)((S + 4 * kThreads - 1) / (4 * kThreads));
     auto go = [&](auto kern) {
-      hipLaunchKernelGGL(kern, dim3((unsigned)rows), dim3(kThreads), 0, stream, sbuf, pbuf, lse, inv_lr, (int)S,
+      hipLaunchKernelGGL(kern, dim3((unsigned)rows), dim3(kThreads), 0, stream, sbuf, pbuf, lse, inv_l, (int)S,
                          u.ld_s, u.ld_p, (int)causal);
     };
     if (dtype == 0) {
@@ -247,9 +240,9 @@ const char* unfused_launch(const void* q, const void* k, const void* v, void* o,
     const int64_t n8 = B * H * S * D / 8;
     const unsigned g = (unsigned)((n8 + kThreads - 1) / kThreads);
     if (dtype == 0)
-      hipLaunchKernelGGL(scale_rows<0>, dim3(g), dim3(kThreads), 0, stream, o32, inv_lr, (uint16_t*)o, n8, (int)D);
+      hipLaunchKernelGGL(scale_rows<0>, dim3(g), dim3(kThreads), 0, stream, o32, inv_l, (uint16_t*)o, n8, (int)D);
     else
-      hipLaunchKernelGGL(scale_rows<1>, dim3(g), dim3(kThreads), 0, stream, o32, inv_lr, (uint16_t*)o, n8, (int)D);
+      hipLaunchKernelGGL(scale_rows<1>, dim3(g), dim3(kThreads), 0, stream, o32, inv_l, (uint16_t*)o, n8, (int)D);
     if (hipGetLastError() != hipSuccess) return "row scaling kernel launch failed";
   }
   return nullptr;

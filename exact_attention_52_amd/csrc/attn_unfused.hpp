@@ -9,7 +9,7 @@ namespace attn {
 
 // Workspace layout (each part 256-byte aligned): S as fp32 rows ld_s apart;
 // P in the input dtype, rows ld_p apart; O before normalisation, fp32
-// [B,H,S,D]; per row 1 / (sum of the rounded P), fp32.
+// [B,H,S,D]; per row 1 / (fp32 sum of P), fp32.
 struct UnfusedLayout {
   int64_t ld_s, ld_p;  // elements
   int64_t s_bytes, p_offset, o_offset, r_offset, bytes;

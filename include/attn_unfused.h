@@ -26,11 +26,10 @@ extern "C" {
  * Steps: S = scale Q K^T as fp32 into the workspace (vendor strided-batched
  * GEMM over the B*H heads, the batched 4-D GEMM of the docs.rs page
  * "aprender-train 0.36.0, entrenar/autograd/cuda_forward/matmul.rs",
- * batched_4d_gemm_forward); a row softmax kernel writing P in `dtype` and
- * unnormalised P rounded to `dtype`, LSE and 1 / (sum of the rounded P); O =
- * P V (vendor GEMM, fp32 accumulation), then scaled by that factor and
- * rounded (the fused kernels normalise the same way).  Per head S*S*12 bytes
- * go through HBM.
+ * batched_4d_gemm_forward); a row softmax kernel writing the unnormalised P
+ * (against the exact row max) rounded to `dtype`, the LSE and 1 / (fp32 sum
+ * of P); O = P V (vendor GEMM, fp32 accumulation), then scaled by that factor
+ * and rounded.  Per head S*S*12 bytes go through HBM.
  *
  *   q, k, v, o, lse, B, H, S, D, scale, causal, dtype, stream: as attn_fwd.
  *   workspace        device memory of at least
