@@ -311,8 +311,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   const attn::BwdPlan plan = attn::bwd_plan((int)D);
   const int64_t gq = B * H * ((Sq + plan.dq_queries_per_workgroup - 1) / plan.dq_queries_per_workgroup);
   const int64_t gk = B * H * ((Skv + plan.dkdv_keys_per_workgroup - 1) / plan.dkdv_keys_per_workgroup);
-  const int64_t gd = (B * H * Sq + plan.delta_rows_per_workgroup - 1) / plan.delta_rows_per_workgroup;
-  if (gq > 0x7FFFFFFF || gk > 0x7FFFFFFF || gd > 0x7FFFFFFF)
+  if (gq > 0x7FFFFFFF || gk > 0x7FFFFFFF)
     return fail(ATTN_ERR_BAD_SHAPE, "grid exceeds the launch limit");
   st = check_device();
   if (st != ATTN_OK) return st;

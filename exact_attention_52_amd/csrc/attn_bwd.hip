@@ -11,7 +11,6 @@ template <int D>
 BwdPlan plan_of() {
   using C = bwd::BwdCfg<D>;
   BwdPlan p;
-  p.delta_rows_per_workgroup = 256 / (D / 8);
   p.dkdv_keys_per_workgroup = C::BN;
   p.dkdv_query_step = C::STEP;
   p.dq_queries_per_workgroup = C::BM;
@@ -24,15 +23,11 @@ BwdPlan plan_of() {
 template <int D, bool CAUSAL, int DT>
 hipError_t launch(BwdProblem p, hipStream_t st) {
   using C = bwd::BwdCfg<D>;
-  const int64_t rows = p.BH * p.Sq;
-  const int rpb = 256 / (D / 8);
-  if (rows > 0)
-    hipLaunchKernelGGL((bwd::attn_bwd_delta<D, DT>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, st,
-                       p);
-  if (p.Skv > 0 && p.BH > 0)
-    hipLaunchKernelGGL((bwd::attn_bwd_dkdv<D, CAUSAL, DT>), dim3((unsigned)(p.BH * p.nk)), dim3(C::NT), 0, st, p);
+  // the dQ kernel writes D_i, which the dK/dV kernel reads
   if (p.Sq > 0 && p.BH > 0)
     hipLaunchKernelGGL((bwd::attn_bwd_dq<D, CAUSAL, DT>), dim3((unsigned)(p.BH * p.nq)), dim3(C::NT), 0, st, p);
+  if (p.Skv > 0 && p.BH > 0)
+    hipLaunchKernelGGL((bwd::attn_bwd_dkdv<D, CAUSAL, DT>), dim3((unsigned)(p.BH * p.nk)), dim3(C::NT), 0, st, p);
   return hipGetLastError();
 }
 

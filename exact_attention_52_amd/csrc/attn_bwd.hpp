@@ -24,7 +24,7 @@ struct BwdProblem {
   const uint16_t* o;
   const uint16_t* dO;
   const float* lse;
-  float* delta;  // written by the first kernel: D_i = rowsum(dO_i * O_i)
+  float* delta;  // written by the dQ kernel (run first): D_i = rowsum(dO_i * O_i)
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
@@ -38,9 +38,8 @@ struct BwdProblem {
   float scale;
 };
 
-// Launch geometry of the three backward kernels for head dim D.
+// Launch geometry of the two backward kernels for head dim D.
 struct BwdPlan {
-  int delta_rows_per_workgroup;
   int dkdv_keys_per_workgroup;  // key tile of the dK/dV kernel
   int dkdv_query_step;          // queries per step of its loop
   int dq_queries_per_workgroup;  // query tile of the dQ kernel
@@ -51,7 +50,7 @@ struct BwdPlan {
 
 BwdPlan bwd_plan(int D);
 
-// Enqueue the delta, dK/dV and dQ kernels on `stream` (p.nq, p.nk are filled
+// Enqueue the dQ (and D_i) and dK/dV kernels on `stream` (p.nq, p.nk are filled
 // in here).  D is 64, 128 or 256; the caller has validated everything.
 hipError_t bwd_launch(BwdProblem p, int D, bool causal, int dtype, hipStream_t stream);
 

@@ -6,10 +6,9 @@
 // "oxicuda-dnn 0.1.8, src/attn/flash_attn/hopper.rs", doc comment of
 // FlashAttention3Plan::generate_backward):
 //   P_ij = exp(scale q_i.k_j - LSE_i)  (0 where masked)
-//   D_i  = rowsum(dO_i * O_i)                        kernel attn_bwd_delta
+//   D_i  = rowsum(dO_i * O_i),  dQ = scale dS K      kernel attn_bwd_dq (first)
 //   dV = P^T dO, dP = dO V^T, dS = P * (dP - D_i),
 //   dK = scale dS^T Q                                kernel attn_bwd_dkdv
-//   dQ = scale dS K                                  kernel attn_bwd_dq
 // (dS is the gradient of the scaled scores, so the chain rule puts `scale`
 // on dK and dQ.)
 //
@@ -27,6 +26,8 @@
 //     per lane), K and V tiles stream through LDS, dQ^T += K^T dS^T with K^T
 //     read transposed.  This recomputes S and dP once more instead of the
 //     page's atomic dQ accumulation: dQ is written once, deterministically.
+//     Each wave first forms D_i of its queries from their O and dO rows and
+//     writes it out for the dK/dV kernel, which runs second.
 //   * The LDS tiles are read both ways (16-byte row reads and transposing
 //     reads), so their rows are spread over 1 KiB copy lines in an order that
 //     keeps both kinds of read free of bank conflicts (XTile below).
@@ -144,29 +145,6 @@ __device__ __forceinline__ void fenced_sync() {
   __builtin_amdgcn_sched_barrier(0);
 }
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-// ---------------------------------------------------------------------------
-// D_i = sum_d dO[i,d] * O[i,d] in fp32, D/8 lanes per row.
-// ---------------------------------------------------------------------------
-template <int D, int DT>
-__global__ __launch_bounds__(256) void attn_bwd_delta(const BwdProblem p) {
-  constexpr int LPR = D / 8, RPB = 256 / LPR;
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
-  const int part = threadIdx.x % LPR;
-  float acc = 0.f;
-  if (row < p.BH * p.Sq) {
-    const int64_t bh = row / p.Sq, i = row % p.Sq;
-    const uint16_t* orow = head_ptr(p.o, p.s_o, bh, p.H) + i * p.s_o.ss;
-    const uint16_t* dorow = head_ptr(p.dO, p.s_do, bh, p.H) + i * p.s_do.ss;
-    const u32x4 a = *reinterpret_cast<const u32x4*>(orow + part * 8);
-    const u32x4 b = *reinterpret_cast<const u32x4*>(dorow + part * 8);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc = dot2<DT>(a[e], b[e], acc);
-  }
-#pragma unroll
-  for (int m = LPR / 2; m >= 1; m /= 2) acc += __shfl_xor(acc, m, 64);
-  if (row < p.BH * p.Sq && part == 0) p.delta[row] = acc;
-}
 
 // Tile shapes per head dim: every tile is one 16-line block of XTile.
 template <int D_>
@@ -395,15 +373,15 @@ void attn_bwd_dkdv(const BwdProblem p) {
       float pr[16], ds[16];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        // the 4 rows of this register group (one broadcast LDS read per half)
+        // the 4 rows of this register group (one broadcast LDS read per
+        // half): exp2 offsets and D_i
         const int rr = 32 * mb + 8 * g + 4 * half;
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + rr);
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(dl + rr);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int i = 4 * g + t;
-          const float nl = -l4[t] * kLog2e;
-          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[i], c, nl));
+          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[i], c, l4[t]));
           if (need_mask) pv = (32 * mb + 8 * g + t) >= lim ? pv : 0.f;
           pr[i] = pv;
           ds[i] = pv * (dpa[i] - d4[t]);
@@ -444,13 +422,31 @@ void attn_bwd_dkdv(const BwdProblem p) {
     }
   };
 
+  // fenced_sync, except that between the wait and the barrier each wave that
+  // copied LSE rows turns its rows, just landed, into the exp2 offsets
+  // -LSE * log2(e) in place (its own LDS accesses execute in order; the
+  // barrier's fence publishes them): one multiply per row instead of one
+  // per score.  The lane index is recomputed there by an opaque instruction
+  // pair: a lane offset hoisted out of the loop would stay live through the
+  // MFMA steps, which already take every register.
+  auto land = [&](float* ls_) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    wait_loads();
+    int ln;
+    __asm__ volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+#pragma unroll
+    for (int m = 0; m < LR / 64; ++m)
+      if (wave == 2 * m) ls_[64 * m + ln] = -ls_[64 * m + ln] * kLog2e;
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
   if (n > 0) fetch(0, qt0, ot0, ls0, dl0);
   for (int s = 0; s < n; s += 2) {
-    fenced_sync();
+    land(ls0);
     if (s + 1 < n) fetch(s + 1, qt1, ot1, ls1, dl1);
     step(s, qt0, ot0, ls0, dl0);
     if (s + 1 >= n) break;
-    fenced_sync();
+    land(ls1);
     if (s + 2 < n) fetch(s + 2, qt0, ot0, ls0, dl0);
     step(s + 1, qt1, ot1, ls1, dl1);
   }
@@ -494,22 +490,32 @@ void attn_bwd_dq(const BwdProblem p) {
   const uint16_t* kh = head_ptr(p.k, p.s_k, bh, p.H);
   const uint16_t* vh = head_ptr(p.v, p.s_v, bh, p.H);
 
-  // this wave's queries: B operands of S^T = K Q^T and dP^T = V dO^T
+  // this wave's queries: B operands of S^T = K Q^T and dP^T = V dO^T (lane
+  // l: query l%32, columns 16kc + 8half + 0..7; rows past Sq read 0)
   u32x4 qf[DK], of[DK];
+  float dl;  // D_i = rowsum(dO_i * O_i), fp32
   {
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(head_ptr(p.q, p.s_q, bh, p.H), rows_bytes(Sq, p.s_q.ss, D));
     const __amdgpu_buffer_rsrc_t orr = make_rsrc(head_ptr(p.dO, p.s_do, bh, p.H), rows_bytes(Sq, p.s_do.ss, D));
+    const __amdgpu_buffer_rsrc_t our = make_rsrc(head_ptr(p.o, p.s_o, bh, p.H), rows_bytes(Sq, p.s_o.ss, D));
     const uint32_t qoff = (uint32_t)(my_q * p.s_q.ss + 8 * half) * 2u;
     const uint32_t ooff = (uint32_t)(my_q * p.s_do.ss + 8 * half) * 2u;
+    const uint32_t uoff = (uint32_t)(my_q * p.s_o.ss + 8 * half) * 2u;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kc = 0; kc < DK; ++kc) {
       qf[kc] = load16(qr, qoff + 32 * kc);
       of[kc] = load16(orr, ooff + 32 * kc);
+      const u32x4 ov = load16(our, uoff + 32 * kc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = dot2<DT>(ov[e], of[kc][e], acc[e]);
     }
+    // this lane's half of the row, plus the other half's (lane l ^ 32)
+    dl = sum_halves((acc[0] + acc[1]) + (acc[2] + acc[3]));
   }
   const bool q_ok = my_q < Sq;
   const float nl = q_ok ? -p.lse[bh * Sq + my_q] * kLog2e : 0.f;
-  const float dl = q_ok ? p.delta[bh * Sq + my_q] : 0.f;
+  if (q_ok && half == 0) p.delta[bh * Sq + my_q] = dl;
   f32x16 dqa[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) dqa[db] = f32x16{};
@@ -543,66 +549,74 @@ void attn_bwd_dq(const BwdProblem p) {
     // score (key kv0 + 32kb + 8g + 4half + t, query my_q) kept iff key <= last
     const int lim = last - kv0 - 4 * half;
     // one 32-key block at a time, each MFMA run a pinned PIPE-deep operand
-    // pipeline (as in the dK/dV kernel)
+    // pipeline (as in the dK/dV kernel); the masking code only in the
+    // (uniform) branch of the tiles that need it
     constexpr int PIPE = 4;
     constexpr int N1 = 2 * DK;  // S^T and dP^T MFMAs, alternating
     constexpr int N3 = 2 * DB;  // dQ^T MFMAs
+    auto blocks = [&](auto masked) __attribute__((always_inline)) {
+      constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb) {
-      f32x16 sa = f32x16{}, dpa = f32x16{};
-      {
-        auto rd = [&](int t) __attribute__((always_inline)) -> u32x4 {
-          return *reinterpret_cast<const u32x4*>(((t & 1) ? vt : kt) + xrow + X::off(32 * kb) + 32 * (t >> 1));
-        };
-        u32x4 buf[PIPE];
+      for (int kb = 0; kb < NB; ++kb) {
+        f32x16 sa = f32x16{}, dpa = f32x16{};
+        {
+          auto rd = [&](int t) __attribute__((always_inline)) -> u32x4 {
+            return *reinterpret_cast<const u32x4*>(((t & 1) ? vt : kt) + xrow + X::off(32 * kb) + 32 * (t >> 1));
+          };
+          u32x4 buf[PIPE];
 #pragma unroll
-        for (int t = 0; t < PIPE; ++t) buf[t] = rd(t);
+          for (int t = 0; t < PIPE; ++t) buf[t] = rd(t);
 #pragma unroll
-        for (int t = 0; t < N1; ++t) {
-          const u32x4 a = buf[t % PIPE];
-          if (t + PIPE < N1) buf[t % PIPE] = rd(t + PIPE);
-          if (t & 1)
-            dpa = E::mfma(a, of[t >> 1], dpa);
-          else
-            sa = E::mfma(a, qf[t >> 1], sa);
+          for (int t = 0; t < N1; ++t) {
+            const u32x4 a = buf[t % PIPE];
+            if (t + PIPE < N1) buf[t % PIPE] = rd(t + PIPE);
+            if (t & 1)
+              dpa = E::mfma(a, of[t >> 1], dpa);
+            else
+              sa = E::mfma(a, qf[t >> 1], sa);
+          }
+          sched_prologue<0, N1, 0, PIPE>();
+          sched_steady<0, N1, 0, PIPE, 0, 1>();
         }
-        sched_prologue<0, N1, 0, PIPE>();
-        sched_steady<0, N1, 0, PIPE, 0, 1>();
-      }
-      float ds[16];
+        float ds[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[i], c, nl));
-        if (need_mask) pv = (32 * kb + 8 * (i >> 2) + (i & 3)) <= lim ? pv : 0.f;
-        ds[i] = pv * (dpa[i] - dl);
-      }
-      u32x4 sf[2];
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const int b = 8 * s2;
-        sf[s2] = u32x4{E::pack2(ds[b], ds[b + 1]), E::pack2(ds[b + 2], ds[b + 3]), E::pack2(ds[b + 4], ds[b + 5]),
-                       E::pack2(ds[b + 6], ds[b + 7])};
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      {
-        // op t: s2 = t / DB, db = t % DB
-        auto rd = [&](int t) __attribute__((always_inline)) -> u32x4 {
-          return tr_operand<X>(kt, trl, 2 * kb + t / DB, t % DB);
-        };
-        u32x4 buf[PIPE];
-#pragma unroll
-        for (int t = 0; t < PIPE; ++t) buf[t] = rd(t);
-#pragma unroll
-        for (int t = 0; t < N3; ++t) {
-          const u32x4 a = buf[t % PIPE];
-          if (t + PIPE < N3) buf[t % PIPE] = rd(t + PIPE);
-          dqa[t % DB] = E::mfma(a, sf[t / DB], dqa[t % DB]);
+        for (int i = 0; i < 16; ++i) {
+          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[i], c, nl));
+          if (MASKED && (D <= 128 || need_mask)) pv = (32 * kb + 8 * (i >> 2) + (i & 3)) <= lim ? pv : 0.f;
+          ds[i] = pv * (dpa[i] - dl);
         }
-        sched_prologue<0, N3, N3, PIPE>();
-        sched_steady<0, N3, N3, PIPE, 0, 1>();
+        u32x4 sf[2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const int b = 8 * s2;
+          sf[s2] = u32x4{E::pack2(ds[b], ds[b + 1]), E::pack2(ds[b + 2], ds[b + 3]), E::pack2(ds[b + 4], ds[b + 5]),
+                         E::pack2(ds[b + 6], ds[b + 7])};
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        {
+          // op t: s2 = t / DB, db = t % DB
+          auto rd = [&](int t) __attribute__((always_inline)) -> u32x4 {
+            return tr_operand<X>(kt, trl, 2 * kb + t / DB, t % DB);
+          };
+          u32x4 buf[PIPE];
+#pragma unroll
+          for (int t = 0; t < PIPE; ++t) buf[t] = rd(t);
+#pragma unroll
+          for (int t = 0; t < N3; ++t) {
+            const u32x4 a = buf[t % PIPE];
+            if (t + PIPE < N3) buf[t % PIPE] = rd(t + PIPE);
+            dqa[t % DB] = E::mfma(a, sf[t / DB], dqa[t % DB]);
+          }
+          sched_prologue<0, N3, N3, PIPE>();
+          sched_steady<0, N3, N3, PIPE, 0, 1>();
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    };
+    if (need_mask || D > 128)  // D = 256: one copy of the loop, masked at run time
+      blocks(std::true_type{});
+    else
+      blocks(std::false_type{});
   };
 
   if (n > 0) fetch(0, kt0, vt0);
