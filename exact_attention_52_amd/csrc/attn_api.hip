@@ -26,7 +26,8 @@
 namespace {
 
 // Per-head-dim tile shapes (TileCfg arguments: D, query waves, key waves,
-// keys per tile, ping-pong kernel, staggered copies, K/V LDS stages).
+// keys per tile, ping-pong kernel, staggered copies, K/V LDS stages,
+// producer wave, in-wave pipeline).
 //   D=64 : kernel 1, 4 query waves x 32 rows = 128 rows, 64-key tiles, two
 //          K/V stages: 35 KiB of LDS and 114 VGPRs, so four workgroups share
 //          a CU (four waves per SIMD).  Each one's copy waits, prologue and
@@ -35,13 +36,17 @@ namespace {
 //          and fill each other's MFMA and VALU gaps.
 //   D=128: ping-pong kernel, 8 waves = 256 rows, 128-key tiles, two stages,
 //          133 KiB LDS
-//   D=256: kernel 1 with staggered copies over two stages, 2 query waves =
-//          64 rows (the page's 64-row Q tile for D=256), each 64-key tile
-//          split over 2 key waves, 134.5 KiB LDS (with the key-split merge's
-//          row sums)
+//   D=256: grids of at least 512 128-row tiles (use_inwave_256): the
+//          in-wave pipelined kernel, 4 waves x 32 rows = 128 rows, 64-key
+//          tiles, two stages, 133 KiB LDS, one wave per SIMD; smaller grids:
+//          kernel 1 with staggered copies over two stages, 2 query waves = 64
+//          rows (the page's 64-row Q tile for D=256), each 64-key tile split
+//          over 2 key waves, 134.5 KiB LDS (with the key-split merge's row
+//          sums)
 using Cfg64 = attn::TileCfg<64, 4, 1, 64, false, false, 2>;
 using Cfg128 = attn::TileCfg<128, 8, 1, 128, true>;
-using Cfg256 = attn::TileCfg<256, 2, 2, 64, false, true>;
+using Cfg256 = attn::TileCfg<256, 4, 1, 64, false, false, 2, false, true>;
+using Cfg256Small = attn::TileCfg<256, 2, 2, 64, false, true>;
 
 template <class C>
 void fill_plan(int64_t B, int64_t H, int64_t S, attn_fwd_plan_t* p) {
@@ -60,7 +65,12 @@ int plan_for(int64_t B, int64_t H, int64_t S, int64_t D, attn_fwd_plan_t* p) {
   switch (D) {
     case 64: fill_plan<Cfg64>(B, H, S, p); break;
     case 128: fill_plan<Cfg128>(B, H, S, p); break;
-    default: fill_plan<Cfg256>(B, H, S, p); break;
+    default:
+      if (attn::use_inwave_256(B * H, S))
+        fill_plan<Cfg256>(B, H, S, p);
+      else
+        fill_plan<Cfg256Small>(B, H, S, p);
+      break;
   }
   if (p->num_workgroups > (int64_t)0x7FFFFFFF)
     return fail(ATTN_ERR_BAD_SHAPE, "grid of %lld workgroups exceeds the launch limit",
@@ -73,6 +83,9 @@ int launch(const attn::Problem& pr, hipStream_t stream) {
   if constexpr (C::PINGPONG)
     hipLaunchKernelGGL((attn::attn_fwd_pingpong_kernel<C, CAUSAL, DT>), dim3((unsigned)pr.G), dim3(C::NT), 0,
                        stream, pr);
+  else if constexpr (C::INWAVE)
+    hipLaunchKernelGGL((attn::attn_fwd_inwave_kernel<C, CAUSAL, DT>), dim3((unsigned)pr.G), dim3(C::NT), 0, stream,
+                       pr);
   else
     hipLaunchKernelGGL((attn::attn_fwd_kernel<C, CAUSAL, DT>), dim3((unsigned)pr.G), dim3(C::NT), 0, stream, pr);
   hipError_t e = hipGetLastError();
@@ -206,7 +219,9 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int64_
   switch (D) {
     case 64: return dispatch<Cfg64>(pr, cz, dtype, hs);
     case 128: return dispatch<Cfg128>(pr, cz, dtype, hs);
-    default: return dispatch<Cfg256>(pr, cz, dtype, hs);
+    default:
+      return plan.block_m == Cfg256::BM ? dispatch<Cfg256>(pr, cz, dtype, hs)
+                                        : dispatch<Cfg256Small>(pr, cz, dtype, hs);
   }
 }
 
@@ -361,10 +376,11 @@ int attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float
                      int64_t S, int64_t D, float scale, int causal, int dtype, int variant, void* stream) {
   const int st = check_sizes(B, H, S, D, dtype);
   if (st != ATTN_OK) return st;
-  if (variant < 0 || variant >= attn::kNumVariants || (variant > 0 && attn::variant_block_m((int)D, variant) == 0))
+  const int vbm = variant > 0 && variant < attn::kNumVariants ? attn::variant_block_m((int)D, variant, B * H, S) : 0;
+  if (variant < 0 || variant >= attn::kNumVariants || (variant > 0 && vbm == 0))
     return fail(ATTN_ERR_BAD_ARGUMENT, "variant %d not available for head_dim %lld (0..%d for D 64 and 128; 0, 5, 6 for 256)",
                 variant, (long long)D, attn::kNumVariants - 1);
-  if (variant > 0 && B * H * ((S + attn::variant_block_m((int)D, variant) - 1) / attn::variant_block_m((int)D, variant)) >
+  if (variant > 0 && B * H * ((S + vbm - 1) / vbm) >
                          0x7FFFFFFF)
     return fail(ATTN_ERR_BAD_SHAPE, "grid exceeds the launch limit");
   const int64_t sh = S * D, sb = H * S * D;

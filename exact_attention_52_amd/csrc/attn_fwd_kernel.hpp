@@ -39,6 +39,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 namespace attn {
 
@@ -108,9 +109,10 @@ struct Elem<DT_BF16> {
 //      consecutive rows of a transposing read, 64 bytes wide across two
 //      16-lane groups, sit 64 bytes apart modulo 256.
 template <int D_, int QW_, int KW_, int BN_, bool PINGPONG_ = false, bool STAGGER_ = false, int STAGES_ = 2,
-          bool PRODUCER_ = false>
+          bool PRODUCER_ = false, bool INWAVE_ = false>
 struct TileCfg {
   static constexpr bool PINGPONG = PINGPONG_;  // use the two-group ping-pong kernel
+  static constexpr bool INWAVE = INWAVE_;      // use the in-wave pipelined kernel (kernel 3)
   static constexpr bool STAGGER = STAGGER_;    // kernel 1: staggered K/V copies, two barriers per tile
   // kernel 1 without STAGGER: LDS stages of K/V (1, 2 or 3), and whether one
   // extra wave issues every HBM -> LDS copy while the others only compute
@@ -167,6 +169,7 @@ struct TileCfg {
   static_assert(STAGES >= 1 && STAGES <= 3, "1 to 3 K/V stages");
   static_assert(STAGES == 2 || (!PINGPONG && !STAGGER), "the ping-pong and staggered schedules use 2 stages");
   static_assert(!PRODUCER || (!PINGPONG && !STAGGER && KW == 1), "a producer wave only in kernel 1, KW = 1");
+  static_assert(!INWAVE || (!PINGPONG && !STAGGER && !PRODUCER && STAGES == 2), "the in-wave pipeline: two stages");
 };
 
 typedef short s16x4 __attribute__((vector_size(8)));
@@ -213,6 +216,25 @@ __device__ __forceinline__ float max_tree(const float* x) {
     if constexpr (N % 3 == 2) y[N / 3] = __builtin_elementwise_maximum(x[N - 2], x[N - 1]);
     return max_tree<M>(y);
   }
+}
+
+// f(std::integral_constant<int, I>{}) for I = 0 .. N-1, in order
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Keep the computation of x where it is written: the empty volatile asm uses
+// x, so the value must exist at this point (the compiler would otherwise sink
+// work whose results are only read later, e.g. P computed for the next
+// tile's MFMAs, out of the slot it was placed in).
+template <class T>
+__device__ __forceinline__ void pin(const T& x) {
+  __asm__ volatile("" ::"v"(x));
 }
 
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier
@@ -680,6 +702,152 @@ struct Wave {
     sched_steady<0, NOPS, NPV, PIPE, NL, LSTRIDE>();
   }
 
+  // ---- kernel 3 (in-wave pipeline): explicit score and P arrays ----
+  // MFMA slot block: qk (S^T = K Q^T over the tile in kt, into s) when QK,
+  // then pv (O^T += V^T P^T over the tile in vt, with pp) when PV, as one
+  // PIPE-deep operand pipeline.  After MFMA t come the reads of operand
+  // t+PIPE, then this slot's share of the NL copy instructions (spread evenly
+  // over the first LSLOTS slots) and of the NV VALU slices (over the first
+  // VSLOTS slots); each slot is fenced from the next, so the instructions
+  // stay in this order.  A wave issues in order: the VALU work placed between
+  // its MFMAs runs while they execute.
+  template <bool QK, bool PV, int NL, int LSLOTS, int NV, int VSLOTS, class COPY, class VALU, int PIPE = 4>
+  __device__ __forceinline__ void mfma_slots(const uint8_t* kt, const uint8_t* vt, f32x16 (&s)[NB],
+                                             const u32x4 (&pp)[2 * NB], const COPY& copy, const VALU& valu) {
+    constexpr int NQK = QK ? DK * NB : 0;
+    constexpr int NPV = PV ? 2 * NB * DB : 0;
+    constexpr int NOPS = NQK + NPV;
+    static_assert(LSLOTS >= 1 && LSLOTS <= NOPS && VSLOTS >= 1 && VSLOTS <= NOPS, "slots within the block");
+    auto load = [&](int t) __attribute__((always_inline)) -> u32x4 {
+      if (t < NQK) {
+        const int kc = t / NB, kb = t % NB;
+        return *reinterpret_cast<const u32x4*>(kt + k_lane + C::k_off(32 * kb) + 32 * kc);
+      }
+      const int t2 = t - NQK, ks = t2 / DB, db = t2 % DB;
+      const uint8_t* vp = vt + v_lane + 64 * db;
+      const u32x2 lo = lds_read_tr16(vp + C::v_off(16 * ks));
+      const u32x2 hi = lds_read_tr16(vp + C::v_off(16 * ks + 8));
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    u32x4 buf[PIPE];
+#pragma unroll
+    for (int t = 0; t < PIPE && t < NOPS; ++t) buf[t] = load(t);
+    // one instantiation per slot (the slices differ in kind, and a loop over
+    // all of them is too large for the unroller)
+    static_for<NOPS>([&](auto tc) __attribute__((always_inline)) {
+      constexpr int t = decltype(tc)::value;
+      const u32x4 a = buf[t % PIPE];
+      if constexpr (t < NQK) {
+        constexpr int kc = t / NB, kb = t % NB;
+        s[kb] = E::mfma(a, qf[kc], kc == 0 ? f32x16{} : s[kb]);
+      } else {
+        constexpr int t2 = t - NQK, ks = t2 / DB, db = t2 % DB;
+        oacc[db] = E::mfma(a, pp[ks], oacc[db]);
+      }
+      if constexpr (t + PIPE < NOPS) buf[t % PIPE] = load(t + PIPE);
+      if constexpr (t < LSLOTS) {
+        constexpr int l0 = t * NL / LSLOTS, l1 = (t + 1) * NL / LSLOTS;
+        static_for<l1 - l0>([&](auto ic) __attribute__((always_inline)) { copy(l0 + decltype(ic)::value); });
+      }
+      if constexpr (t < VSLOTS) {
+        constexpr int v0 = t * NV / VSLOTS, v1 = (t + 1) * NV / VSLOTS;
+        static_for<v1 - v0>([&](auto ic) __attribute__((always_inline)) {
+          valu(std::integral_constant<int, v0 + decltype(ic)::value>{});
+        });
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  }
+
+  // softmax of one tile (scores s -> packed P pp, as softmax() computes them)
+  // cut into NSLICES slices for mfma_slots: 0 masks, 1..NB take the row max
+  // over score block kb and then across the lane pair, NB+1 decides the
+  // rescale (O^T's own rescale is left to the caller: `pend` is set when
+  // alpha != 1 for some lane), then one slice per pair of scores computes
+  // and packs P with the pair's sum (a group of 8 scores completes its
+  // partial sum in its fourth slice), and the last adds the tile's sum.
+  struct SoftmaxState {
+    float mx;
+    float pe[8 * NB];  // pair sums
+    float ls[2 * NB];  // 8-score group sums
+  };
+  static constexpr int NSLICES = 8 * NB + NB + 3;
+  template <int sl>
+  __device__ __forceinline__ void softmax_slice(int j, f32x16 (&s)[NB], u32x4 (&pp)[2 * NB], SoftmaxState& st,
+                                                bool& pend) {
+    if constexpr (sl == 0) {
+      const int kv0 = j * BN + kbase;
+      const bool need_mask = (kv0 + C::KSUB > Skv) || (CAUSAL && kv0 + C::KSUB - 1 > wq_first + koff);
+      if (need_mask) {
+        const int last = CAUSAL ? (my_q + koff < Skv - 1 ? my_q + koff : Skv - 1) : Skv - 1;
+        const int lim = last - kv0 - 4 * half;
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int off = kb * 32 + 8 * (i >> 2) + (i & 3);
+            s[kb][i] = off > lim ? -__builtin_inff() : s[kb][i];
+          }
+      }
+    } else if constexpr (sl <= NB) {
+      constexpr int kb = sl - 1;
+      float sc[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[i] = s[kb][i];
+      const float m = max_tree<16>(sc);
+      if constexpr (kb == 0)
+        st.mx = m;
+      else
+        st.mx = __builtin_elementwise_maximum(st.mx, m);
+      if constexpr (kb == NB - 1) st.mx = max_halves(st.mx);
+      pin(st.mx);
+    } else if constexpr (sl == NB + 1) {
+      const float mt = st.mx * c;
+      alpha = 1.f;
+      pend = false;
+      if (__builtin_amdgcn_ballot_w64(mt > m_thr) != 0) {
+        const float m_new = __builtin_elementwise_maximum(m_run, mt);
+        const bool none = m_new == -__builtin_inff();
+        const float a = none ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        nm_ref = none ? 0.f : -m_new;
+        m_thr = m_new + (C::EXACT_MAX ? 0.f : kRescaleSlack);
+        l_run *= a;
+        p_top *= a;
+        e_top *= a;
+        alpha = a;
+        pend = true;
+      }
+    } else if constexpr (sl < NSLICES - 1) {
+      constexpr int q = sl - (NB + 2);  // pair 0 .. 8NB-1
+      constexpr int g = q / 4, pr = q % 4, kb = g / 2, s2 = g % 2;
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * s2 + 2 * pr], c, nm_ref));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * s2 + 2 * pr + 1], c, nm_ref));
+      pp[g][pr] = E::pack2(p0, p1);
+      st.pe[q] = p0 + p1;
+      pin(pp[g][pr]);
+      pin(st.pe[q]);
+      if constexpr (pr == 3) {
+        st.ls[g] = (st.pe[q - 3] + st.pe[q - 2]) + (st.pe[q - 1] + st.pe[q]);
+        pin(st.ls[g]);
+      }
+    } else {
+#pragma unroll
+      for (int w = 2 * NB; w > 1; w /= 2)
+#pragma unroll
+        for (int i = 0; i < w / 2; ++i) st.ls[i] += st.ls[i + w / 2];
+      l_run += st.ls[0];
+      pin(l_run);
+      if constexpr (!C::EXACT_MAX) {
+        const float pm = __builtin_amdgcn_exp2f(__builtin_fmaf(st.mx, c, nm_ref));
+        const float em = E::round(pm) - pm;
+        if (pm > p_top) p_top = pm, e_top = em;
+        pin(p_top);
+        pin(e_top);
+      }
+    }
+  }
+
   // O = O_acc / l (RNE to 16 bits), LSE = (m + log2 l) ln 2.
   // A row with no key (causal, Sq > Skv) has l = 0: O = 0 and LSE = -inf.
   // The accumulator layout gives each lane 8-byte pieces of its one row, so
@@ -813,6 +981,87 @@ __device__ __forceinline__ void wait_loads_but() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 0xF) | ((N & 0x30) << 10));
 }
 
+// The end of kernels 1 and 3, after each wave's last read of the K/V stages:
+// the key-split merge (KW > 1) and the output, staged through the stage
+// arrays (stage arrays of one-stage shapes are 16-byte stand-ins).
+template <class C, bool CAUSAL, int DT>
+__device__ __forceinline__ void finish_tile(Wave<C, CAUSAL, DT>& w, const HeadView& hv, int qw, int kw, int lane,
+                                            uint8_t* kt0, uint8_t* kt1, uint8_t* vt0, uint8_t* vt1) {
+  constexpr int D = C::D, DB = C::DB;
+  // Staged epilogue where the stage arrays hold a piece for every writing
+  // wave (with a key split, only the kw = 0 waves write, and their pieces
+  // must lie in the K arrays: with two or more stages the merge below reads
+  // partials from V stages only; with one it uses kt0 too).
+  using Areas = EpiAreas<Wave<C, CAUSAL, DT>::EPI_BYTES, C::K_TILE, C::STAGES >= 2 ? C::K_TILE : 16, C::V_TILE,
+                         C::STAGES >= 2 ? C::V_TILE : 16>;
+  constexpr bool STAGED = C::KW == 1 ? Areas::TOTAL >= C::NW
+                                     : (C::STAGES >= 2 && (C::KW - 1) * C::QW <= 2 && Areas::P0 + Areas::P1 >= C::QW);
+  wait_loads();  // the (empty) copies issued past the last tile
+  // the key-split merge and the staged epilogue reuse the stage arrays: every
+  // wave's copies must have landed before any wave writes there
+  if constexpr (C::KW > 1 || STAGED) __syncthreads();
+
+  // merge the key-split waves (KW > 1): the O partial of wave (kw, qw),
+  // kw > 0, goes to slot (kw - 1) * QW + qw of the stage arrays (vt0, vt1,
+  // kt0, kt1 with two or more stages; vt0, kt0 with one), its l, m, p_top
+  // and e_top to a small array of their own
+  if constexpr (C::KW > 1) {
+    constexpr int NSLOT = (C::KW - 1) * C::QW;
+    constexpr int SLOTS = C::STAGES >= 2 ? 4 : 2;
+    constexpr int OBYTES = D / 2 * 64 * 4;  // one wave's O partial
+    static_assert(NSLOT <= SLOTS && OBYTES <= C::V_TILE && (NSLOT <= SLOTS / 2 || OBYTES <= C::K_TILE),
+                  "merge area too small");
+    __shared__ float mscal[NSLOT][4][64];
+    auto slot = [&](int i) __attribute__((always_inline)) -> uint8_t* {
+      if constexpr (SLOTS == 2) return i == 0 ? vt0 : kt0;
+      return i == 0 ? vt0 : i == 1 ? vt1 : i == 2 ? kt0 : kt1;
+    };
+    if (kw > 0) {
+      const int sl = (kw - 1) * C::QW + qw;
+      float* dst = reinterpret_cast<float*>(slot(sl));
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dst[(db * 16 + i) * 64 + lane] = w.oacc[db][i];
+      mscal[sl][0][lane] = w.l_run;
+      mscal[sl][1][lane] = w.m_run;
+      mscal[sl][2][lane] = w.p_top;
+      mscal[sl][3][lane] = w.e_top;
+    }
+    __syncthreads();
+    if (kw > 0) return;
+#pragma unroll
+    for (int ww = 1; ww < C::KW; ++ww) {
+      const int sl = (ww - 1) * C::QW + qw;
+      const float* src = reinterpret_cast<const float*>(slot(sl));
+      const float lb = mscal[sl][0][lane];
+      const float mb = mscal[sl][1][lane];
+      const float pb = mscal[sl][2][lane];
+      const float eb = mscal[sl][3][lane];
+      const float mm = fmaxf(w.m_run, mb);
+      const float mref = (mm == -__builtin_inff()) ? 0.f : mm;
+      const float fa = __builtin_amdgcn_exp2f(w.m_run - mref);
+      const float fb = __builtin_amdgcn_exp2f(mb - mref);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          w.oacc[db][i] = w.oacc[db][i] * fa + src[(db * 16 + i) * 64 + lane] * fb;
+      w.l_run = w.l_run * fa + lb * fb;
+      // the larger of the two largest P, on the merged scale, with its error
+      const float pa = w.p_top * fa, pbs = pb * fb;
+      w.e_top = pa >= pbs ? w.e_top * fa : eb * fb;
+      w.p_top = pa >= pbs ? pa : pbs;
+      w.m_run = mm;
+    }
+  }
+
+  if constexpr (STAGED)
+    w.epilogue_staged(hv, Areas::pick(qw, kt0, kt1, vt0, vt1));
+  else
+    w.epilogue(hv);
+}
+
 // ---------------------------------------------------------------------------
 // Kernel 1: every wave runs qk, softmax, pv per tile.  Copy schedules:
 //   STAGGER (two LDS stages of K and of V): every copy gets about a tile and
@@ -831,7 +1080,7 @@ __device__ __forceinline__ void wait_loads_but() {
 // ---------------------------------------------------------------------------
 template <class C, bool CAUSAL, int DT>
 __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(const Problem p) {
-  constexpr int D = C::D, BN = C::BN, BM = C::BM, DB = C::DB;
+  constexpr int BN = C::BN, BM = C::BM, DB = C::DB;
   constexpr int LPW = C::LINES / C::NW;              // copy lines per wave per operand
   constexpr int NQK = C::DK * C::NB, NPV = 2 * C::NB * DB;  // MFMAs of qk, pv
   constexpr int LSQ = NQK / LPW, LSP = NPV / LPW;      // MFMAs per copy
@@ -1017,78 +1266,7 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(const Problem p) {
     wait_loads();
     return;
   }
-  // Staged epilogue where the stage arrays hold a piece for every writing
-  // wave (with a key split, only the kw = 0 waves write, and their pieces
-  // must lie in the K arrays: with two or more stages the merge below reads
-  // partials from V stages only; with one it uses kt0 too).
-  using Areas = EpiAreas<Wave<C, CAUSAL, DT>::EPI_BYTES, C::K_TILE, C::STAGES >= 2 ? C::K_TILE : 16, C::V_TILE,
-                         C::STAGES >= 2 ? C::V_TILE : 16>;
-  constexpr bool STAGED = C::KW == 1 ? Areas::TOTAL >= C::NW
-                                     : (C::STAGES >= 2 && (C::KW - 1) * C::QW <= 2 && Areas::P0 + Areas::P1 >= C::QW);
-  wait_loads();  // the (empty) copies issued past the last tile
-  // the key-split merge and the staged epilogue reuse the stage arrays: every
-  // wave's copies must have landed before any wave writes there
-  if constexpr (C::KW > 1 || STAGED) __syncthreads();
-
-  // merge the key-split waves (KW > 1): the O partial of wave (kw, qw),
-  // kw > 0, goes to slot (kw - 1) * QW + qw of the stage arrays (vt0, vt1,
-  // kt0, kt1 with two or more stages; vt0, kt0 with one), its l, m, p_top
-  // and e_top to a small array of their own
-  if constexpr (C::KW > 1) {
-    constexpr int NSLOT = (C::KW - 1) * C::QW;
-    constexpr int SLOTS = C::STAGES >= 2 ? 4 : 2;
-    constexpr int OBYTES = D / 2 * 64 * 4;  // one wave's O partial
-    static_assert(NSLOT <= SLOTS && OBYTES <= C::V_TILE && (NSLOT <= SLOTS / 2 || OBYTES <= C::K_TILE),
-                  "merge area too small");
-    __shared__ float mscal[NSLOT][4][64];
-    auto slot = [&](int i) __attribute__((always_inline)) -> uint8_t* {
-      if constexpr (SLOTS == 2) return i == 0 ? vt0 : kt0;
-      return i == 0 ? vt0 : i == 1 ? vt1 : i == 2 ? kt0 : kt1;
-    };
-    if (kw > 0) {
-      const int sl = (kw - 1) * C::QW + qw;
-      float* dst = reinterpret_cast<float*>(slot(sl));
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) dst[(db * 16 + i) * 64 + lane] = w.oacc[db][i];
-      mscal[sl][0][lane] = w.l_run;
-      mscal[sl][1][lane] = w.m_run;
-      mscal[sl][2][lane] = w.p_top;
-      mscal[sl][3][lane] = w.e_top;
-    }
-    __syncthreads();
-    if (kw > 0) return;
-#pragma unroll
-    for (int ww = 1; ww < C::KW; ++ww) {
-      const int sl = (ww - 1) * C::QW + qw;
-      const float* src = reinterpret_cast<const float*>(slot(sl));
-      const float lb = mscal[sl][0][lane];
-      const float mb = mscal[sl][1][lane];
-      const float pb = mscal[sl][2][lane];
-      const float eb = mscal[sl][3][lane];
-      const float mm = fmaxf(w.m_run, mb);
-      const float mref = (mm == -__builtin_inff()) ? 0.f : mm;
-      const float fa = __builtin_amdgcn_exp2f(w.m_run - mref);
-      const float fb = __builtin_amdgcn_exp2f(mb - mref);
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          w.oacc[db][i] = w.oacc[db][i] * fa + src[(db * 16 + i) * 64 + lane] * fb;
-      w.l_run = w.l_run * fa + lb * fb;
-      // the larger of the two largest P, on the merged scale, with its error
-      const float pa = w.p_top * fa, pbs = pb * fb;
-      w.e_top = pa >= pbs ? w.e_top * fa : eb * fb;
-      w.p_top = pa >= pbs ? pa : pbs;
-      w.m_run = mm;
-    }
-  }
-
-  if constexpr (STAGED)
-    w.epilogue_staged(hv, Areas::pick(qw, kt0, kt1, vt0, vt1));
-  else
-    w.epilogue(hv);
+  finish_tile(w, hv, qw, kw, lane, kt0, kt1, vt0, vt1);
 }
 
 // ---------------------------------------------------------------------------
@@ -1255,6 +1433,141 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_pingpong_kernel(const Problem 
   using Areas = EpiAreas<Wave<C, CAUSAL, DT>::EPI_BYTES, C::K_TILE, C::K_TILE, C::V_TILE, C::V_TILE>;
   static_assert(Areas::TOTAL >= 8, "the staged epilogue needs a piece per wave");
   w.epilogue_staged(hv, Areas::pick(wave, kt0, kt1, vt0, vt1));
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 3 (in-wave pipeline): one wave per SIMD, each wave alone with the
+// matrix core of its SIMD, so the overlap of MFMA and VALU work comes from
+// the wave's own instruction stream.  Iteration j of a wave issues
+//   MFMAs: qk(j+1) into the other score array, then pv(j-1)
+//   VALU:  softmax(j) (score array of tile j -> packed P of tile j), in
+//          slices placed between those MFMAs
+// and waits for its copies of K_{j+2} and V_j, then meets the other waves at
+// one barrier.  The rescale of O^T that softmax(j) may ask for runs at the
+// start of iteration j+1, before pv(j).  Tile t's K and V live in stage
+// t % 2; the copies of iteration j go to the stages that iteration j-1 was
+// the last to read.  Score and P arrays alternate between two named sets, so
+// the loop is unrolled by two.
+// ---------------------------------------------------------------------------
+// D = 256 shape choice: the in-wave kernel's 128-row query tiles where the
+// grid holds at least two rounds of them for a 256-CU part; smaller grids
+// take 64-row tiles (kernel 1, twice the workgroups).  Measured on MI355X:
+// the 128-row tiles are 12-15 % faster at 1x8x8192 causal and 1x16x4096,
+// but slower where they leave CUs idle or long causal tiles set the end
+// (1x16x2048 causal 61 against 51 us, 2x8x1024 31 against 25 us).
+constexpr int64_t kInwaveMinWorkgroups = 512;
+__host__ __device__ inline bool use_inwave_256(int64_t BH, int64_t S) {
+  return BH * ((S + 127) / 128) >= kInwaveMinWorkgroups;
+}
+
+// The copies of an iteration go out over its first quarter of MFMA slots
+// (each copy then has most of an iteration to land; issued later, they made
+// the iteration 3-4 % slower), the softmax slices over all of them (packed
+// into the first two thirds: 1-3 % slower).
+constexpr int kInwaveCopyDiv = 4;
+template <class C, bool CAUSAL, int DT>
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::D <= 128 ? 2 : 1)))
+void attn_fwd_inwave_kernel(const Problem p) {
+  static_assert(C::INWAVE && C::NW == 4, "the in-wave pipeline runs 4 waves, one per SIMD");
+  constexpr int BN = C::BN, BM = C::BM, NB = C::NB;
+  constexpr int LPW = C::LINES / C::NW;  // copy lines per wave per operand
+  using W = Wave<C, CAUSAL, DT>;
+
+  __shared__ __attribute__((aligned(1024))) uint8_t kt0[C::K_TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t kt1[C::K_TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vt0[C::V_TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vt1[C::V_TILE];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int qw = wave % C::QW, kw = wave / C::QW;
+
+  int64_t tile64, bh64;
+  workgroup_tile(blockIdx.x, p.G, p.nq, CAUSAL, p.hchunk, &tile64, &bh64);
+  const int q0 = (int)tile64 * BM;
+  const HeadView hv = head_view(p, bh64);
+
+  // Q through the V stages, which the loop's first copies only reach after
+  // the barrier that follows qk(0): the kw = 0 waves copy the rows of their
+  // query wave, every wave reads its fragment
+  constexpr int QPV = C::V_TILE / W::Q_BYTES;  // query waves' rows per V stage
+  static_assert(2 * QPV >= C::QW, "the Q rows must fit in the V stages");
+  W w;
+  w.template init<false>(hv, q0 + qw * 32, kw * C::KSUB, p.c);
+
+  const int q_end = (q0 + BM < hv.Sq) ? q0 + BM : hv.Sq;
+  const int kv_end = CAUSAL ? (q_end + hv.koff < 0 ? 0 : (q_end + hv.koff < hv.Skv ? q_end + hv.koff : hv.Skv))
+                            : hv.Skv;
+  const int n = (kv_end + BN - 1) / BN;
+  uint8_t* const q_area = (qw < QPV ? vt0 + qw * W::Q_BYTES : vt1 + (qw - QPV) * W::Q_BYTES);
+  if (n == 0) {  // uniform over the workgroup: no key for any row
+    if (kw == 0) w.epilogue(hv);
+    return;
+  }
+
+  TileCopier<C, true> kcp;
+  TileCopier<C, false> vcp;
+  kcp.init(hv.k, hv.k_ss, hv.Skv, lane);
+  vcp.init(hv.v, hv.v_ss, hv.Skv, lane);
+  {
+    const __amdgpu_buffer_rsrc_t r0 = kcp.tile(0, true), r1 = kcp.tile(BN, n > 1);
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) kcp.line(r0, kt0, wave * LPW + i), kcp.line(r1, kt1, wave * LPW + i);
+  }
+  if (kw == 0) w.copy_q(hv, q_area);
+  wait_loads();
+  __syncthreads();
+  w.read_q(q_area);
+
+  f32x16 s0[NB], s1[NB];
+  u32x4 p0[2 * NB], p1[2 * NB];
+  bool pend = false;
+  auto no_copy = [](int) {};
+  auto no_valu = [](auto) {};
+  // qk(0), alone; the barrier after it frees kt0 and the Q areas for copies
+  w.template mfma_slots<true, false, 0, 1, 0, 1>(kt0, vt0, s0, p1, no_copy, no_valu);
+  barrier_keep_loads();
+
+  auto iter = [&](auto pv, int j, f32x16(&s_cur)[NB], u32x4(&p_cur)[2 * NB], f32x16(&s_next)[NB],
+                  const u32x4(&p_prev)[2 * NB], const uint8_t* kt_qk, const uint8_t* vt_pv, uint8_t* kt_ld,
+                  uint8_t* vt_ld) __attribute__((always_inline)) {
+    constexpr bool PV = decltype(pv)::value;
+    if constexpr (PV) {
+      if (pend) w.rescale_o();  // softmax(j-1)'s rescale, before pv(j-1)
+    }
+    const __amdgpu_buffer_rsrc_t rk = kcp.tile((j + 2) * BN, j + 2 < n);
+    const __amdgpu_buffer_rsrc_t rv = vcp.tile(j * BN, true);
+    auto copy = [&](int i) __attribute__((always_inline)) {
+      if (i < LPW)
+        kcp.line(rk, kt_ld, wave * LPW + i);
+      else
+        vcp.line(rv, vt_ld, wave * LPW + i - LPW);
+    };
+    typename W::SoftmaxState st;
+    auto valu = [&](auto sl) __attribute__((always_inline)) {
+      w.template softmax_slice<decltype(sl)::value>(j, s_cur, p_cur, st, pend);
+    };
+    constexpr int NS = C::DK * NB + (PV ? 2 * NB * C::DB : 0);  // MFMA slots (the first iteration: qk only)
+    constexpr int LS = NS / kInwaveCopyDiv, VS = NS;
+    w.template mfma_slots<true, PV, 2 * LPW, LS, W::NSLICES, VS>(kt_qk, vt_pv, s_next, p_prev, copy, valu);
+    wait_loads();  // K_{j+2} and V_j landed
+    barrier_keep_loads();
+  };
+
+  using Y = std::true_type;
+  using N = std::false_type;
+  iter(N{}, 0, s0, p0, s1, p1, kt1, vt1, kt0, vt0);
+  for (int j = 1; j < n; j += 2) {
+    iter(Y{}, j, s1, p1, s0, p0, kt0, vt0, kt1, vt1);
+    if (j + 1 < n) iter(Y{}, j + 1, s0, p0, s1, p1, kt1, vt1, kt0, vt0);
+  }
+  // pv(n-1)
+  if (pend) w.rescale_o();
+  if ((n - 1) & 1)
+    w.template mfma_slots<false, true, 0, 1, 0, 1>(kt1, vt1, s0, p1, no_copy, no_valu);
+  else
+    w.template mfma_slots<false, true, 0, 1, 0, 1>(kt0, vt0, s0, p0, no_copy, no_valu);
+  finish_tile(w, hv, qw, kw, lane, kt0, kt1, vt0, vt1);
 }
 
 }  // namespace attn

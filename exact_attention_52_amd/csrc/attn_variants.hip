@@ -11,7 +11,8 @@
 //      while the other waves only compute
 //   5: the shipped tile shape of the head dim in kernel 1 with one stage
 //   6: the shipped tile shape of the head dim in kernel 1 with two stages and
-//      one barrier per tile (no ping-pong, no staggered copies)
+//      one barrier per tile (no ping-pong, no staggered copies, no in-wave
+//      pipeline)
 // Variants 1-4: D=64 uses the shipped D=64 shape (4 waves x 32 query rows,
 // 64-key tiles), so variant 2 is the shipped kernel itself; D=128 uses 4
 // computing waves and 64-key tiles, the largest D=128 shape for which three
@@ -42,7 +43,8 @@ struct Shipped<128, S> {
 };
 template <int S>
 struct Shipped<256, S> {
-  using C = TileCfg<256, 2, 2, 64, false, false, S>;
+  using C = TileCfg<256, 2, 2, 64, false, false, S>;    // grids below use_inwave_256
+  using Big = TileCfg<256, 4, 1, 64, false, false, S>;  // the in-wave kernel's shape
 };
 
 template <class C, bool CAUSAL, int DT>
@@ -74,18 +76,24 @@ hipError_t schedule(const Problem& p, bool causal, int dtype, int v, hipStream_t
 
 template <int D>
 hipError_t shipped_shape(const Problem& p, bool causal, int dtype, int v, hipStream_t st) {
+  if constexpr (D == 256) {
+    if (use_inwave_256(p.G, p.Sq)) {  // p.G holds B*H here
+      if (v == 5) return pick<typename Shipped<D, 1>::Big>(p, causal, dtype, st);
+      return pick<typename Shipped<D, 2>::Big>(p, causal, dtype, st);
+    }
+  }
   if (v == 5) return pick<typename Shipped<D, 1>::C>(p, causal, dtype, st);
   return pick<typename Shipped<D, 2>::C>(p, causal, dtype, st);
 }
 
 }  // namespace
 
-int variant_block_m(int D, int v) {
+int variant_block_m(int D, int v, int64_t BH, int64_t S) {
   if (v < 1 || v >= kNumVariants) return 0;
   if (v >= 5) {
     if (D == 64) return Shipped<64, 1>::C::BM;
     if (D == 128) return Shipped<128, 1>::C::BM;
-    if (D == 256) return Shipped<256, 1>::C::BM;
+    if (D == 256) return use_inwave_256(BH, S) ? Shipped<256, 1>::Big::BM : Shipped<256, 1>::C::BM;
     return 0;
   }
   if (D == 64) return V64<2, false>::BM;

@@ -15,7 +15,8 @@ constexpr int kNumVariants = 7;  // 0 is the shipped configuration
 // for an unsupported (v, D) or a grid over the launch limit.
 hipError_t variant_launch(Problem p, int D, bool causal, int dtype, int v, hipStream_t stream);
 
-// Query rows per workgroup of variant v at head dim D (0 if unsupported).
-int variant_block_m(int D, int v);
+// Query rows per workgroup of variant v at head dim D for BH heads of S
+// query rows (0 if unsupported).
+int variant_block_m(int D, int v, int64_t BH, int64_t S);
 
 }  // namespace attn

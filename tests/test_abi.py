@@ -99,7 +99,19 @@ def test_plan_rules(D, S):
     assert p["lds_bytes"] <= 160 * 1024
     assert p["kv_stages"] == 2
     if D == 256:
-        assert bm == 64  # the 64-row query tile of the D=256 workload
+        # 64-row query tiles (the page's D=256 tile), except where the grid of
+        # 128-row tiles fills the 256 CUs at least twice: the in-wave kernel
+        assert bm == (128 if 15 * -(-S // 128) >= 512 else 64)
+        assert p["waves_k"] == (1 if bm == 128 else 2)
+
+
+@pytest.mark.parametrize("B,H,S,bm", [(1, 8, 8192, 128), (1, 8, 8191, 128), (1, 8, 8064, 64), (1, 16, 4096, 128),
+                                      (1, 16, 2048, 64), (2, 8, 1024, 64), (4, 128, 128, 128), (1, 511, 128, 64)])
+def test_d256_shape_rule(B, H, S, bm):
+    # the boundary of the size rule: B*H*ceil(S/128) >= 512
+    p = ea.attn_fwd_plan(B, H, S, 256, True, 1)
+    assert p["block_m"] == bm, p
+    assert p["num_workgroups"] == B * H * -(-S // bm)
 
 
 def test_supported_and_rejected_head_dims_and_types():
