@@ -535,6 +535,11 @@ def main():
                             "tflops": round(fl / (t_us * 1e-6) / 1e12, 1),
                             "frac_of_peak": round(fl / (t_us * 1e-6) / 1e12 / PEAK_TFLOPS, 4)}
             outputs[name] = (shp, wds, *host(o_o, l_o))
+            if args.clock_ms > 0 and t_us >= 50.0:
+                # the steady clock of this workload's kernel, back to back
+                sc = float(np.float32(1.0 / math.sqrt(shp[3])))
+                others[name]["shader_clock"] = ClockSampler().during(
+                    fwd_launcher(ea, *dv, sc, shp[5], o_o, l_o, torch.cuda.current_stream(), 0), ms=args.clock_ms)
             del o_o, l_o
             if not args.no_backward:
                 _, ddo = make_do(shp)
