@@ -221,7 +221,8 @@ int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
  *   4  2 stages and one extra producer wave that issues every HBM -> LDS
  *      copy while the other waves only compute
  *   5  the shipped tile shape of the head dim, 1 stage, one wave step after
- *      another (no ping-pong of wave groups, no staggered copies)
+ *      another (no ping-pong of wave groups, no staggered copies, no in-wave
+ *      pipeline; at D = 256 the shape attn_fwd picks for these sizes)
  *   6  the shipped tile shape of the head dim, 2 stages, one barrier per tile
  * Variants 1-4 exist for D = 64 (the shipped 4-wave, 64-key tile shape, so
  * variant 2 is attn_fwd itself) and D = 128 (4 computing waves, 64-key
@@ -239,7 +240,9 @@ int attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float
  * attn_fwd_plan -- the launch geometry attn_fwd would use (host only, no HIP
  * call, no device needed).  Mirrors the page's launch_params: one workgroup
  * per (query tile, batch*head), num_q_tiles = ceil(S / block_m); the key
- * length changes the loop trip count, not the grid.
+ * length changes the loop trip count, not the grid.  block_m is 128 at D=64,
+ * 256 at D=128; at D=256 it is 128 where B*H*ceil(S/128) >= 512 (the
+ * in-wave pipelined kernel) and 64 otherwise.
  */
 typedef struct {
   int64_t block_m;               /* query rows per workgroup               */
