@@ -70,16 +70,42 @@ def min_bytes(B, H, S, D):
 FWD_SOURCES = ("attn_api.hip", "attn_fwd_kernel.hpp")
 
 
+def strip_comments(src):
+    """C/C++ source without its comments and blank lines (string and
+    character literals kept as they are), each line right-stripped."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            while i < n and src[i] != "\n":
+                i += 1
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    lines = (ln.rstrip() for ln in "".join(out).split("\n"))
+    return "\n".join(ln for ln in lines if ln)
+
+
 def kernel_source_hash():
-    """Hash of the forward kernel's sources: the committed HBM traffic figure
-    is used only while it matches (the backward and the comparator live in
-    other files and do not invalidate it)."""
+    """Hash of the forward kernel's sources, comments and blank lines left
+    out: the committed HBM traffic figure is used only while it matches (the
+    backward and the comparator live in other files and do not invalidate
+    it, and neither does a comment)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "exact_attention_52_amd", "csrc")
     for name in FWD_SOURCES:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + strip_comments(f.read()).encode())
     return h.hexdigest()[:16]
 
 

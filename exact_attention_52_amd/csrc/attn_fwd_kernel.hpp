@@ -1,4 +1,4 @@
-// attn_fwd_kernel.hpp -- gfx950 (CDNA4) kernel of the exact attention forward.
+// attn_fwd_kernel.hpp -- gfx950 (CDNA4) kernels of the exact attention forward.
 //
 // Computes, per (batch*head, query tile), O = softmax(scale * Q K^T, causal
 // mask) V and LSE with an online softmax: a running max m and running sum l
@@ -31,8 +31,14 @@
 //     disjoint banks.
 //   * exp2/log2 are the hardware v_exp_f32/v_log_f32 with the scale folded
 //     as c = scale*log2(e); P and O are rounded to nearest-even.
-//   * Causal: key tiles wholly after a wave's last query are skipped, and
-//     only tiles crossing the diagonal (or the ragged end) are masked.
+//   * Causal: key tiles wholly after a wave's last query are skipped (or, in
+//     the kernels that pipeline across waves or tiles, get P = 0), and only
+//     tiles crossing the diagonal (or the ragged end) are masked.
+//   * Three schedules of the same per-wave steps: kernel 1 (each wave runs
+//     qk, softmax, pv per tile; several workgroups per CU at D=64), kernel 2
+//     (D=128: two wave groups per SIMD alternate MFMA and softmax phases) and
+//     kernel 3 (D=256 on large grids: one wave per SIMD interleaves the next
+//     tile's qk and the previous tile's pv MFMAs with this tile's softmax).
 #pragma once
 
 #include <hip/hip_runtime.h>

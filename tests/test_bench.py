@@ -38,6 +38,14 @@ def test_traffic_is_used_only_for_the_profiled_kernel_source(tmp_path, monkeypat
     assert bench.read_traffic() == pytest.approx(123456.0)
 
 
+def test_source_hash_ignores_comments_only():
+    src = 'int a = 1; // note\n/* block\n comment */ const char* s = "x // y /* z */";\n\n  char q = \'"\';\n'
+    assert bench.strip_comments(src) == 'int a = 1;\n const char* s = "x // y /* z */";\n  char q = \'"\';'
+    assert bench.strip_comments("a/**/b") == "ab"
+    # code changes show: one character of code differs
+    assert bench.strip_comments("int a = 1;") != bench.strip_comments("int a = 2;")
+
+
 def test_backward_flop_convention():
     # five S x S x D GEMMs (2 flops per multiply-add), halved when causal; the
     # kernels execute seven (dQ recomputes S and dP)
