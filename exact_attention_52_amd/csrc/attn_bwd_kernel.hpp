@@ -350,7 +350,17 @@ void attn_bwd_dkdv(const BwdProblem p) {
     constexpr int N3 = 2 * 2 * DB;  // dV and dK MFMAs, alternating
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      f32x16 sa = f32x16{}, dpa = f32x16{};
+      // dP starts from -D_i of its rows (LDS holds them negated), so the
+      // MFMAs leave dP - D_i: one broadcast LDS read per register group gives
+      // the 4 rows of that group, in the accumulator's own register order
+      f32x16 sa = f32x16{}, dpa;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dl + 32 * mb + 8 * g + 4 * half);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) dpa[4 * g + t] = d4[t];
+      }
+      __builtin_amdgcn_sched_barrier(0);
       {
         auto rd = [&](int t) __attribute__((always_inline)) -> u32x4 {
           return *reinterpret_cast<const u32x4*>(((t & 1) ? ot : qt) + xrow + X::off(32 * mb) + 32 * (t >> 1));
@@ -373,18 +383,17 @@ void attn_bwd_dkdv(const BwdProblem p) {
       float pr[16], ds[16];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        // the 4 rows of this register group (one broadcast LDS read per
-        // half): exp2 offsets and D_i
+        // the exp2 offsets of the 4 rows of this register group (one
+        // broadcast LDS read per half)
         const int rr = 32 * mb + 8 * g + 4 * half;
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + rr);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dl + rr);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int i = 4 * g + t;
           float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[i], c, l4[t]));
           if (need_mask) pv = (32 * mb + 8 * g + t) >= lim ? pv : 0.f;
           pr[i] = pv;
-          ds[i] = pv * (dpa[i] - d4[t]);
+          ds[i] = pv * dpa[i];  // P * (dP - D_i)
         }
       }
       u32x4 pf[2], sf[2];
@@ -423,30 +432,33 @@ void attn_bwd_dkdv(const BwdProblem p) {
   };
 
   // fenced_sync, except that between the wait and the barrier each wave that
-  // copied LSE rows turns its rows, just landed, into the exp2 offsets
-  // -LSE * log2(e) in place (its own LDS accesses execute in order; the
-  // barrier's fence publishes them): one multiply per row instead of one
-  // per score.  The lane index is recomputed there by an opaque instruction
-  // pair: a lane offset hoisted out of the loop would stay live through the
-  // MFMA steps, which already take every register.
-  auto land = [&](float* ls_) __attribute__((always_inline)) {
+  // copied row values turns its rows, just landed, into what the step uses
+  // (its own LDS accesses execute in order; the barrier's fence publishes
+  // them): the exp2 offsets -LSE * log2(e), one multiply per row instead of
+  // one per score, and -D_i, the starting value of dP.  The lane index is
+  // recomputed there by an opaque instruction pair: a lane offset hoisted
+  // out of the loop would stay live through the MFMA steps, which already
+  // take every register.
+  auto land = [&](float* ls_, float* dl_) __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
     wait_loads();
     int ln;
     __asm__ volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
 #pragma unroll
-    for (int m = 0; m < LR / 64; ++m)
+    for (int m = 0; m < LR / 64; ++m) {
       if (wave == 2 * m) ls_[64 * m + ln] = -ls_[64 * m + ln] * kLog2e;
+      if (wave == 2 * m + 1) dl_[64 * m + ln] = -dl_[64 * m + ln];
+    }
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
   };
   if (n > 0) fetch(0, qt0, ot0, ls0, dl0);
   for (int s = 0; s < n; s += 2) {
-    land(ls0);
+    land(ls0, dl0);
     if (s + 1 < n) fetch(s + 1, qt1, ot1, ls1, dl1);
     step(s, qt0, ot0, ls0, dl0);
     if (s + 1 >= n) break;
-    land(ls1);
+    land(ls1, dl1);
     if (s + 2 < n) fetch(s + 2, qt0, ot0, ls0, dl0);
     step(s + 1, qt1, ot1, ls1, dl1);
   }
