@@ -21,7 +21,10 @@ per launch (gaps between launches included).  `launch_stats` gives the mean,
 median, min and max of a second pass with HIP events around every launch
 (events that add a few microseconds between launches, hence not in the
 timed region).  `shader_clock` is the GFX clock sampled while the
-headline kernel runs back to back right after the timed region.
+headline kernel runs back to back right after the timed region, with the
+socket power, the power cap and the share of that window the firmware
+throttled the clock for package power; the reference GEMM carries the same
+readings.
 
 The CPU leg runs after all GPU timing: the fp64 oracle, as it stands, over
 every row of every timed workload (`cpu_baseline` is its rate on the headline
@@ -238,9 +241,12 @@ def launch_stats(per_ms):
 
 
 class ClockSampler:
-    """The shader (GFX) clock of cuda:0 read through amdsmi (the library behind
-    amd-smi) from a sampling thread while kernels run back to back.  Reporting
-    only: any failure leaves the reading None with the reason."""
+    """The shader (GFX) clock and socket power of cuda:0 read through amdsmi
+    (the library behind amd-smi) from a sampling thread while kernels run back
+    to back, with the card's power cap and the share of the window the
+    firmware spent throttling the clock for package power (its PPT violation
+    counter).  Reporting only: any failure leaves a reading None with the
+    reason."""
 
     def __init__(self):
         self.handle, self.error, self.api = None, None, None
@@ -260,18 +266,37 @@ class ClockSampler:
         except Exception as e:  # noqa: BLE001 -- reporting only
             self.error = f"amdsmi unavailable: {e}"
 
-    def read_mhz(self):
-        """Mean of the per-XCD current GFX clocks (MHz), or the GFX clock."""
+    def read(self):
+        """(mean of the per-XCD current GFX clocks, or the GFX clock, in MHz;
+        current socket power in W or None)."""
         m = self.api.amdsmi_get_gpu_metrics_info(self.handle)
+        w = m.get("current_socket_power")
+        w = float(w) if isinstance(w, (int, float)) and 0 < w < 100000 else None
         clks = m.get("current_gfxclks")
         if isinstance(clks, (list, tuple)):
             vals = [float(c) for c in clks if isinstance(c, (int, float)) and 0 < c < 10000]
             if vals:
-                return sum(vals) / len(vals)
+                return sum(vals) / len(vals), w
         c = m.get("current_gfxclk")
         if isinstance(c, (int, float)) and 0 < c < 10000:
-            return float(c)
-        return float(self.api.amdsmi_get_clock_info(self.handle, self.api.AmdSmiClkType.GFX)["clk"])
+            return float(c), w
+        return float(self.api.amdsmi_get_clock_info(self.handle, self.api.AmdSmiClkType.GFX)["clk"]), w
+
+    def power_cap_w(self):
+        try:
+            cap = self.api.amdsmi_get_power_cap_info(self.handle).get("power_cap")
+            return round(float(cap) / 1e6, 1) if isinstance(cap, (int, float)) and cap > 0 else None
+        except Exception:  # noqa: BLE001 -- reporting only
+            return None
+
+    def ppt_counters(self):
+        """(PPT power-throttle accumulator, sample accumulator) or None."""
+        try:
+            v = self.api.amdsmi_get_violation_status(self.handle)
+            a, n = v.get("acc_ppt_pwr"), v.get("acc_counter")
+            return (a, n) if isinstance(a, int) and isinstance(n, int) else None
+        except Exception:  # noqa: BLE001 -- reporting only
+            return None
 
     def during(self, launch, ms=1500.0, skip_ms=500.0, period_s=0.005):
         """Runs launch() back to back for about `ms` of wall time (synchronised
@@ -283,14 +308,19 @@ class ClockSampler:
         import torch
         if self.handle is None:
             return {"mhz_median": None, "error": self.error}
-        samples, errs, stop = [], [], threading.Event()
+        samples, watts, errs, stop = [], [], [], threading.Event()
+        ppt = []
 
         def loop():
             while not stop.is_set():
                 try:
-                    mhz = self.read_mhz()
+                    mhz, w = self.read()
                     if (time.perf_counter() - t0) * 1e3 >= skip_ms:
+                        if not ppt:
+                            ppt.append(self.ppt_counters())
                         samples.append(mhz)
+                        if w is not None:
+                            watts.append(w)
                 except Exception as e:  # noqa: BLE001
                     errs.append(str(e))
                     return
@@ -304,17 +334,26 @@ class ClockSampler:
                 launch()
             n += 20
             torch.cuda.synchronize()
+        ppt_end = self.ppt_counters()
         stop.set()
         th.join()
         if not samples:
             return {"mhz_median": None, "error": errs[0] if errs else "no samples"}
         a = np.asarray(samples)
+        throttled = None
+        if ppt and ppt[0] is not None and ppt_end is not None and ppt_end[1] > ppt[0][1]:
+            throttled = round((ppt_end[0] - ppt[0][0]) / (ppt_end[1] - ppt[0][1]), 3)
         return {"mhz_median": round(float(np.median(a)), 1), "mhz_min": round(float(a.min()), 1),
                 "mhz_max": round(float(a.max()), 1), "samples": int(a.size), "launches": n,
                 "window_ms": round((time.perf_counter() - t0) * 1e3, 1),
-                "source": f"amdsmi gpu_metrics current_gfxclks (mean over the XCDs), sampled every "
-                          f"{period_s * 1e3:.0f} ms from {skip_ms:.0f} ms on while the kernel ran back to back "
-                          f"after the timed region"}
+                "socket_power_w_median": round(float(np.median(watts)), 1) if watts else None,
+                "power_cap_w": self.power_cap_w(),
+                "ppt_throttle_share": throttled,
+                "source": f"amdsmi gpu_metrics current_gfxclks (mean over the XCDs) and current_socket_power, "
+                          f"sampled every {period_s * 1e3:.0f} ms from {skip_ms:.0f} ms on while the kernel ran "
+                          f"back to back after the timed region; power_cap_w from the power-cap info; "
+                          f"ppt_throttle_share = growth of the PPT power-violation accumulator over the growth "
+                          f"of its sample counter in the same window"}
 
 
 def bwd_flops(B, H, S, D, causal, gemms=5):
@@ -397,11 +436,13 @@ def time_unfused(ea, shape, dev, steps, warmup):
     return t0.elapsed_time(t1) / steps, o, lse
 
 
-def reference_gemm(n, steps=50):
+def reference_gemm(n, steps=50, clock_ms=0.0):
     """Context for the MFMA roofline: a plain fp16 n x n x n torch.matmul (the vendor
     GEMM library) on random N(0,1) data, timed back to back like the attention launches.
     Random-data MFMA work runs the card at its power limit, so this is the dense-MFMA
-    rate the box actually sustains; it is not used for any figure of merit."""
+    rate the box actually sustains; it is not used for any figure of merit.  With
+    clock_ms > 0 the GEMM then runs back to back that long under the clock and power
+    sampler."""
     import torch
     g = torch.Generator(device="cuda:0").manual_seed(0)
     a = torch.randn(n, n, device="cuda:0", dtype=torch.float16, generator=g)
@@ -416,10 +457,13 @@ def reference_gemm(n, steps=50):
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
+    out = {"what": f"torch.matmul fp16 {n}x{n}x{n}, random N(0,1), {steps} back to back",
+           "us_per_call": round(ms * 1e3, 1), "tflops": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)}
+    if clock_ms > 0:
+        out["shader_clock"] = ClockSampler().during(lambda: torch.matmul(a, b, out=c), ms=clock_ms)
     del a, b, c
     torch.cuda.empty_cache()
-    return {"what": f"torch.matmul fp16 {n}x{n}x{n}, random N(0,1), {steps} back to back",
-            "us_per_call": round(ms * 1e3, 1), "tflops": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)}
+    return out
 
 
 def full_oracle(shape, words):
@@ -593,7 +637,7 @@ def main():
             del dv
             torch.cuda.empty_cache()
 
-    gemm = reference_gemm(args.ref_gemm) if args.ref_gemm > 0 and not args.no_others else None
+    gemm = reference_gemm(args.ref_gemm, clock_ms=args.clock_ms) if args.ref_gemm > 0 and not args.no_others else None
     if gemm:
         print(f"# reference gemm: {gemm}", file=sys.stderr, flush=True)
 
