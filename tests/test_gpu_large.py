@@ -1,7 +1,9 @@
 """Largest sizes: long sequences (one head near the 32-bit per-head offset
 range the kernels use), a grid of 2^18 heads, the backward at S = 2^17
-(2^16 for D = 256) and over 2^16 short heads, checked on outputs the oracle computes one by one (sampled query rows,
-sampled keys few queries see) and on identities that hold at any size.
+(2^16 for D = 256) and over 2^16 short heads, tensors past 4 GiB (forward
+and backward), checked on outputs the oracle computes one by one (sampled
+query rows, sampled keys few queries see, sampled heads) and on identities
+that hold at any size.
 
 Inputs here are seeded standard normals from numpy's PCG64 (not the Philox
 generator of the workloads: at 2^28 elements per tensor that would take
@@ -121,3 +123,44 @@ def test_backward_many_heads(ea, oracle_mod):
     for name, g, r in zip(("dq", "dk", "dv", "delta"), got, ref):
         g = g.float().cpu().numpy().astype(np.float64)
         assert np.abs(g - r).max() <= tol * max(1.0, np.abs(r).max()), name
+
+
+@pytest.mark.parametrize("D,dtype,causal", [(64, "fp16", True), (128, "fp16", False), (256, "bf16", True)])
+def test_tensors_past_4gib(ea, oracle_mod, D, dtype, causal):
+    # Every tensor larger than 2^32 bytes (heads of 256 rows, enough of them
+    # that the last ones start past 4 GiB): forward and backward, checked in
+    # full on sampled heads on both sides of the 4 GiB mark.  The inputs are
+    # seeded normals drawn on the device by torch (host generation of 2^31
+    # elements per tensor would take minutes); the sampled heads' words are
+    # copied back for the oracle.
+    import torch
+    S = 256
+    head_bytes = S * D * 2
+    H = (1 << 32) // head_bytes + 37
+    B = 1
+    print(f"past 4 GiB: B={B} H={H} S={S} D={D} {dtype} causal={causal}", flush=True)
+    tdt = torch.float16 if dtype == "fp16" else torch.bfloat16
+    g = torch.Generator(device="cuda:0").manual_seed(4321 + D)
+    q, k, v, do = (torch.randn((B, H, S, D), generator=g, device="cuda:0", dtype=tdt) for _ in range(4))
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    o, lse = ea.fwd(q, k, v, scale=scale, causal=causal)
+    dq, dk, dv, delta = ea.bwd(q, k, v, o, lse, do, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    first_past = (1 << 32) // head_bytes
+    heads = [0, first_past - 1, first_past, H // 2, H - 1]
+
+    def words_of(t):
+        return t[:, heads].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    qw, kw, vw, dow = (words_of(t) for t in (q, k, v, do))
+    o_ref, lse_ref = oracle_mod.attn_fwd(qw, kw, vw, dtype, scale, causal)
+    eo, el = errors(o_to_f64(o[:, heads]), lse[:, heads].cpu().numpy().astype(np.float64), o_ref, lse_ref)
+    assert eo <= TOL_O[dtype], f"max|dO| {eo:.3e}"
+    assert el <= TOL_LSE, f"max dLSE {el:.3e}"
+    ref = oracle_mod.attn_bwd(qw, kw, vw, dow, dtype, scale, causal)
+    tol = 4 * U[dtype]
+    for name, t, r in zip(("dq", "dk", "dv", "delta"), (dq, dk, dv, delta), ref):
+        x = t[:, heads].float().cpu().numpy().astype(np.float64)
+        assert np.abs(x - r).max() <= tol * max(1.0, np.abs(r).max()), name
+    del q, k, v, do, o, lse, dq, dk, dv, delta
+    torch.cuda.empty_cache()
