@@ -1349,6 +1349,17 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_pingpong_kernel(const Problem 
   kcp.init(hv.k, hv.k_ss, hv.Skv, lane);
   vcp.init(hv.v, hv.v_ss, hv.Skv, lane);
 
+  // With two stages the output leaves inside the last iteration (j = n,
+  // pv(n-1) only): group 0 stages its rows in the K arrays during Y_n, while
+  // group 1 runs its last pv, and group 1 stages its rows in the V array
+  // that holds no tile any more, right after that pv.  No K array is read or
+  // copied into after Y_{n-1}, and the free V array last held V_{n-2}.
+  constexpr bool EARLY_OUT = ST == 2;
+  using W = Wave<C, CAUSAL, DT>;
+  using KAreas = EpiAreas<W::EPI_BYTES, C::K_TILE, C::K_TILE, 0, 0>;
+  static_assert(!EARLY_OUT || (KAreas::TOTAL >= 4 && 4 * W::EPI_BYTES <= C::V_TILE),
+                "a group's output must fit the K arrays and one V array");
+
   // One iteration of this wave.  PV, QK select the halves of the MFMA block;
   // group 0 (COPIES) also copies the next tiles.  kt_j holds K_j, vt_prev
   // holds V_{j-1}; the copies of K_{j+ST-1} and V_{j+ST-2} go to kt_ld and
@@ -1386,6 +1397,19 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_pingpong_kernel(const Problem 
     }
     if (COPIES || !LAST) barrier_keep_loads();
   };
+  // the last iteration with two stages: pv(n-1) from vt_prev, then the
+  // output (vt_free is the V array without a tile)
+  auto last = [&](auto copies, const uint8_t* vt_prev, uint8_t* vt_free) __attribute__((always_inline)) {
+    if constexpr (kPingPongDeferRescale) w.rescale_o();
+    w.template mfma_ops<true, false>(vt_prev, kt0);
+    if constexpr (decltype(copies)::value) {
+      barrier_keep_loads();  // end of X_n
+      w.epilogue_staged(hv, KAreas::pick(wave, kt0, kt1, kt0, kt0));
+    } else {
+      w.epilogue_staged(hv, vt_free + (wave & 3) * W::EPI_BYTES);
+    }
+    barrier_keep_loads();  // end of Y_n
+  };
   auto loop = [&](auto copies) __attribute__((always_inline)) {
     using Y = std::true_type;
     using N = std::false_type;
@@ -1405,7 +1429,7 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_pingpong_kernel(const Problem 
         iter(copies, Y{}, Y{}, j, kt1, kt0, vt1, vt0);
         if (j + 1 < n) iter(copies, Y{}, Y{}, j + 1, kt0, kt1, vt0, vt1);
       }
-      iter(copies, Y{}, N{}, n, kt0, kt0, vt0, (n & 1) ? vt0 : vt1);
+      last(copies, (n & 1) ? vt0 : vt1, (n & 1) ? vt1 : vt0);
     }
   };
 
@@ -1435,10 +1459,12 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_pingpong_kernel(const Problem 
     loop(std::false_type{});
   }
 
-  // the loop's last barrier has passed: every wave is done with LDS
-  using Areas = EpiAreas<Wave<C, CAUSAL, DT>::EPI_BYTES, C::K_TILE, C::K_TILE, C::V_TILE, C::V_TILE>;
-  static_assert(Areas::TOTAL >= 8, "the staged epilogue needs a piece per wave");
-  w.epilogue_staged(hv, Areas::pick(wave, kt0, kt1, vt0, vt1));
+  if constexpr (!EARLY_OUT) {
+    // the loop's last barrier has passed: every wave is done with LDS
+    using Areas = EpiAreas<W::EPI_BYTES, C::K_TILE, C::K_TILE, C::V_TILE, C::V_TILE>;
+    static_assert(Areas::TOTAL >= 8, "the staged epilogue needs a piece per wave");
+    w.epilogue_staged(hv, Areas::pick(wave, kt0, kt1, vt0, vt1));
+  }
 }
 
 // ---------------------------------------------------------------------------
