@@ -7,7 +7,7 @@ seeded synthetic input of the headline workload, by default
 B=2, H=16, S=4096, D=128, fp16, non-causal, Q,K ~ 2 N(0,1), V ~ N(0,1).
 
 Defaults: 100 untimed warm-up launches, then 100 timed ones (about 25 ms
-each at c4): the clock settles only after a few dozen back-to-back launches
+each for the headline workload): the clock settles only after a few dozen back-to-back launches
 of a fresh process, and a shorter warm-up would average over that ramp.
 Every forward warm-up (the headline's and each other workload's) also lasts
 at least 30 ms of wall time, however short the launches; the JSON line
@@ -180,8 +180,8 @@ def time_workload(ea, shape, dev, steps, warmup, variant=0):
     on the kernel's stream: its mean is the average launch duration, gaps
     between launches included.  The per-launch durations come from a second
     pass of as many launches right after it, each between two events of its
-    own: those events put a few microseconds of gap between launches (at c4
-    the region with them took ~3 % longer per step), so they stay out of the
+    own: those events put a few microseconds of gap between launches (for the
+    headline workload the region with them took ~3 % longer per step), so they stay out of the
     timed region and serve only the per-call statistics."""
     import torch
     B, H, S, D, dtype, causal = shape
@@ -508,7 +508,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     # the card's clock ramps over a process's first few dozen launches
-    # (c4: ~340 us per launch for the first 20, ~265 for the next 20, a
+    # (headline workload: ~340 us per launch for the first 20, ~265 for the next 20, a
     # steady ~241 from about the 60th on), so the default warm-up covers it
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=HEADLINE)

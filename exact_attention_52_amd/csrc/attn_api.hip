@@ -366,8 +366,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   const int st = check_sizes(B, H, S, D, dtype);
   if (st != ATTN_OK) return st;
   const int64_t sh = S * D, sb = H * S * D;
-  const View c4 = {nullptr, sb, sh, D, S, "q"};
-  View vq = c4, vk = c4, vv = c4, vo = c4;
+  const View packed = {nullptr, sb, sh, D, S, "q"};
+  View vq = packed, vk = packed, vv = packed, vo = packed;
   vk.name = "k", vv.name = "v", vo.name = "o";
   return run(q, k, v, o, lse, B, H, S, S, D, vq, vk, vv, vo, scale, causal, dtype, stream);
 }
@@ -384,8 +384,8 @@ int attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float
                          0x7FFFFFFF)
     return fail(ATTN_ERR_BAD_SHAPE, "grid exceeds the launch limit");
   const int64_t sh = S * D, sb = H * S * D;
-  const View c4 = {nullptr, sb, sh, D, S, "q"};
-  View vq = c4, vk = c4, vv = c4, vo = c4;
+  const View packed = {nullptr, sb, sh, D, S, "q"};
+  View vq = packed, vk = packed, vv = packed, vo = packed;
   vk.name = "k", vv.name = "v", vo.name = "o";
   return run(q, k, v, o, lse, B, H, S, S, D, vq, vk, vv, vo, scale, causal, dtype, stream, variant);
 }
