@@ -213,7 +213,8 @@ __device__ __forceinline__ void store_rows(uint8_t* area, const f32x16 (&acc)[D 
     for (int i = 0; i < 32 / RPI; ++i) {
       const int r = i * RPI + rl;
       const u32x4 v = *reinterpret_cast<const u32x4*>(area + r * RS + 16 * cl);
-      if (row0 + r < rows) *reinterpret_cast<u32x4*>(head + (int64_t)(row0 + r) * ss + 8 * cl) = v;
+      // whole rows, written once: non-temporal, as the forward's output
+      if (row0 + r < rows) store_nt(v, reinterpret_cast<u32x4*>(head + (int64_t)(row0 + r) * ss + 8 * cl));
     }
     __asm__ volatile("" ::: "memory");
   }
