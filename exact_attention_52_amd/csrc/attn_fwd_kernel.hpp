@@ -747,6 +747,17 @@ struct Wave {
       const u32x2 hi = lds_read_tr16(vp + C::v_off(16 * ks + 8));
       return u32x4{lo[0], lo[1], hi[0], hi[1]};
     };
+    // The wave's registers do not hold O, Q, two score and two P arrays at
+    // once: the compiler parks some in AGPRs and, left alone, copies the Q
+    // fragment back to VGPRs (four v_accvgpr_read per MFMA pair, ~60 VALU
+    // instructions per iteration).  An MFMA reads its B operand from AGPRs
+    // as well, so Q is pinned there and read in place (bit-identical; B=1
+    // H=8 S=8192 D=256 causal 254.8 -> 246.7 us, B=1 H=16 S=4096 D=256
+    // 247.8 -> 241.8 us).
+    if constexpr (QK) {
+#pragma unroll
+      for (int kc = 0; kc < DK; ++kc) __asm__ volatile("" : "+a"(qf[kc]));
+    }
     u32x4 buf[PIPE];
 #pragma unroll
     for (int t = 0; t < PIPE && t < NOPS; ++t) buf[t] = load(t);
