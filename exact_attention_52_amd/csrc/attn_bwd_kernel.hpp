@@ -84,6 +84,19 @@ constexpr bool offsets_split() {
   return true;
 }
 
+// At D = 256 a wave's operands and accumulators exceed its 256 VGPRs: the
+// compiler parks some in AGPRs and, left alone, parks the B-operand
+// fragments (K/V rows in dK/dV, Q/dO rows in dQ) there and copies them back
+// before their MFMAs (311 moves per 128 MFMAs in dK/dV, 112 per 96 in dQ).
+// An MFMA reads its B operand from AGPRs as well, so the fragments are
+// pinned there and read in place (bit-identical; backward at B=1 H=8 S=8192
+// D=256 causal 929 -> 885 us, B=1 H=16 S=4096 D=256 885 -> 847 us).
+template <int N>
+__device__ __forceinline__ void pin_agprs(u32x4 (&a)[N], u32x4 (&b)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) __asm__ volatile("" : "+a"(a[i]), "+a"(b[i]));
+}
+
 // The first row of head bh (= b*H + h) of a tensor with strides s.
 template <class T>
 __device__ __forceinline__ T* head_ptr(T* base, const Strides& s, int64_t bh, int H) {
@@ -354,6 +367,7 @@ void attn_bwd_dkdv(const BwdProblem p) {
       // dP starts from -D_i of its rows (LDS holds them negated), so the
       // MFMAs leave dP - D_i: one broadcast LDS read per register group gives
       // the 4 rows of that group, in the accumulator's own register order
+      if constexpr (C::WAVES_PER_SIMD == 1) pin_agprs(kf, vf);
       f32x16 sa = f32x16{}, dpa;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -571,6 +585,7 @@ void attn_bwd_dq(const BwdProblem p) {
       constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb) {
+        if constexpr (C::WAVES_PER_SIMD == 1) pin_agprs(qf, of);
         f32x16 sa = f32x16{}, dpa = f32x16{};
         {
           auto rd = [&](int t) __attribute__((always_inline)) -> u32x4 {
