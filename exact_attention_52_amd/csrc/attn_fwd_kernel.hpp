@@ -1516,11 +1516,12 @@ __host__ __device__ inline bool use_inwave_256(int64_t BH, int64_t S) {
   return BH * ((S + 127) / 128) >= kInwaveMinWorkgroups;
 }
 
-// The copies of an iteration go out over its first quarter of MFMA slots
-// (each copy then has most of an iteration to land; issued later, they made
-// the iteration 3-4 % slower), the softmax slices over all of them (packed
+// The copies of an iteration go out over its first half of MFMA slots (each
+// copy then has over half an iteration to land; over all the slots the
+// iteration took 5 % longer, over the first eighth 4 %, over the first
+// quarter or third 0.2-1.3 %), the softmax slices over all of them (packed
 // into the first two thirds: 1-3 % slower).
-constexpr int kInwaveCopyDiv = 4;
+constexpr int kInwaveCopyDiv = 2;
 template <class C, bool CAUSAL, int DT>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::D <= 128 ? 2 : 1)))
 void attn_fwd_inwave_kernel(const Problem p) {
