@@ -91,6 +91,11 @@ constexpr bool offsets_split() {
 // An MFMA reads its B operand from AGPRs as well, so the fragments are
 // pinned there and read in place (bit-identical; backward at B=1 H=8 S=8192
 // D=256 causal 929 -> 885 us, B=1 H=16 S=4096 D=256 885 -> 847 us).
+// An empty side effect: it keeps a small uniform branch (the mask selects of
+// the tiles that need them) a branch, where the compiler would otherwise turn
+// it into selects that run on every tile.
+__device__ __forceinline__ void keep_branch() { __asm__ volatile(""); }
+
 template <int N>
 __device__ __forceinline__ void pin_agprs(u32x4 (&a)[N], u32x4 (&b)[N]) {
 #pragma unroll
@@ -396,19 +401,42 @@ void attn_bwd_dkdv(const BwdProblem p) {
         sched_steady<0, N1, 0, PIPE, 0, 1>();
       }
       float pr[16], ds[16];
+      // the exp2 offsets of the 4 rows of register group g (one broadcast LDS
+      // read per half)
+      auto offs = [&](int g) __attribute__((always_inline)) {
+        return *reinterpret_cast<const f32x4*>(ls + 32 * mb + 8 * g + 4 * half);
+      };
+      if constexpr (C::WAVES_PER_SIMD == 2) {
+        // the mask selects in a uniform branch of their own (folded into the
+        // exp2 loop, they ran on every tile: the compiler merged the tile's
+        // need_mask into each select)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        // the exp2 offsets of the 4 rows of this register group (one
-        // broadcast LDS read per half)
-        const int rr = 32 * mb + 8 * g + 4 * half;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + rr);
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 l4 = offs(g);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int i = 4 * g + t;
-          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[i], c, l4[t]));
-          if (need_mask) pv = (32 * mb + 8 * g + t) >= lim ? pv : 0.f;
-          pr[i] = pv;
-          ds[i] = pv * dpa[i];  // P * (dP - D_i)
+          for (int t = 0; t < 4; ++t) pr[4 * g + t] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[4 * g + t], c, l4[t]));
+        }
+        if (need_mask) {
+          keep_branch();
+#pragma unroll
+          for (int i = 0; i < 16; ++i) pr[i] = (32 * mb + 8 * (i >> 2) + (i & 3)) >= lim ? pr[i] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ds[i] = pr[i] * dpa[i];  // P * (dP - D_i)
+      } else {
+        // D = 256: the select folded in (the form that keeps the operand
+        // fragments in place, see pin_agprs; the split form moved them)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 l4 = offs(g);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int i = 4 * g + t;
+            float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[i], c, l4[t]));
+            if (need_mask) pv = (32 * mb + 8 * g + t) >= lim ? pv : 0.f;
+            pr[i] = pv;
+            ds[i] = pv * dpa[i];  // P * (dP - D_i)
+          }
         }
       }
       u32x4 pf[2], sf[2];
@@ -581,8 +609,7 @@ void attn_bwd_dq(const BwdProblem p) {
     constexpr int PIPE = 4;
     constexpr int N1 = 2 * DK;  // S^T and dP^T MFMAs, alternating
     constexpr int N3 = 2 * DB;  // dQ^T MFMAs
-    auto blocks = [&](auto masked) __attribute__((always_inline)) {
-      constexpr bool MASKED = decltype(masked)::value;
+    auto blocks = [&]() __attribute__((always_inline)) {
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb) {
         if constexpr (C::WAVES_PER_SIMD == 1) pin_agprs(qf, of);
@@ -606,13 +633,20 @@ void attn_bwd_dq(const BwdProblem p) {
           sched_prologue<0, N1, 0, PIPE>();
           sched_steady<0, N1, 0, PIPE, 0, 1>();
         }
-        float ds[16];
+        // the mask selects run in a uniform branch of their own: with two
+        // copies of the whole block (masked and not) the compiler gave the
+        // dQ^T accumulators different registers in each and copied all of
+        // them at every step (64 moves at D=128)
+        float pv[16], ds[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[i], c, nl));
-          if (MASKED && (D <= 128 || need_mask)) pv = (32 * kb + 8 * (i >> 2) + (i & 3)) <= lim ? pv : 0.f;
-          ds[i] = pv * (dpa[i] - dl);
+        for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[i], c, nl));
+        if (need_mask) {
+          keep_branch();
+#pragma unroll
+          for (int i = 0; i < 16; ++i) pv[i] = (32 * kb + 8 * (i >> 2) + (i & 3)) <= lim ? pv[i] : 0.f;
         }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ds[i] = pv[i] * (dpa[i] - dl);
         u32x4 sf[2];
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
@@ -641,10 +675,7 @@ void attn_bwd_dq(const BwdProblem p) {
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    if (need_mask || D > 128)  // D = 256: one copy of the loop, masked at run time
-      blocks(std::true_type{});
-    else
-      blocks(std::false_type{});
+    blocks();
   };
 
   if (n > 0) fetch(0, kt0, vt0);
