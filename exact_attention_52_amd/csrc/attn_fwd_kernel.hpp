@@ -1318,7 +1318,8 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(const Problem p) {
 // Y_j it waits for the copies that X_{j+1} reads (three stages: those of the
 // previous iteration; two: those of this one).  Copies past the last tile
 // read through an empty buffer descriptor: they fetch nothing and fill a
-// stage no later phase reads.
+// stage no later phase reads.  With two stages each group writes its output
+// inside the last iteration, right after its last pv (group 0 during Y_n).
 // ---------------------------------------------------------------------------
 // MFMAs between two copy instructions in group 0's MFMA block
 constexpr int kPingPongCopyStride = 3;
