@@ -73,7 +73,7 @@ def min_bytes(B, H, S, D):
 
 
 # the sources that define the forward kernel and its launch configuration
-FWD_SOURCES = ("attn_api.hip", "attn_fwd_kernel.hpp")
+FWD_SOURCES = ("attn_api.hip", "attn_fwd_kernel.hpp", "attn_grid.hpp")
 
 
 def strip_comments(src):

@@ -23,7 +23,7 @@ def _c(name):
 # libattn.so: the fused forward, its schedule variants and the backward.
 SOURCES = [_c("attn_api.hip"), _c("attn_bwd.hip"), _c("attn_variants.hip")]
 HEADERS = [_c("attn_fwd_kernel.hpp"), _c("attn_bwd_kernel.hpp"), _c("attn_bwd.hpp"), _c("attn_variants.hpp"),
-           _c("attn_common.hpp"), os.path.join(INCLUDE, "attn.h")]
+           _c("attn_grid.hpp"), _c("attn_common.hpp"), os.path.join(INCLUDE, "attn.h")]
 # libattn_unfused.so: the unfused comparator, the only code that uses the
 # vendor BLAS, in a library of its own.
 UNFUSED_SOURCES = [_c("attn_unfused.hip")]

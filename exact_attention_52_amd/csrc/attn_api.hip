@@ -210,6 +210,8 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int64_
   pr.qsign = scale < 0.f ? 0x80008000u : 0u;
   hipStream_t hs = (hipStream_t)stream;
   const bool cz = causal != 0;
+  pr.map = attn::make_tile_map(pr.G, pr.nq, cz, pr.hchunk);
+  pr.dH = attn::make_div31((uint32_t)H);
   if (variant != 0) {
     pr.G = B * H;  // the variant sets its own tile count and grid from B*H
     const hipError_t e = attn::variant_launch(pr, (int)D, cz, dtype, variant, hs);
@@ -346,6 +348,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   // the dQ kernel streams K and V of its head, the dK/dV kernel Q and dO
   p.hchunk_q = attn::causal_head_chunk(Skv, D);
   p.hchunk_k = attn::causal_head_chunk(Sq, D);
+  p.dH = attn::make_div31((uint32_t)H);
   // the backward masks P itself (never a score), so c may take any sign;
   // a tiny positive c is kept >= FLT_MIN as in the forward
   float c = (float)((double)scale * 1.4426950408889634074);
@@ -454,7 +457,14 @@ int attn_fwd_workgroup_tile(int64_t B, int64_t H, int64_t S, int64_t D, int caus
   if (wg < 0 || wg >= p.num_workgroups)
     return fail(ATTN_ERR_BAD_ARGUMENT, "workgroup %lld outside [0, %lld)", (long long)wg,
                 (long long)p.num_workgroups);
-  attn::workgroup_tile(wg, p.num_workgroups, p.num_q_tiles, causal != 0, attn::causal_head_chunk(S, D), q_tile, bh);
+  const attn::TileMap m = attn::make_tile_map(p.num_workgroups, p.num_q_tiles, causal != 0, attn::causal_head_chunk(S, D));
+  uint32_t t = 0, b = 0;
+  if (causal)
+    attn::workgroup_tile<true>(m, (uint32_t)wg, &t, &b);
+  else
+    attn::workgroup_tile<false>(m, (uint32_t)wg, &t, &b);
+  *q_tile = t;
+  *bh = b;
   return ok();
 }
 

@@ -36,6 +36,8 @@ hipError_t dispatch(BwdProblem p, bool causal, int dtype, hipStream_t st) {
   using C = bwd::BwdCfg<D>;
   p.nq = (p.Sq + C::BM - 1) / C::BM;
   p.nk = (p.Skv + C::BN - 1) / C::BN;
+  p.map_q = make_tile_map(p.BH * p.nq, p.nq, causal, p.hchunk_q);
+  p.map_k = make_tile_map(p.BH * p.nk, p.nk, causal, p.hchunk_k);
   if (dtype == DT_F16)
     return causal ? launch<D, true, DT_F16>(p, st) : launch<D, false, DT_F16>(p, st);
   return causal ? launch<D, true, DT_BF16>(p, st) : launch<D, false, DT_BF16>(p, st);

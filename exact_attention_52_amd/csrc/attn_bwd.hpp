@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "attn_grid.hpp"
+
 namespace attn {
 
 // Batch, head and row strides (elements) of one [B,H,rows,D] tensor whose
@@ -34,6 +36,8 @@ struct BwdProblem {
   int nq, nk;  // query tiles per head (dQ kernel), key tiles per head (dK/dV kernel)
   int64_t BH;  // B * H
   int64_t hchunk_q, hchunk_k;  // heads per chunk of the causal orders (dQ, dK/dV kernels)
+  TileMap map_q, map_k;        // workgroup -> (tile, b*H + h) of the dQ and dK/dV kernels
+  Div31 dH;                    // division by H
   float c;     // scale * log2(e), kept >= FLT_MIN
   float scale;
 };
@@ -50,8 +54,8 @@ struct BwdPlan {
 
 BwdPlan bwd_plan(int D);
 
-// Enqueue the dQ (and D_i) and dK/dV kernels on `stream` (p.nq, p.nk are filled
-// in here).  D is 64, 128 or 256; the caller has validated everything.
+// Enqueue the dQ (and D_i) and dK/dV kernels on `stream` (p.nq, p.nk and the
+// tile maps are filled in here).  D is 64, 128 or 256; the caller has validated everything.
 hipError_t bwd_launch(BwdProblem p, int D, bool causal, int dtype, hipStream_t stream);
 
 }  // namespace attn

@@ -104,8 +104,9 @@ __device__ __forceinline__ void pin_agprs(u32x4 (&a)[N], u32x4 (&b)[N]) {
 
 // The first row of head bh (= b*H + h) of a tensor with strides s.
 template <class T>
-__device__ __forceinline__ T* head_ptr(T* base, const Strides& s, int64_t bh, int H) {
-  return base + (bh / H) * s.sb + (bh % H) * s.sh;
+__device__ __forceinline__ T* head_ptr(T* base, const Strides& s, uint32_t bh, int H, Div31 dH) {
+  const uint32_t b = div31(bh, dH);
+  return base + (int64_t)b * s.sb + (int64_t)(bh - b * (uint32_t)H) * s.sh;
 }
 
 // HBM -> LDS copies of XTile tiles of one head (rows of D elements, ss
@@ -289,15 +290,16 @@ void attn_bwd_dkdv(const BwdProblem p) {
   // key tiles in order of decreasing cost when causal (key tile 0 is seen by
   // the most queries), in chunks of heads per XCD as the forward's query
   // tiles; otherwise contiguous runs per XCD as in the forward
-  int64_t kt64, bh;
-  workgroup_tile(blockIdx.x, p.BH * p.nk, p.nk, CAUSAL, p.hchunk_k, &kt64, &bh);
-  if (CAUSAL) kt64 = p.nk - 1 - kt64;
+  uint32_t kt, bh32;
+  workgroup_tile<CAUSAL>(p.map_k, blockIdx.x, &kt, &bh32);
+  const int64_t bh = bh32;
+  if (CAUSAL) kt = (uint32_t)p.nk - 1 - kt;
   const int Sq = p.Sq, Skv = p.Skv, koff = Skv - Sq;
-  const int k0 = (int)kt64 * BN, kbase = k0 + 32 * wave, my_k = kbase + col;
-  const uint16_t* qh = head_ptr(p.q, p.s_q, bh, p.H);
-  const uint16_t* doh = head_ptr(p.dO, p.s_do, bh, p.H);
-  const uint16_t* kh = head_ptr(p.k, p.s_k, bh, p.H);
-  const uint16_t* vh = head_ptr(p.v, p.s_v, bh, p.H);
+  const int k0 = (int)kt * BN, kbase = k0 + 32 * wave, my_k = kbase + col;
+  const uint16_t* qh = head_ptr(p.q, p.s_q, bh32, p.H, p.dH);
+  const uint16_t* doh = head_ptr(p.dO, p.s_do, bh32, p.H, p.dH);
+  const uint16_t* kh = head_ptr(p.k, p.s_k, bh32, p.H, p.dH);
+  const uint16_t* vh = head_ptr(p.v, p.s_v, bh32, p.H, p.dH);
   const float* lseh = p.lse + bh * Sq;
   const float* delh = p.delta + bh * Sq;
   const __amdgpu_buffer_rsrc_t lse_r = make_rsrc(lseh, (uint32_t)Sq * 4u);
@@ -513,8 +515,8 @@ void attn_bwd_dkdv(const BwdProblem p) {
   constexpr bool STAGED = 32 * (2 * D + 16) <= X::BYTES && !(CAUSAL && D == 128);
   if constexpr (STAGED) __syncthreads();
   uint8_t* const area = wave == 0 ? qt0 : wave == 1 ? qt1 : wave == 2 ? ot0 : ot1;
-  store_rows<D, DT, STAGED>(area, dka, p.scale, head_ptr(p.dk, p.s_dk, bh, p.H), p.s_dk.ss, kbase, Skv, lane);
-  store_rows<D, DT, STAGED>(area, dva, 1.f, head_ptr(p.dv, p.s_dv, bh, p.H), p.s_dv.ss, kbase, Skv, lane);
+  store_rows<D, DT, STAGED>(area, dka, p.scale, head_ptr(p.dk, p.s_dk, bh32, p.H, p.dH), p.s_dk.ss, kbase, Skv, lane);
+  store_rows<D, DT, STAGED>(area, dva, 1.f, head_ptr(p.dv, p.s_dv, bh32, p.H, p.dH), p.s_dv.ss, kbase, Skv, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -538,21 +540,22 @@ void attn_bwd_dq(const BwdProblem p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 31, half = lane >> 5;
 
-  int64_t tile64, bh;
-  workgroup_tile(blockIdx.x, p.BH * p.nq, p.nq, CAUSAL, p.hchunk_q, &tile64, &bh);
+  uint32_t tile, bh32;
+  workgroup_tile<CAUSAL>(p.map_q, blockIdx.x, &tile, &bh32);
+  const int64_t bh = bh32;
   const int Sq = p.Sq, Skv = p.Skv, koff = Skv - Sq;
-  const int q0 = (int)tile64 * BM, wq_first = q0 + 32 * wave, my_q = wq_first + col;
-  const uint16_t* kh = head_ptr(p.k, p.s_k, bh, p.H);
-  const uint16_t* vh = head_ptr(p.v, p.s_v, bh, p.H);
+  const int q0 = (int)tile * BM, wq_first = q0 + 32 * wave, my_q = wq_first + col;
+  const uint16_t* kh = head_ptr(p.k, p.s_k, bh32, p.H, p.dH);
+  const uint16_t* vh = head_ptr(p.v, p.s_v, bh32, p.H, p.dH);
 
   // this wave's queries: B operands of S^T = K Q^T and dP^T = V dO^T (lane
   // l: query l%32, columns 16kc + 8half + 0..7; rows past Sq read 0)
   u32x4 qf[DK], of[DK];
   float dl;  // D_i = rowsum(dO_i * O_i), fp32
   {
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(head_ptr(p.q, p.s_q, bh, p.H), rows_bytes(Sq, p.s_q.ss, D));
-    const __amdgpu_buffer_rsrc_t orr = make_rsrc(head_ptr(p.dO, p.s_do, bh, p.H), rows_bytes(Sq, p.s_do.ss, D));
-    const __amdgpu_buffer_rsrc_t our = make_rsrc(head_ptr(p.o, p.s_o, bh, p.H), rows_bytes(Sq, p.s_o.ss, D));
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(head_ptr(p.q, p.s_q, bh32, p.H, p.dH), rows_bytes(Sq, p.s_q.ss, D));
+    const __amdgpu_buffer_rsrc_t orr = make_rsrc(head_ptr(p.dO, p.s_do, bh32, p.H, p.dH), rows_bytes(Sq, p.s_do.ss, D));
+    const __amdgpu_buffer_rsrc_t our = make_rsrc(head_ptr(p.o, p.s_o, bh32, p.H, p.dH), rows_bytes(Sq, p.s_o.ss, D));
     const uint32_t qoff = (uint32_t)(my_q * p.s_q.ss + 8 * half) * 2u;
     const uint32_t ooff = (uint32_t)(my_q * p.s_do.ss + 8 * half) * 2u;
     const uint32_t uoff = (uint32_t)(my_q * p.s_o.ss + 8 * half) * 2u;
@@ -693,7 +696,7 @@ void attn_bwd_dq(const BwdProblem p) {
   constexpr bool STAGED = 32 * (2 * D + 16) <= X::BYTES;
   if constexpr (STAGED) __syncthreads();
   uint8_t* const area = wave == 0 ? kt0 : wave == 1 ? kt1 : wave == 2 ? vt0 : vt1;
-  store_rows<D, DT, STAGED>(area, dqa, p.scale, head_ptr(p.dq, p.s_dq, bh, p.H), p.s_dq.ss, wq_first, Sq, lane);
+  store_rows<D, DT, STAGED>(area, dqa, p.scale, head_ptr(p.dq, p.s_dq, bh32, p.H, p.dH), p.s_dq.ss, wq_first, Sq, lane);
 }
 
 }  // namespace bwd

@@ -47,6 +47,8 @@
 #include <type_traits>
 #include <utility>
 
+#include "attn_grid.hpp"
+
 namespace attn {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -327,60 +329,6 @@ __device__ __forceinline__ void load16_lds(__amdgpu_buffer_rsrc_t r, uint8_t* ld
 // relative precision.
 constexpr float kRescaleSlack = 8.0f;
 
-// Workgroup id -> (query tile, b*H + h).  Workgroups are handed to the 8 XCDs
-// round-robin in id order, so id g runs on XCD g % 8, and each XCD gives its
-// next workgroup to the first CU that frees up.
-//   Causal: tile costs differ (query tile t has t+1 tiles' worth of keys), so
-//   each XCD runs its tiles longest first (list scheduling in
-//   longest-processing-time order pairs long and short tiles on each CU).
-//   When heads is a multiple of 8, head h runs on XCD h % 8, and each XCD
-//   works through its heads `hchunk` at a time: all tiles of a chunk of heads
-//   in order of decreasing cost, then the next chunk.  The K/V rows the
-//   XCD's running workgroups read then belong to a few heads and stay in its
-//   4 MB L2 (with every head's last tile first, 64 heads' K/V at once went
-//   through HBM 3.15x over).  hchunk >= heads / 8 gives one chunk: plain
-//   longest-first over the XCD's heads.  Otherwise (heads not a multiple of
-//   8) id g takes the (g / heads)-th tile counted from the last and head
-//   g % heads.
-//   Non-causal: equal costs; each XCD gets a contiguous run of logical work
-//   (whole heads where the counts allow), in head order.
-__host__ __device__ inline void workgroup_tile(int64_t g64, int64_t G64, int64_t nq64, int causal, int64_t hchunk64,
-                                               int64_t* tile, int64_t* bh) {
-  // grids stay below 2^31 workgroups (checked at launch): 32-bit arithmetic
-  const uint32_t g = (uint32_t)g64, G = (uint32_t)G64, nq = (uint32_t)nq64;
-  const uint32_t X = 8;
-  const uint32_t xcd = g % X, slot = g / X;
-  if (causal) {
-    const uint32_t heads = G / nq;
-    const uint32_t hchunk = hchunk64 > (int64_t)heads ? heads : (uint32_t)(hchunk64 > 0 ? hchunk64 : 0);
-    if (heads % X != 0 || hchunk == 0) {
-      *bh = g % heads;
-      *tile = nq - 1 - g / heads;
-      return;
-    }
-    const uint32_t hx = heads / X;                 // heads of this XCD
-    const uint32_t c = hchunk < hx ? hchunk : hx;  // heads per chunk
-    const uint32_t chunk = slot / (c * nq);
-    const uint32_t r = slot - chunk * c * nq;
-    const uint32_t cw = (hx - chunk * c) < c ? (hx - chunk * c) : c;  // heads in this chunk
-    *tile = nq - 1 - r / cw;
-    *bh = (int64_t)(chunk * c + r % cw) * X + xcd;
-    return;
-  }
-  const uint32_t base = G / X, rem = G % X;
-  const uint32_t logical = xcd * base + (xcd < rem ? xcd : rem) + slot;
-  *bh = logical / nq;
-  *tile = logical % nq;
-}
-
-// Heads per chunk of the causal order above: as many as keep the chunk's K
-// and V rows within kL2ChunkBytes of the XCD's L2.
-constexpr int64_t kL2ChunkBytes = (int64_t)4 << 20;
-__host__ __device__ inline int64_t causal_head_chunk(int64_t Skv, int64_t D) {
-  const int64_t kv = 4 * Skv * D;  // K and V rows of one head, 16-bit
-  const int64_t c = kv > 0 ? kL2ChunkBytes / kv : kL2ChunkBytes;
-  return c > 1 ? c : 1;
-}
 
 // ---------------------------------------------------------------------------
 // The problem in global memory
@@ -400,6 +348,8 @@ struct Problem {
   int Sq, Skv, H, nq;                                      // nq query tiles per head
   int64_t G;                                               // workgroups
   int64_t hchunk;                                          // heads per chunk (causal order)
+  TileMap map;                                             // workgroup -> (query tile, b*H + h)
+  Div31 dH;                                                // division by H
   float c;                                                 // |scale| * log2(e), > 0
   uint32_t qsign;  // 0x80008000 when scale < 0: Q is negated in registers
 };
@@ -416,14 +366,15 @@ struct HeadView {
   uint32_t qsign;     // XOR mask of every 32-bit word of the Q fragment
 };
 
-__device__ __forceinline__ HeadView head_view(const Problem& p, int64_t bh) {
-  const int64_t b = bh / p.H, h = bh % p.H;
+__device__ __forceinline__ HeadView head_view(const Problem& p, uint32_t bh) {
+  const uint32_t b32 = div31(bh, p.dH);
+  const int64_t b = b32, h = bh - b32 * (uint32_t)p.H;
   HeadView hv;
   hv.q = p.q + b * p.q_sb + h * p.q_sh;
   hv.k = p.k + b * p.k_sb + h * p.k_sh;
   hv.v = p.v + b * p.v_sb + h * p.v_sh;
   hv.o = p.o + b * p.o_sb + h * p.o_sh;
-  hv.lse = p.lse + bh * p.Sq;
+  hv.lse = p.lse + (int64_t)bh * p.Sq;
   hv.q_ss = p.q_ss, hv.k_ss = p.k_ss, hv.v_ss = p.v_ss, hv.o_ss = p.o_ss;
   hv.Sq = p.Sq, hv.Skv = p.Skv, hv.koff = p.Skv - p.Sq;
   hv.qsign = p.qsign;
@@ -1132,10 +1083,10 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(const Problem p) {
   // the copying wave of a PRODUCER workgroup (wave NW) computes nothing
   const bool producer = C::PRODUCER && wave == C::NW;
 
-  int64_t tile64, bh64;
-  workgroup_tile(blockIdx.x, p.G, p.nq, CAUSAL, p.hchunk, &tile64, &bh64);
-  const int q0 = (int)tile64 * BM;
-  const HeadView hv = head_view(p, bh64);
+  uint32_t tile, bh;
+  workgroup_tile<CAUSAL>(p.map, blockIdx.x, &tile, &bh);
+  const int q0 = (int)tile * BM;
+  const HeadView hv = head_view(p, bh);
 
   // Q through LDS where a second K/V stage exists: the loop's first iteration
   // writes it (the staggered schedule: vt1 only), so the waves stage their Q
@@ -1348,10 +1299,10 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_pingpong_kernel(const Problem 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int group = wave >> 2;
 
-  int64_t tile64, bh64;
-  workgroup_tile(blockIdx.x, p.G, p.nq, CAUSAL, p.hchunk, &tile64, &bh64);
-  const int q0 = (int)tile64 * BM;
-  const HeadView hv = head_view(p, bh64);
+  uint32_t tile, bh;
+  workgroup_tile<CAUSAL>(p.map, blockIdx.x, &tile, &bh);
+  const int q0 = (int)tile * BM;
+  const HeadView hv = head_view(p, bh);
 
   // with two stages the V stage arrays are free until the first iteration
   // copies V_0: the waves stage their Q rows there
@@ -1540,10 +1491,10 @@ void attn_fwd_inwave_kernel(const Problem p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int qw = wave % C::QW, kw = wave / C::QW;
 
-  int64_t tile64, bh64;
-  workgroup_tile(blockIdx.x, p.G, p.nq, CAUSAL, p.hchunk, &tile64, &bh64);
-  const int q0 = (int)tile64 * BM;
-  const HeadView hv = head_view(p, bh64);
+  uint32_t tile, bh;
+  workgroup_tile<CAUSAL>(p.map, blockIdx.x, &tile, &bh);
+  const int q0 = (int)tile * BM;
+  const HeadView hv = head_view(p, bh);
 
   // Q through the V stages, which the loop's first copies only reach after
   // the barrier that follows qk(0): the kw = 0 waves copy the rows of their

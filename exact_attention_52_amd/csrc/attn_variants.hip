@@ -53,6 +53,7 @@ hipError_t go(Problem p, hipStream_t st) {
   const int64_t BH = p.G;  // the caller passes B*H here
   p.G = (int64_t)p.nq * BH;
   if (p.G > 0x7FFFFFFF) return hipErrorInvalidValue;
+  p.map = make_tile_map(p.G, p.nq, CAUSAL, p.hchunk);
   hipLaunchKernelGGL((attn_fwd_kernel<C, CAUSAL, DT>), dim3((unsigned)p.G), dim3(C::NT), 0, st, p);
   return hipGetLastError();
 }

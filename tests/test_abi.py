@@ -201,6 +201,45 @@ def test_workgroup_map_keeps_heads_on_one_xcd():
         assert bh // 4 == wg % 8
 
 
+def plain_map(G, nq, causal, hchunk, g):
+    """The documented workgroup order with plain integer division (the
+    library divides by multiplying with reciprocals fixed on the host)."""
+    X = 8
+    xcd, slot = g % X, g // X
+    if causal:
+        heads = G // nq
+        hc = heads if hchunk > heads else max(hchunk, 0)
+        if heads % X or hc == 0:
+            return nq - 1 - g // heads, g % heads
+        hx = heads // X
+        c = min(hc, hx)
+        chunk = slot // (c * nq)
+        r = slot - chunk * c * nq
+        cw = min(hx - chunk * c, c)
+        return nq - 1 - r // cw, (chunk * c + r % cw) * X + xcd
+    base, rem = G // X, G % X
+    logical = xcd * base + min(xcd, rem) + slot
+    return logical % nq, logical // nq
+
+
+# grids up to 2^30 workgroups (quotients of numerators near 2^31), tile
+# counts and head counts that are and are not powers of two, short last
+# chunks, heads not a multiple of 8
+@pytest.mark.parametrize("B,H,S,D", [(1, 1 << 23, 16384, 64), (1, 8388613, 8192, 64), (7, 3 << 18, 4000, 128),
+                                     (5, 77, 100000, 256), (2, 1 << 20, 2048, 128), (1, 1 << 22, 8191, 256),
+                                     (3, 1000, 5000, 64), (1, 24, 300, 128)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_workgroup_map_matches_plain_division(B, H, S, D, causal):
+    import random
+    p = ea.attn_fwd_plan(B, H, S, D, causal, 0)
+    G, nq = p["num_workgroups"], p["num_q_tiles"]
+    hchunk = max(1, (4 << 20) // (4 * S * D))
+    rng = random.Random(G)
+    ids = list(range(min(G, 300))) + list(range(max(0, G - 300), G)) + [rng.randrange(G) for _ in range(600)]
+    for wg in ids:
+        assert ea.attn_fwd_workgroup_tile(B, H, S, D, causal, 0, wg) == plain_map(G, nq, causal, hchunk, wg), wg
+
+
 FAKE = 0x10000  # never dereferenced: every case below fails before any HIP call
 
 
