@@ -126,11 +126,6 @@ struct TileCfg {
   // extra wave issues every HBM -> LDS copy while the others only compute
   static constexpr int STAGES = STAGES_;
   static constexpr bool PRODUCER = PRODUCER_;
-  // Running-max policy of the softmax: exact at D = 128, where the ping-pong
-  // kernel rescales O^T in the MFMA phase nearly for free; lagging by up to
-  // kRescaleSlack elsewhere, where the rescale sits on the wave's own
-  // critical path (see Wave::softmax)
-  static constexpr bool EXACT_MAX = D_ == 128;
   static constexpr int D = D_;
   static constexpr int QW = QW_;             // waves along query rows
   static constexpr int KW = KW_;             // waves along each key tile
@@ -420,6 +415,8 @@ struct Wave {
                      // their relative rounding), while the plain fp32 sum
                      // would add w* d* V* of the dominant key: 2.03e-3 on a
                      // peaky fp16 row with |O| ~ 4.5, over the 2e-3 bound
+  bool pend_rs;      // the last deferred softmax asked for a rescale of O^T
+                     // (wave-uniform: the caller skips the multiplies when not)
   float alpha;       // exp2(old m_run - new m_run) of the last softmax: the
                      // factor O^T still owes when the rescale is deferred
   int lane, half, wq_first, wq_last, my_q, kbase, Sq, Skv, koff, k_lane, v_lane;
@@ -459,6 +456,7 @@ struct Wave {
     p_top = 0.f;
     e_top = 0.f;
     alpha = 1.f;
+    pend_rs = false;
   }
 
   // Q through LDS.  Loaded straight into the fragment, a load instruction
@@ -492,6 +490,7 @@ struct Wave {
 #pragma unroll
     for (int i = 0; i < 2 * NB; ++i) pf[i] = u32x4{0u, 0u, 0u, 0u};
     alpha = 1.f;
+    pend_rs = false;
   }
 
   // does this wave have any unmasked key in tile j?
@@ -546,23 +545,24 @@ struct Wave {
     const float mx = max_halves(max_tree<16 * NB>(sc));
 
     // Rescale only when some row's max outgrew the reference by the slack
-    // (0 with EXACT_MAX; always on the first tile with an unmasked key,
-    // m_run being -inf before); the branch is uniform across the wave.
+    // (always on the first tile with an unmasked key, m_run being -inf
+    // before); the branch is uniform across the wave.
     // c > 0, so a fully masked max stays -inf and never turns into NaN.
     const float mt = mx * c;
-    if constexpr (DEFER_RESCALE) alpha = 1.f;
+    if constexpr (DEFER_RESCALE) alpha = 1.f, pend_rs = false;
     if (__builtin_amdgcn_ballot_w64(mt > m_thr) != 0) {
       const float m_new = __builtin_elementwise_maximum(m_run, mt);
       const bool none = m_new == -__builtin_inff();
       const float a = none ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       nm_ref = none ? 0.f : -m_new;
-      m_thr = m_new + (C::EXACT_MAX ? 0.f : kRescaleSlack);
+      m_thr = m_new + kRescaleSlack;
       l_run *= a;
       p_top *= a;
       e_top *= a;
       if constexpr (DEFER_RESCALE) {
         alpha = a;
+        pend_rs = true;
       } else {
 #pragma unroll
         for (int db = 0; db < DB; ++db) oacc[db] *= a;
@@ -590,11 +590,10 @@ struct Wave {
 #pragma unroll
       for (int i = 0; i < w / 2; ++i) ls[i] += ls[i + w / 2];
     l_run += ls[0];
-    if constexpr (!C::EXACT_MAX) {
+    {
       // The largest P of this row in this tile, computed exactly as above,
       // and the error of its 16-bit rounding: the one of the row's largest P
-      // so far joins O's normaliser (see e_top).  With the exact running max
-      // that P is exp2(0) = 1, exact in 16 bits, and e_top stays 0.
+      // so far joins O's normaliser (see e_top)
       const float pm = __builtin_amdgcn_exp2f(__builtin_fmaf(mx, c, nm_ref));
       const float em = E::round(pm) - pm;
       if (pm > p_top) p_top = pm, e_top = em;
@@ -791,7 +790,7 @@ struct Wave {
         const float a = none ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
         nm_ref = none ? 0.f : -m_new;
-        m_thr = m_new + (C::EXACT_MAX ? 0.f : kRescaleSlack);
+        m_thr = m_new + kRescaleSlack;
         l_run *= a;
         p_top *= a;
         e_top *= a;
@@ -818,13 +817,11 @@ struct Wave {
         for (int i = 0; i < w / 2; ++i) st.ls[i] += st.ls[i + w / 2];
       l_run += st.ls[0];
       pin(l_run);
-      if constexpr (!C::EXACT_MAX) {
-        const float pm = __builtin_amdgcn_exp2f(__builtin_fmaf(st.mx, c, nm_ref));
-        const float em = E::round(pm) - pm;
-        if (pm > p_top) p_top = pm, e_top = em;
-        pin(p_top);
-        pin(e_top);
-      }
+      const float pm = __builtin_amdgcn_exp2f(__builtin_fmaf(st.mx, c, nm_ref));
+      const float em = E::round(pm) - pm;
+      if (pm > p_top) p_top = pm, e_top = em;
+      pin(p_top);
+      pin(e_top);
     }
   }
 
@@ -1274,10 +1271,13 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_kernel(const Problem p) {
 // ---------------------------------------------------------------------------
 // MFMAs between two copy instructions in group 0's MFMA block
 constexpr int kPingPongCopyStride = 3;
-// Whether the ping-pong rescales O^T (when a row max moved) at the start of
-// the next MFMA phase instead of in the softmax phase.  Deferred is faster:
-// the softmax phase is the longer one, and with the multiplies there the
-// compiler spilled registers of the causal kernel.
+// Whether the ping-pong rescales O^T (when a row max moved past the slack) at
+// the start of the next MFMA phase instead of in the softmax phase.  Deferred
+// is faster: the softmax phase is the longer one, and with the multiplies
+// there the compiler spilled registers of the causal kernel.  The multiplies
+// run only on a wave-uniform flag: with the lagging max few wave-tiles need
+// them, and issued on every tile (alpha = 1) they were 64 VALU instructions
+// per tile beside the MFMAs in a kernel whose clock the power limit sets.
 constexpr bool kPingPongDeferRescale = true;
 template <class C, bool CAUSAL, int DT>
 __global__ __launch_bounds__(C::NT) void attn_fwd_pingpong_kernel(const Problem p) {
@@ -1356,10 +1356,14 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_pingpong_kernel(const Problem 
           vcp.line(rv, vt_ld, wave * LPW + i - LPW);
       };
       constexpr int LS = (PV && QK) ? kPingPongCopyStride : 2;
-      if constexpr (kPingPongDeferRescale && PV) w.rescale_o();
+      if constexpr (kPingPongDeferRescale && PV) {
+        if (w.pend_rs) w.rescale_o();
+      }
       w.template mfma_ops<PV, QK, 2 * LPW, LS>(vt_prev, kt_j, copy);
     } else {
-      if constexpr (kPingPongDeferRescale && PV) w.rescale_o();
+      if constexpr (kPingPongDeferRescale && PV) {
+        if (w.pend_rs) w.rescale_o();
+      }
       w.template mfma_ops<PV, QK>(vt_prev, kt_j);
     }
     barrier_keep_loads();
@@ -1376,7 +1380,9 @@ __global__ __launch_bounds__(C::NT) void attn_fwd_pingpong_kernel(const Problem 
   // the last iteration with two stages: pv(n-1) from vt_prev, then the
   // output (vt_free is the V array without a tile)
   auto last = [&](auto copies, const uint8_t* vt_prev, uint8_t* vt_free) __attribute__((always_inline)) {
-    if constexpr (kPingPongDeferRescale) w.rescale_o();
+    if constexpr (kPingPongDeferRescale) {
+      if (w.pend_rs) w.rescale_o();
+    }
     w.template mfma_ops<true, false>(vt_prev, kt0);
     if constexpr (decltype(copies)::value) {
       barrier_keep_loads();  // end of X_n
