@@ -493,10 +493,14 @@ struct Wave {
     pend_rs = false;
   }
 
-  // does this wave have any unmasked key in tile j?
+  // does this wave have any unmasked key in tile j?  Every operand is the
+  // same in all lanes; readfirstlane lets the compiler see that too (in the
+  // ping-pong kernel it had kept one in a VGPR and exec-masked the P = 0
+  // moves of zero_pf(), issuing them on every tile)
   __device__ __forceinline__ bool active(int j) const {
     const int kv0 = j * BN + kbase;
-    return kv0 < Skv && (!CAUSAL || kv0 <= wq_last + koff) && wq_first < Sq;
+    const bool a = kv0 < Skv && (!CAUSAL || kv0 <= wq_last + koff) && wq_first < Sq;
+    return __builtin_amdgcn_readfirstlane((int)a) != 0;
   }
 
   __device__ __forceinline__ void qk(const uint8_t* kt) {
