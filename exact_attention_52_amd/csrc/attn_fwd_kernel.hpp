@@ -521,8 +521,13 @@ struct Wave {
   template <bool DEFER_RESCALE = false>
   __device__ __forceinline__ void softmax(int j) {
     const int kv0 = j * BN + kbase;
-    // mask keys past the end or after the query (diagonal / ragged tiles)
-    const bool need_mask = (kv0 + C::KSUB > Skv) || (CAUSAL && kv0 + C::KSUB - 1 > wq_first + koff);
+    // mask keys past the end or after the query (diagonal / ragged tiles).
+    // The test is wave-uniform; in the ping-pong kernel readfirstlane makes
+    // it a scalar branch (the compiler had exec-masked the mask there; A/B:
+    // causal B=2 H=16 S=4096 bf16 126.5 -> 125.4 us), while kernel 1 at
+    // D=256 ran 3 % slower that way and keeps the compiler's choice.
+    const bool mask_test = (kv0 + C::KSUB > Skv) || (CAUSAL && kv0 + C::KSUB - 1 > wq_first + koff);
+    const bool need_mask = C::PINGPONG ? __builtin_amdgcn_readfirstlane((int)mask_test) != 0 : mask_test;
     if (need_mask) {
       // score i of block kb is key kv0 + 4*half + off(kb, i); it is kept iff
       // key <= min(my_q + koff, Skv-1) (causal) or key <= Skv-1: one compare
