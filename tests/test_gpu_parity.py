@@ -146,6 +146,28 @@ def test_rising_max_every_tile(ea, oracle_mod, D, dtype):
 
 @pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("step", [3.0, 6.0])
+def test_rising_max_in_steps(ea, oracle_mod, D, dtype, step):
+    # the scores of keys 64m .. 64m+63 are step * m: the row max rises by
+    # step * log2(e) (4.3 or 8.7) per 64 keys, below or just above the 2^8
+    # slack of the lagging reference max, so rescales fire on some key tiles
+    # and not on others, and P runs up towards 2^8 between them
+    B, H, S = 1, 2, 700
+    qf = np.zeros((B, H, S, D))
+    qf[..., 0] = 1.0
+    kf = np.zeros((B, H, S, D))
+    kf[..., 0] = step * (np.arange(S) // 64)
+    q, k = inputs.round_to_bits(qf, dtype), inputs.round_to_bits(kf, dtype)
+    _, _, v = inputs.gen_qkv(B, H, S, D, dtype, seed=29)
+    for causal in (False, True):
+        o, lse = run(ea, q, k, v, dtype, 1.0, causal)
+        o_ref, lse_ref = oracle_mod.attn_fwd(q, k, v, dtype, 1.0, causal)
+        eo, el = errors(o, lse, o_ref, lse_ref)
+        assert eo <= TOL_O[dtype] and el <= TOL_LSE, (causal, eo, el)
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_negative_scale(ea, oracle_mod, D, dtype, causal):
     # the page's sm_scale is a plain f32: a negative scale flips the softmax
