@@ -577,6 +577,12 @@ void attn_bwd_dq(const BwdProblem p) {
   f32x16 dqa[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) dqa[db] = f32x16{};
+  // -D_i in every entry: the accumulator operand of each block's first dP
+  // MFMA, so the MFMAs leave dP - D_i (as in the dK/dV kernel) and no
+  // subtraction runs per score (16 VALU instructions per 32-key block)
+  f32x16 negd;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) negd[i] = -dl;
 
   const int q_end = q0 + BM < Sq ? q0 + BM : Sq;
   int kv_end = CAUSAL ? q_end + koff : Skv;
@@ -616,7 +622,7 @@ void attn_bwd_dq(const BwdProblem p) {
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb) {
         if constexpr (C::WAVES_PER_SIMD == 1) pin_agprs(qf, of);
-        f32x16 sa = f32x16{}, dpa = f32x16{};
+        f32x16 sa = f32x16{}, dpa;
         {
           auto rd = [&](int t) __attribute__((always_inline)) -> u32x4 {
             return *reinterpret_cast<const u32x4*>(((t & 1) ? vt : kt) + xrow + X::off(32 * kb) + 32 * (t >> 1));
@@ -629,7 +635,7 @@ void attn_bwd_dq(const BwdProblem p) {
             const u32x4 a = buf[t % PIPE];
             if (t + PIPE < N1) buf[t % PIPE] = rd(t + PIPE);
             if (t & 1)
-              dpa = E::mfma(a, of[t >> 1], dpa);
+              dpa = E::mfma(a, of[t >> 1], t == 1 ? negd : dpa);
             else
               sa = E::mfma(a, qf[t >> 1], sa);
           }
@@ -649,7 +655,7 @@ void attn_bwd_dq(const BwdProblem p) {
           for (int i = 0; i < 16; ++i) pv[i] = (32 * kb + 8 * (i >> 2) + (i & 3)) <= lim ? pv[i] : 0.f;
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) ds[i] = pv[i] * (dpa[i] - dl);
+        for (int i = 0; i < 16; ++i) ds[i] = pv[i] * dpa[i];  // P * (dP - D_i)
         u32x4 sf[2];
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
