@@ -168,7 +168,7 @@ def test_workgroup_map_is_bijection_and_longest_first(B, H, S, D, causal):
 
 
 def test_causal_map_chunks_heads_within_the_l2_budget():
-    # c2 (B16 H32 S1024 D64): K and V of a head are 256 KiB, so a chunk holds
+    # B=16 H=32 S=1024 D=64: K and V of a head are 256 KiB, so a chunk holds
     # 16 heads (4 MiB); every XCD's first 16 * 8 workgroups cover 16 heads
     B, H, S, D = 16, 32, 1024, 64
     for x in range(8):
@@ -177,7 +177,7 @@ def test_causal_map_chunks_heads_within_the_l2_budget():
 
 
 def test_causal_map_balances_each_xcd():
-    # c3 (B4 H16 S2048 D128 causal): 64 x 8 tiles, tile t costs t + 1. Greedy
+    # B=4 H=16 S=2048 D=128 causal: 64 x 8 tiles, tile t costs t + 1. Greedy
     # list scheduling of each XCD's workgroups, in id order, onto 32 CUs that
     # each hold one workgroup at a time gives every CU the same total (with
     # 1 MiB of K and V per head, a chunk is 4 of the XCD's 8 heads).

@@ -96,11 +96,11 @@ def test_full_parity_checks_every_element():
 
 
 def test_roofline_bound_follows_the_workload():
-    # c4: 2.75e11 FLOP at 2.5 PFLOP/s (110 us) against 134.7 MB at 8 TB/s (17 us): MFMA-bound
+    # B=2 H=16 S=4096 D=128: 2.75e11 FLOP at 2.5 PFLOP/s (110 us) against 134.7 MB at 8 TB/s (17 us): MFMA-bound
     r = bench.roofline((2, 16, 4096, 128, "fp16", False), 0.25)
     assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s"
     assert r["achieved"] == pytest.approx(bench.flops(2, 16, 4096, 128, False) / 0.25e-3 / 1e12, rel=1e-5)
-    # c2: 6.87e10 FLOP (27.5 us) against 270.5 MB (33.8 us): HBM-bound
+    # B=16 H=32 S=1024 D=64 causal: 6.87e10 FLOP (27.5 us) against 270.5 MB (33.8 us): HBM-bound
     r = bench.roofline((16, 32, 1024, 64, "fp16", True), 0.1)
     assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["traffic"] is None
     assert r["achieved"] == pytest.approx(bench.min_bytes(16, 32, 1024, 64) / 0.1e-3 / 1e9, rel=1e-3)

@@ -51,7 +51,7 @@ def test_unfused_peaky_workload_every_element(ea, oracle_mod):
     # element of O and LSE against the oracle
     import torch
     B, H, S, D, dtype, causal, mult = inputs.WORKLOADS["c4_b2h16s4096d128_fp16_peaky"]
-    print("unfused workload c4, every element", flush=True)
+    print("unfused, B=2 H=16 S=4096 D=128 fp16, every element", flush=True)
     q, k, v = inputs.gen_qkv(B, H, S, D, dtype, seed=0, qk_mult=mult)
     scale = float(np.float32(1.0 / math.sqrt(D)))
     o, lse = ea.fwd_unfused(*(to_dev(x, dtype) for x in (q, k, v)), scale=scale, causal=causal)
